@@ -1,0 +1,410 @@
+"""Pins for the CPU oracle: each test ties one oracle function to something
+other than itself -- format specifications, hand-derived values, closed forms,
+library routines, or brute force on tiny inputs."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa2_oracle as O
+from fp4_kv_cache_02_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                yield line
+
+
+def bf16(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- O1 / O2 --
+
+def test_e2m1_codebook_matches_spec():
+    for line in _rows("e2m1_codebook.txt"):
+        code, val = line.split()
+        got = O.e2m1_value(int(code))
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+
+
+def test_e4m3_reference_points():
+    for line in _rows("e4m3_points.txt"):
+        code, val = line.split()
+        got = float(O.e4m3_value(int(code, 16)))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+
+
+def test_e4m3_decode_matches_torch_float8():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_value(np.arange(256))
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_e4m3_roundtrip_and_extremes():
+    codes = np.arange(0x7F)                     # every finite non-negative code
+    assert np.array_equal(O.e4m3_encode(O.e4m3_value(codes).astype(np.float32)), codes)
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0x01) == 2.0 ** -9
+    assert O.e4m3_encode(np.float32(1e6)) == 0x7E   # saturates
+
+
+def test_e4m3_rounding_matches_torch_below_overflow():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.uniform(0, 460, 20000), np.exp(rng.uniform(-12, 6, 20000)),
+        O.e4m3_value(np.arange(0x7E)) * 0.5 + O.e4m3_value(np.arange(1, 0x7F)) * 0.5,  # midpoints
+    ]).astype(np.float32)
+    x = x[x < 464]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), ref)
+
+
+# ---------------------------------------------------------------------- O3 --
+
+def test_e2m1_round_ties_and_saturation():
+    for line in _rows("e2m1_rounding.txt"):
+        y, mag = (float(t) for t in line.split())
+        for sgn in (1.0, -1.0):
+            c = int(O.e2m1_encode(np.float32(sgn * y)))
+            assert abs(O.e2m1_value(c)) == mag, (y, c)
+            assert (c >> 3) == (1 if sgn < 0 else 0)
+
+
+def test_quantize_layout_and_requantize_identity():
+    rng = np.random.default_rng(3)
+    N = 64
+    codes = rng.integers(0, 16, size=(N, 512))
+    scale = rng.integers(0x08, 0x70, size=(N, 32)).astype(np.uint8)
+    # force max |code| == 6 in every block, so amax/6 is exactly the scale
+    codes.reshape(N, 32, 16)[:, :, 5] = 7
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    x = O.dequantize_fp4(packed, scale).astype(np.float32)
+    p2, s2 = O.quantize_fp4(x)
+    assert np.array_equal(s2, scale)
+    # -0 and +0 both decode to 0; compare decoded values and the sign bit of nonzeros
+    assert np.array_equal(O.dequantize_fp4(p2, s2), O.dequantize_fp4(packed, scale))
+    # nibble order: channel 0 in the low nibble
+    x1 = np.zeros((1, 512), np.float32)
+    x1[0, 0], x1[0, 1] = 6.0, -3.0
+    p, s = O.quantize_fp4(x1)
+    assert O.e4m3_value(s[0, 0]) == 1.0 and p[0, 0] == (7 | (13 << 4))
+    assert p.shape[1] + s.shape[1] == 288
+
+
+def test_quantize_error_bound_and_zero_block():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((256, 512)).astype(np.float32)
+    x[0, :16] = 0.0
+    p, s = O.quantize_fp4(x)
+    assert np.all(p[0, :8] == 0) and s[0, 0] == 0
+    y = O.dequantize_fp4(p, s)
+    blocks = np.abs(x).reshape(256, 32, 16).max(axis=2)
+    sc = np.repeat(O.e4m3_value(s), 16, axis=1)
+    # every element within half a grid step of the scaled grid (step <= 2*scale
+    # for |x/scale| < 4, saturation only above 6*scale)
+    err = np.abs(y - x)
+    assert np.all(err <= sc * 1.0 + 1e-12)
+    assert np.all(np.abs(y).reshape(256, 32, 16).max(axis=2) <= 6 * O.e4m3_value(s) + 1e-12)
+    assert blocks.shape == (256, 32)
+
+
+def test_dequantised_values_exact_in_bf16_and_fp16():
+    codes = np.arange(16)
+    scales = np.arange(0x7F)
+    v = O.e2m1_value(codes)[:, None] * O.e4m3_value(scales)[None, :]
+    v = v.reshape(-1)
+    assert np.array_equal(torch.from_numpy(v).to(torch.bfloat16).double().numpy(), v)
+    assert np.array_equal(torch.from_numpy(v).to(torch.float16).double().numpy(), v)
+    nz = np.abs(v[v != 0])
+    assert nz.min() == 2.0 ** -10 and nz.max() == 2688.0
+
+
+# ---------------------------------------------------------------------- O4 --
+
+def _case(line):
+    name, qs, ks, ws, exp = (t.strip() for t in line.split("|"))
+    q = np.zeros((4, 64), np.float32)
+    for item in qs.split(","):
+        hc, val = item.split("=")
+        h, c = hc.split(":")
+        q[int(h), int(c)] = float(val)
+    k = np.zeros((1, 64), np.float32)
+    for item in ks.split(","):
+        c, val = item.split("=")
+        k[0, int(c)] = float(val)
+    w = np.array([float(t) for t in ws.split(",")], np.float32)
+    return name, q, k, w, float(exp)
+
+
+def test_score_rounding_cases():
+    for line in _rows("score_rounding_cases.txt"):
+        name, q, k, w, exp = _case(line)
+        qb, kb = bf16(q), bf16(k)
+        assert np.array_equal(O.bf16_to_f64(qb), q.astype(np.float64)), name
+        assert np.array_equal(O.bf16_to_f64(kb), k.astype(np.float64)), name
+        got = O.index_scores(qb, kb, w)
+        assert got.dtype == np.float32 and float(got[0]) == exp, (name, float(got[0]), exp)
+
+
+def test_score_integer_closed_form():
+    """With small integer inputs every partial sum is exact, so the score is the
+    exact integer sum_h w_h * max(0, q_h . k) whatever the order."""
+    rng = np.random.default_rng(11)
+    q = rng.integers(-4, 5, size=(4, 64))
+    k = rng.integers(-4, 5, size=(500, 64))
+    w = rng.integers(0, 4, size=4)
+    got = O.index_scores(bf16(q), bf16(k), w.astype(np.float32))
+    for n in range(k.shape[0]):
+        exact = sum(int(w[h]) * max(0, sum(int(q[h, i]) * int(k[n, i]) for i in range(64)))
+                    for h in range(4))
+        assert got[n] == exact
+    # without weights the default is 1 per head
+    got1 = O.index_scores(bf16(q), bf16(k[:3]))
+    for n in range(3):
+        assert got1[n] == sum(max(0, int(np.dot(q[h], k[n]))) for h in range(4))
+
+
+def test_score_close_to_exact_value():
+    """On random bf16 data the canonical fp32 score is within the standard
+    summation error bound of the exact value."""
+    rng = np.random.default_rng(12)
+    qb = bf16(rng.standard_normal((4, 64)))
+    kb = bf16(rng.standard_normal((2000, 64)))
+    q, k = O.bf16_to_f64(qb), O.bf16_to_f64(kb)
+    exact = np.maximum(k @ q.T, 0.0).sum(axis=1)
+    bound = (np.abs(k) @ np.abs(q).T).sum(axis=1) * 70 * 2.0 ** -24 + 1e-30
+    got = O.index_scores(qb, kb).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+# ---------------------------------------------------------------------- O5 --
+
+def _brute_topk(vals, k):
+    # total order: larger value first; -0 below +0; then lower index first
+    def rank(i):
+        v = vals[i]
+        return (-v, 0 if math.copysign(1.0, v) > 0 else 1, i)
+    present = [i for i in range(len(vals)) if vals[i] != -math.inf]
+    chosen = sorted(sorted(present, key=rank)[:k])
+    return chosen + [-1] * (k - len(chosen))
+
+
+def test_topk_brute_force_tiny():
+    rng = np.random.default_rng(5)
+    for trial in range(400):
+        n = int(rng.integers(0, 40))
+        k = int(rng.integers(1, 12))
+        pool = np.array([0.0, -0.0, 1.0, 1.0, 2.5, -3.0, -np.inf, 7.0], np.float32)
+        vals = rng.choice(pool, size=n) if trial % 2 else rng.standard_normal(n).astype(np.float32)
+        got = O.topk(vals.astype(np.float32), k).tolist()
+        assert got == _brute_topk([float(v) for v in vals.astype(np.float32)], k), (vals, k)
+
+
+def test_topk_all_equal_and_short():
+    s = np.full(100, 3.0, np.float32)
+    assert O.topk(s, 10).tolist() == list(range(10))
+    s = np.arange(5, dtype=np.float32)
+    assert O.topk(s, 8).tolist() == [0, 1, 2, 3, 4, -1, -1, -1]
+    assert O.topk(np.zeros(0, np.float32), 3).tolist() == [-1, -1, -1]
+
+
+def test_order_key_is_monotone():
+    vals = np.array([-np.inf, -3.0, -1e-40, -0.0, 0.0, 1e-40, 1.0, 3.0, np.inf], np.float32)
+    keys = O.order_key(vals)
+    assert np.all(np.diff(keys.astype(np.int64)) > 0)
+
+
+# ---------------------------------------------------------------- O6 / O7 --
+
+def test_block_max_and_candidates_brute_force():
+    rng = np.random.default_rng(6)
+    for trial in range(200):
+        L = int(rng.integers(1, 120))
+        keep = int(rng.integers(1, 10))
+        s = rng.choice(np.array([0.0, 1.0, 2.0, 5.0], np.float32), size=L) if trial % 2 else \
+            rng.standard_normal(L).astype(np.float32)
+        nb = (L + 7) // 8
+        bm = [max(float(v) for v in s[8 * b:min(L, 8 * b + 8)]) for b in range(nb)]
+        assert np.array_equal(O.block_max(s, L), np.array(bm, np.float32))
+        assert O.hier_candidates(s, L, keep).tolist() == _brute_topk(bm, keep)
+
+
+def test_candidates_contain_full_topk():
+    """A block holding a Top-k position ranks ahead of every block holding
+    none, so with keep >= k the candidate set contains the Full layer's Top-k."""
+    rng = np.random.default_rng(8)
+    for trial in range(100):
+        L = int(rng.integers(50, 3000))
+        k = int(rng.integers(1, 40))
+        keep = k + int(rng.integers(0, 5))
+        s = rng.integers(0, 4, size=L).astype(np.float32) if trial % 2 else \
+            rng.standard_normal(L).astype(np.float32)
+        top = O.topk(s, k)
+        cand = set(O.candidate_positions(O.hier_candidates(s, L, keep), L).tolist())
+        assert set(int(p) for p in top if p >= 0) <= cand
+
+
+def test_reindex_with_same_query_equals_full():
+    rng = np.random.default_rng(9)
+    L = 5000
+    qb = bf16(rng.standard_normal((4, 64)))
+    kb = bf16(rng.standard_normal((L, 64)))
+    s = O.index_scores(qb, kb)
+    full = O.topk(s, 64)
+    cand = O.hier_candidates(s, L, 100)
+    assert np.array_equal(O.reindex_topk(qb, kb, cand, L, 64), full)
+    # L small enough that every block is a candidate: candidates == all
+    assert np.array_equal(O.reindex_topk(qb, kb, O.hier_candidates(s, L, 1000), L, 64), full)
+    assert np.array_equal(O.reindex_topk(qb, kb, None, L, 64), full)
+
+
+# ---------------------------------------------------------------------- O8 --
+
+def _rand_bits(rng, shape):
+    return bf16(rng.standard_normal(shape))
+
+
+def test_attention_full_selection_equals_dense_sdpa():
+    """Selecting every position reduces the sparse branch to dense attention;
+    checked against torch's scaled_dot_product_attention in float64."""
+    rng = np.random.default_rng(10)
+    L, W = 96, 20
+    codes = rng.integers(0, 256, size=(L, 256)).astype(np.uint8)
+    sc = rng.integers(0x28, 0x40, size=(L, 32)).astype(np.uint8)
+    kv = O.dequantize_fp4(codes, sc)
+    q = _rand_bits(rng, (16, 512))
+    sk, sv = _rand_bits(rng, (W, 512)), _rand_bits(rng, (W, 512))
+    sm = 1.0 / math.sqrt(512)
+    out, lse = O.attention(q, kv, sk, sv, sm)
+    K = torch.from_numpy(np.concatenate([kv, O.bf16_to_f64(sk)]))
+    V = torch.from_numpy(np.concatenate([kv, O.bf16_to_f64(sv)]))
+    Q = torch.from_numpy(O.bf16_to_f64(q))
+    ref = torch.nn.functional.scaled_dot_product_attention(Q[None], K[None], V[None], scale=sm)[0]
+    assert np.allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+    z = sm * (Q @ K.T)
+    assert np.allclose(lse, torch.logsumexp(z, dim=1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_single_key_and_permutation():
+    rng = np.random.default_rng(13)
+    kv = O.dequantize_fp4(rng.integers(0, 256, (1, 256)).astype(np.uint8),
+                          np.full((1, 32), 0x38, np.uint8))
+    q = _rand_bits(rng, (16, 512))
+    out, _ = O.attention(q, kv, None, None, 0.05)
+    assert np.array_equal(out, np.broadcast_to(kv, (16, 512)))
+    kv2 = O.dequantize_fp4(rng.integers(0, 256, (30, 256)).astype(np.uint8),
+                           rng.integers(0x30, 0x40, (30, 32)).astype(np.uint8))
+    o1, l1 = O.attention(q, kv2, None, None, 0.05)
+    perm = rng.permutation(30)
+    o2, l2 = O.attention(q, kv2[perm], None, None, 0.05)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-13) and np.allclose(l1, l2, rtol=1e-13)
+
+
+def test_attention_split_merge_equals_joint():
+    rng = np.random.default_rng(14)
+    kv = O.dequantize_fp4(rng.integers(0, 256, (40, 256)).astype(np.uint8),
+                          rng.integers(0x30, 0x40, (40, 32)).astype(np.uint8))
+    q = _rand_bits(rng, (16, 512))
+    sk, sv = _rand_bits(rng, (10, 512)), _rand_bits(rng, (10, 512))
+    joint = O.attention(q, kv, sk, sv, 0.04)
+    a = O.attention(q, kv[:17], None, None, 0.04)
+    b = O.attention(q, kv[17:], None, None, 0.04)
+    c = O.attention(q, np.zeros((0, 512)), sk, sv, 0.04)
+    m = O.merge_partials([a[0], b[0], c[0]], [a[1], b[1], c[1]])
+    assert np.allclose(m[0], joint[0], rtol=1e-12, atol=1e-12)
+    assert np.allclose(m[1], joint[1], rtol=1e-12, atol=1e-12)
+    empty = O.attention(q, np.zeros((0, 512)), None, None, 0.04)
+    assert np.all(empty[0] == 0) and np.all(empty[1] == -np.inf)
+
+
+# ---------------------------------------------------------------- O9 / O10 --
+
+def _small_group(paged, seed=21):
+    rng = np.random.default_rng(seed)
+    lens = [700, 333, 64]
+    B = len(lens)
+    page = 64
+    if paged:
+        npg = [(L + page - 1) // page for L in lens]
+        perm = rng.permutation(sum(npg)).astype(np.int32)
+        pt = np.full((B, max(npg)), -1, np.int32)
+        off = 0
+        for b, n in enumerate(npg):
+            pt[b, :n] = perm[off:off + n]
+            off += n
+        nslots = sum(npg) * page
+        stride = 0
+    else:
+        pt, stride = None, max(lens)
+        nslots = B * stride
+    return rng, lens, pt, stride, nslots
+
+
+def test_paged_equals_contiguous_and_reuse_equals_full():
+    rng, lens, _, stride, nslots_c = _small_group(False)
+    _, _, pt, _, nslots_p = _small_group(True)
+    B = len(lens)
+    # logical per-position data, placed into both layouts
+    kid = [bf16(rng.standard_normal((L, 64))) for L in lens]
+    kvp = [rng.integers(0, 256, (L, 256)).astype(np.uint8) for L in lens]
+    kvs = [rng.integers(0x30, 0x40, (L, 32)).astype(np.uint8) for L in lens]
+
+    def build(nslots, ptab, strd):
+        K = np.zeros((nslots, 64), np.uint16)
+        P = np.zeros((nslots, 256), np.uint8)
+        S = np.zeros((nslots, 32), np.uint8)
+        for b, L in enumerate(lens):
+            sl = O.slot_of(b, np.arange(L), ptab, 64, strd)
+            K[sl], P[sl], S[sl] = kid[b], kvp[b], kvs[b]
+        return O.Cache(P, S, K, lens, ptab, 64, strd)
+
+    cc, cp = build(nslots_c, None, stride), build(nslots_p, pt, 0)
+    qi = bf16(rng.standard_normal((B, 4, 64)))
+    q = bf16(rng.standard_normal((B, 16, 512)))
+    sk = bf16(rng.standard_normal((B, 128, 512)))
+    sv = bf16(rng.standard_normal((B, 128, 512)))
+    st, ln = np.zeros(B, np.int32), np.array([128, 100, 64], np.int32)
+    rs = np.arange(B)
+    res = []
+    for cache in (cc, cp):
+        state = O.GroupState(B)
+        r_full = O.layer_step(O.FULL, cache, state, rs, qi, q, sk, sv, st, ln, 0.05, hier=True,
+                              k=32, keep=40)
+        r_reuse = O.layer_step(O.REUSE, cache, state, rs, None, q, sk, sv, st, ln, 0.05)
+        res.append((state, r_full, r_reuse))
+    (s1, f1, u1), (s2, f2, u2) = res
+    for r in range(B):
+        assert np.array_equal(s1.topk[r], s2.topk[r]) and np.array_equal(s1.cand[r], s2.cand[r])
+        assert np.array_equal(f1[r][0], f2[r][0])
+        # Reuse with the same indices, query and window reproduces the Full result
+        assert np.array_equal(f1[r][0], u1[r][0]) and np.array_equal(f1[r][1], u1[r][1])
+    # Reindex with the Full layer's query gives back the Full Top-k (keep >= k)
+    state = res[0][0]
+    before = [t.copy() for t in state.topk]
+    O.layer_step(O.REINDEX, cc, state, rs, qi, q, sk, sv, st, ln, 0.05, k=32)
+    for r in range(B):
+        assert np.array_equal(state.topk[r], before[r])
+
+
+def test_byte_accounting_identity():
+    """The pages' 890 bytes/token of global KV: per entry 256 B of E2M1 codes
+    + 32 B of E4M3 scales, 2.5 entries per token (3 encoder Full layers at
+    ratio 2, one decoder Full layer at ratio 1), plus 68 B of indexer key."""
+    p, s = O.quantize_fp4(np.zeros((1, 512), np.float32))
+    entry = p.nbytes + s.nbytes
+    assert entry == 288
+    assert 2.5 * (entry + 68) == 890
