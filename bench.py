@@ -1,0 +1,238 @@
+"""Benchmark: CSA2 decode tokens/s/layer and fraction of the HBM roofline.
+
+Default workload: a decoder group of 4 layers (Full + 3 Reuse), decode batch 8,
+context 131072 per sequence -- the 128K-context decode configuration.  One
+step = every layer of the group once (indexer scan, Top-512, FP4 gather +
+dequantisation + attention with the 128-token window) for one batch.
+
+Prints ONE JSON line.  See --help for the options; with no flags it runs on
+one GPU and finishes within a few minutes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=1, help="workload id (1: 128K decode group)")
+    p.add_argument("--replicas", type=int, default=3,
+                   help="input replicas cycled per step so the 256 MB last-level cache cannot serve them")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=1, help="rows in the CPU oracle sample")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 1 GiB device copy (for counter scaling)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w):
+    """Per step: indexer keys 128 B/position + q_idx 512 B + Top-512 out 2048 B
+    per Full row; per attention row-layer 460 800 B (512 FP4 entries of 288 B,
+    window K+V 2*128*1024 B, query 16 KiB, output 32 KiB fp32, indices 2 KiB)."""
+    per_attn = 512 * 288 + 2 * 128 * 1024 + 16 * 512 * 2 + 16 * 512 * 4 + 512 * 4
+    scan = 0
+    attn_layers = 0
+    for m in w.schedule:
+        if m == "F":
+            scan += sum(128 * L + 512 + 2048 for L in w.seq_lens)
+            if w.hier:
+                scan += 8192 * w.B
+        elif m == "I":
+            scan += w.B * (2048 * 8 * 128 + 8192 + 512 + 2048)
+    for li, m in enumerate(w.schedule):
+        if not (m == "F" and w.hier and w.full_blocks_only):
+            attn_layers += 1
+    return scan + attn_layers * w.R * per_attn, scan, attn_layers
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_src):
+    """HBM bytes per launch of the scan kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "index_score_scan_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        if d.get("src_sha") != src_sha(kernel_src):
+            return None
+        return float(d["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, rows):
+    """The oracle, untuned, on a bounded sample: `rows` query rows through every
+    layer of the group (scan + Top-512 + attention per layer), one thread."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    from fp4_kv_cache_02_amd import synth
+    from oracle import csa2_oracle as O
+
+    rows = list(range(min(rows, w.R)))
+    n_slots, pt, _ = synth.slots_layout(w)
+    # only the sampled rows' data is materialised (the oracle reads nothing else)
+    K = np.zeros((n_slots, 64), np.uint16)
+    q_full = synth.gen_q_idx(w, 0) if w.planted > 0 else None
+    P = np.zeros((n_slots, 256), np.uint8)
+    S = np.zeros((n_slots, 32), np.uint8)
+    if w.kv_pool:
+        pool_p, pool_s = O.quantize_fp4(synth.gen_kv_pool(w))
+    for b in rows:
+        L = w.seq_lens[b]
+        sl = synth.slot_index(w, pt, b, np.arange(L))
+        K[sl] = synth.gen_k_idx_seq(w, b, q_full)
+        if w.kv_pool:
+            m = synth.gen_kv_pool_map(w, b)
+            P[sl], S[sl] = pool_p[m], pool_s[m]
+        else:
+            P[sl], S[sl] = O.quantize_fp4(synth.gen_kv_values(w, b, 0, L))
+    cache = O.Cache(P, S, K, w.seq_lens, pt, 64, 0 if w.paged else w.n_max)
+    layer_in = []
+    for li, m in enumerate(w.schedule):
+        k, v, _, st, ln = synth.gen_swa(w, li)
+        layer_in.append((synth.gen_q_idx(w, li) if m in "FI" else None, synth.gen_q(w, li), k, v, st, ln))
+    state = O.GroupState(w.R)
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    attended = 0
+    for li, m in enumerate(w.schedule):
+        qi, q, k, v, st, ln = layer_in[li]
+        blocks_only = m == "F" and w.hier and w.full_blocks_only
+        O.layer_step(synth.MODES[m], cache, state, list(range(w.R)), qi, q, k, v, st, ln,
+                     1.0 / math.sqrt(512), hier=w.hier, blocks_only=blocks_only, rows=rows)
+        attended += 0 if blocks_only else len(rows)
+    dt = time.perf_counter() - t0
+    if ctx is not None:
+        ctx.restore_original_limits()
+    return {"value": attended / dt, "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.R} rows through all {len(w.schedule)} layers of the group "
+                      f"({attended} row-layers), {dt:.1f} s, 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU design "
+                                   "(sequence- or context-parallel) is not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 3}))
+        return
+
+    from fp4_kv_cache_02_amd import csa2, group, synth
+
+    w = synth.workload(args.config)
+    t_setup = time.perf_counter()
+    base = group.build_inputs(w)
+    reps = [base]
+    # extra replicas of the per-position caches (the per-layer inputs are small)
+    for _ in range(max(0, args.replicas - 1)):
+        reps.append(group.GroupInputs(kv_fp4=base.kv_fp4.clone(), kv_scale=base.kv_scale.clone(),
+                                      k_idx=base.k_idx.clone(), seq_len=base.seq_len, page_table=base.page_table,
+                                      seq_stride=base.seq_stride, row_seq=base.row_seq, layers=base.layers))
+    runners = [group.GroupRunner(w, inp) for inp in reps]
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        runners[i % len(runners)].step()
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        runners[i % len(runners)].step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    algo, scan_bytes, attn_layers = algorithmic_bytes(w)
+    value = w.R * attn_layers / (ms * 1e-3)
+
+    # dominant kernel: the Full layer's indexer scan, launched exactly as in the
+    # step (same entry point, arguments and grid), timed per launch with events
+    li_full = w.schedule.index("F")
+    kern_ms = []
+    for i in range(max(5, args.steps)):
+        r = runners[i % len(runners)]
+        L = r.inp.layers[li_full]
+        scores = torch.empty((w.R, w.n_max), dtype=torch.float32, device="cuda")
+        bmax = torch.empty((w.R, (w.n_max + 7) // 8), dtype=torch.float32, device="cuda") if w.hier else None
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        csa2.csa2_index_score(L.q_idx, r.kidx, r.inp.seq_len, scores, row_seq=r.inp.row_seq, n_max=w.n_max,
+                              block_max=bmax)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            kern_ms.append(a.elapsed_time(b))
+    kern_ms = float(np.mean(kern_ms))
+    scan_algo = sum(128 * L + 512 for L in w.seq_lens)   # indexer keys + query, per launch
+    achieved = scan_algo / (kern_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(os.path.join(ROOT, "fp4_kv_cache_02_amd", "csrc", "index_score.hip"))
+
+    out = {
+        "metric": "CSA2 decode tokens/s/layer + % of HBM roofline at 128K and 1M ctx",
+        "value": value,
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4(e2m1)+e4m3 main KV, bf16 indexer/query/window, f32 accumulate",
+        "data": "synthetic (seeded; N(0,1) main KV quantised on the GPU, 1% planted indexer keys)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.n_max, "layers": w.schedule,
+                   "topk": 512, "window": 128, "replicas": len(runners)},
+        "step_algorithmic_bytes": algo,
+        "step_gbps": algo / (ms * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"kernel": "index_score_kernel (Full-layer scan)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": scan_algo, "avg_launch_ms": kern_ms},
+        "setup_s": t_setup,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

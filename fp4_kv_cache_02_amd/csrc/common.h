@@ -1,0 +1,70 @@
+// Shared device helpers for the CSA2 kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+#define CSA2_DEV __device__ __forceinline__
+
+namespace csa2 {
+
+constexpr int kWave = 64;
+
+// Order-preserving key of a float32 score: larger score -> larger key, -0 < +0.
+// Key 0 is reserved for "absent" (it would be a NaN bit pattern); -inf, the
+// marker of an absent entry, is mapped to it as well.
+CSA2_DEV uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (s == -__builtin_inff()) ? 0u : k;
+}
+CSA2_DEV float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Physical slot of position p of sequence b (-1 when outside the cache).
+struct SlotMap {
+  const int32_t* page_table;
+  int64_t seq_stride;
+  int64_t n_slots;
+  int32_t max_pages;
+  CSA2_DEV int64_t operator()(int b, int64_t p) const {
+    int64_t s;
+    if (page_table) {
+      int64_t pg = p >> 6;
+      if (pg >= max_pages) return -1;
+      int32_t phys = page_table[(int64_t)b * max_pages + pg];
+      s = (int64_t)phys * 64 + (p & 63);
+    } else {
+      s = (int64_t)b * seq_stride + p;
+    }
+    return (s >= 0 && s < n_slots) ? s : -1;
+  }
+};
+
+inline SlotMap make_slot_map(const csa2_cache& c) {
+  SlotMap m;
+  m.page_table = c.page_table;
+  m.seq_stride = c.seq_stride;
+  m.n_slots = c.n_slots;
+  m.max_pages = c.max_pages;
+  return m;
+}
+
+// bf16 bit pattern -> float (exact).
+CSA2_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+CSA2_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// E4M3 (OCP E4M3FN) byte -> float, exact: the bits are placed in a float32
+// whose exponent field is the E4M3 exponent, then rescaled by 2^120 (bias 127
+// -> 7); exponent 0 lands in float32's subnormal range and scales correctly.
+CSA2_DEV float e4m3_to_float(uint32_t c) {
+  float v = __uint_as_float(((c & 0x7Fu) << 20)) * 0x1p120f;
+  return (c & 0x80u) ? -v : v;
+}
+
+CSA2_DEV int lane_id() { return __lane_id(); }
+
+}  // namespace csa2

@@ -111,8 +111,8 @@ def workload(cfg: int, reduced: bool = False) -> Workload:
                         full_blocks_only=True, kv_pool=65536)
     if cfg == 3:
         if reduced:
-            return Workload("cfg3_reduced_prefill_F5R_C256_E8192", seed, [8192], "FRRRRR",
-                            prefill_rows=256, prefill_pos=16384, raw_fp4=True)
+            return Workload("cfg3_reduced_prefill_F5R_C64_E8192", seed, [8192], "FRRRRR",
+                            prefill_rows=64, prefill_pos=16384, raw_fp4=True)
         return Workload("cfg3_prefill_F5R_C4096_E131072", seed, [131072], "FRRRRR",
                         prefill_rows=4096, prefill_pos=262144, raw_fp4=True)
     if cfg == 4:

@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every entry point its header declares, and
+rejects bad arguments on the host before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def C():
+    from fp4_kv_cache_02_amd import csa2
+    return csa2
+
+
+def test_every_declared_symbol_is_exported(C):
+    names = _declared()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(C.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(C.EXPORTED)
+
+
+def test_status_strings_and_version(C):
+    for s in range(6):
+        assert C.csa2_status_string(s)
+    assert C.csa2_status_string(0) == "ok"
+    assert "gfx950" in C.csa2_version()
+
+
+def test_workspace_sizes_are_monotone(C):
+    a = C.csa2_workspace_bytes(C.FULL, 8, 131072, False)
+    b = C.csa2_workspace_bytes(C.FULL, 8, 131072, True)
+    c = C.csa2_workspace_bytes(C.REUSE, 8, 131072, False)
+    assert 0 < c < a < b
+    assert C.csa2_workspace_bytes(C.FULL, 16, 131072, False) > a
+    assert C.csa2_topk_workspace_bytes(8, 131072, 512) > C.csa2_topk_workspace_bytes(8, 4096, 512)
+    assert C.csa2_attn_workspace_bytes(16) > C.csa2_attn_workspace_bytes(8)
+
+
+def _lib(C):
+    return ctypes.CDLL(C.LIB_PATH)
+
+
+def test_host_validation_errors(C):
+    lib = _lib(C)
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    cache = C.csa2_cache()
+    # NULL inputs
+    lib.csa2_index_score.restype = ctypes.c_int
+    lib.csa2_index_score.argtypes = C._index_score.argtypes
+    assert lib.csa2_index_score(None, None, ctypes.byref(cache), None, None, None, 0, 1, 16, None, None, None) \
+        == 1
+    cache.data = 0x1000
+    cache.n_slots = 16
+    # R out of range
+    assert lib.csa2_index_score(fake, None, ctypes.byref(cache), None, fake, None, 0, 0, 16, fake, None,
+                                None) == 2
+    # too many candidate blocks
+    assert lib.csa2_index_score(fake, None, ctypes.byref(cache), None, fake, fake, 4096, 1, 16, fake, None,
+                                None) == 2
+    # unsupported: block maxima with candidates
+    assert lib.csa2_index_score(fake, None, ctypes.byref(cache), None, fake, fake, 8, 1, 16, fake, fake,
+                                None) == 3
+    # paged cache with a page size other than 64
+    cache.page_table = 0x1000
+    cache.page_size = 32
+    cache.max_pages = 4
+    assert lib.csa2_index_score(fake, None, ctypes.byref(cache), None, fake, None, 0, 1, 16, fake, None,
+                                None) == 1
+    # Top-k: k out of range, missing workspace, too small workspace
+    assert C._topk(fake, 16, None, None, 1, 16, 0, None, fake, fake, 1 << 30, None) == 2
+    assert C._topk(fake, 16, None, None, 1, 16, 4096, None, fake, fake, 1 << 30, None) == 2
+    assert C._topk(fake, 16, None, None, 1, 16, 8, None, fake, None, 0, None) == 4
+    assert C._topk(fake, 1 << 20, None, None, 4, 1 << 20, 512, None, fake, fake, 1024, None) == 4
+    # stride smaller than the row
+    assert C._topk(fake, 8, None, None, 1, 16, 8, None, fake, fake, 1 << 30, None) == 2
+    # attention: k above 512, NULL window
+    kv = C.csa2_cache()
+    kv.data, kv.scale, kv.n_slots = 0x1000, 0x1000, 16
+    assert C._attn(fake, ctypes.byref(kv), None, fake, fake, 513, fake, fake, 128, fake, fake, 0.1, 1, fake,
+                   None, fake, 1 << 30, None) == 2
+    assert C._attn(fake, ctypes.byref(kv), None, fake, fake, 512, None, fake, 128, fake, fake, 0.1, 1, fake,
+                   None, fake, 1 << 30, None) == 1
+    # main KV without scales
+    kv.scale = None
+    assert C._attn(fake, ctypes.byref(kv), None, fake, fake, 512, fake, fake, 128, fake, fake, 0.1, 1, fake,
+                   None, fake, 1 << 30, None) == 1
+    # layer step: bad mode, missing workspace
+    a = C.csa2_layer_args()
+    s = C.csa2_shared()
+    assert C._layer(7, ctypes.byref(a), ctypes.byref(s), None, 0, None) == 3
+    a.R = 1
+    s.B, s.n_max = 1, 16
+    s.seq_len = s.topk_idx = 0x1000
+    s.kv.data, s.kv.scale, s.kv.n_slots = 0x1000, 0x1000, 16
+    a.q = a.swa_k = a.swa_v = a.swa_start = a.swa_len = a.out = 0x1000
+    assert C._layer(C.REUSE, ctypes.byref(a), ctypes.byref(s), None, 0, None) == 4
+    assert C._layer(C.REUSE, ctypes.byref(a), ctypes.byref(s), fake, 100, None) == 4
+    # Full needs an indexer query
+    assert C._layer(C.FULL, ctypes.byref(a), ctypes.byref(s), fake, 1 << 40, None) == 1
+    # quantiser: negative count; workspace init with a tiny buffer
+    assert C._quant(fake, -1, None, fake, fake, 16, None) == 2
+    assert C._quant(fake, 32, None, fake, fake, 16, None) == 2
+    assert C._ws_init(fake, 16, None) == 4
+    assert C._ws_init(None, 1 << 20, None) == 1

@@ -1,0 +1,75 @@
+"""End-to-end parity of CSA2 layer groups (csa2_layer_step) against the oracle,
+on the five workloads at reduced sizes (same structure: schedules, planted
+keys, hierarchical candidates, paging, prefill rows).  Indices and candidate
+blocks bit-exact after every layer; outputs within 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_02_amd import synth
+from oracle import csa2_oracle as O
+from tests.gpu_util import ATTN_TOL, host, lse_ok, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def numpy_caches(w):
+    """Main KV (quantised by the oracle from the seeded N(0,1) values, or raw
+    FP4 bytes) and indexer keys at their slots."""
+    n_slots, pt, _ = synth.slots_layout(w)
+    if w.raw_fp4:
+        P, S = synth.gen_fp4_raw(w, n_slots)
+    else:
+        P = np.zeros((n_slots, 256), np.uint8)
+        S = np.zeros((n_slots, 32), np.uint8)
+        for b in range(w.B):
+            L = w.seq_lens[b]
+            p, s = O.quantize_fp4(synth.gen_kv_values(w, b, 0, L))
+            sl = synth.slot_index(w, pt, b, np.arange(L))
+            P[sl], S[sl] = p, s
+    from fp4_kv_cache_02_amd.group import k_idx_slots_from_synth
+    K = k_idx_slots_from_synth(w, n_slots, pt)
+    return P, S, K, pt, n_slots
+
+
+def run_and_compare(w, check_rows=None):
+    from fp4_kv_cache_02_amd import group
+    P, S, K, pt, n_slots = numpy_caches(w)
+    inp = group.build_inputs(w, kv_fp4=P, kv_scale=S)
+    run = group.GroupRunner(w, inp)
+    cache = O.Cache(P, S, K, w.seq_lens, pt, 64, 0 if w.paged else w.n_max)
+    row_seq = np.zeros(w.R, np.int64) if w.prefill_rows else np.arange(w.R)
+    state = O.GroupState(w.R)
+    rows = list(range(w.R)) if check_rows is None else check_rows
+    for li, m in enumerate(w.schedule):
+        say(w.name, "layer", li, m)
+        run.step_layer(li)
+        torch.cuda.synchronize()
+        k, v, _, st, ln = synth.gen_swa(w, li)
+        qi = synth.gen_q_idx(w, li) if m in "FI" else None
+        q = synth.gen_q(w, li)
+        blocks_only = m == "F" and w.hier and w.full_blocks_only
+        res = O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln, group.SM_SCALE,
+                           hier=w.hier, blocks_only=blocks_only, rows=rows)
+        if m == "F" and w.hier:
+            gc = host(run.cand)
+            for r in rows:
+                assert np.array_equal(gc[r], state.cand[r]), (w.name, li, r)
+        if blocks_only:
+            continue
+        gt = host(run.topk_idx)
+        go, gl = host(run.out[li]), host(run.lse[li])
+        for r in rows:
+            assert np.array_equal(gt[r], state.topk[r]), (w.name, li, r)
+            e = rel_err(go[r], res[r][0])
+            assert np.all(e <= ATTN_TOL), (w.name, li, r, e.max())
+            assert lse_ok(gl[r], res[r][1]), (w.name, li, r)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
+def test_group_reduced(cfg):
+    run_and_compare(synth.workload(cfg, reduced=True))
+
+
+def test_group_prefill_reduced():
+    run_and_compare(synth.workload(3, reduced=True))
