@@ -18,12 +18,21 @@ using namespace csa2;
 namespace {
 
 constexpr size_t kAlign = 256;
-// control words: topk tickets, attention tickets (must be zero between calls)
-constexpr size_t kCtrlTopk = 0;
-constexpr size_t kCtrlAttn = (size_t)CSA2_MAX_ROWS * 4;
-constexpr size_t kCtrlBytes = (size_t)CSA2_MAX_ROWS * 8;
+// reserved control words at the start of every workspace (zeroed by
+// csa2_workspace_init; no kernel of this version uses them)
+constexpr size_t kCtrlBytes = kAlign;
+constexpr int64_t kSelCapHost = 16384;        // values one Top-k block holds
+constexpr int64_t kMaxTopkN = kSelCapHost * 64;  // two levels of maxima
+
+#ifdef CSA2_TRACE
+uint64_t* g_trace[3] = {nullptr, nullptr, nullptr};   // scan, top-k, attention
+#define CSA2_SET_TRACE(args, which) (args).trace = g_trace[which]
+#else
+#define CSA2_SET_TRACE(args, which) (void)0
+#endif
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Bump {
   char* base;
@@ -36,42 +45,6 @@ struct Bump {
   }
 };
 
-struct TopkWs {
-  uint32_t* cand_key;
-  int32_t* cand_idx;
-  int32_t* seg_info;
-};
-
-TopkWs carve_topk(Bump& bp, int R, int n_max, int k) {
-  const int S = topk_segments(n_max);
-  const int kcap = topk_kcap(k);
-  TopkWs t;
-  if (S <= 1) {  // single segment per row: selection is direct, no candidates
-    t.cand_key = nullptr;
-    t.cand_idx = nullptr;
-    t.seg_info = nullptr;
-    return t;
-  }
-  t.cand_key = bp.take<uint32_t>((size_t)R * S * kcap);
-  t.cand_idx = bp.take<int32_t>((size_t)R * S * kcap);
-  t.seg_info = bp.take<int32_t>((size_t)R * S * 4);
-  return t;
-}
-
-struct AttnWs {
-  float* part_o;
-  float* part_ml;
-  int n_main, n_splits;
-};
-
-AttnWs carve_attn(Bump& bp, int R, int k) {
-  AttnWs w;
-  w.n_splits = attn_splits(k, &w.n_main);
-  w.part_o = bp.take<float>((size_t)R * w.n_splits * 16 * 512);
-  w.part_ml = bp.take<float>((size_t)R * w.n_splits * 32);
-  return w;
-}
-
 bool cache_ok(const csa2_cache* c, bool need_scale) {
   if (!c || !c->data) return false;
   if (need_scale && !c->scale) return false;
@@ -83,9 +56,11 @@ bool cache_ok(const csa2_cache* c, bool need_scale) {
 
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
+// ---------------------------------------------------------------- scoring --
+
 csa2_status do_index_score(const uint16_t* q_idx, const float* head_w, const csa2_cache* k_idx,
                            const int32_t* row_seq, const int32_t* seq_len, const int32_t* cand,
-                           int32_t n_cand, int32_t R, int32_t n_max, float* scores, float* bmax,
+                           int32_t n_cand, int32_t R, int32_t n_max, float* scores, float* bmax, float* max64,
                            hipStream_t st) {
   IdxArgs a;
   a.q32 = (const uint32_t*)q_idx;
@@ -98,46 +73,143 @@ csa2_status do_index_score(const uint16_t* q_idx, const float* head_w, const csa
   a.n_cand = n_cand;
   a.R = R;
   a.n_max = n_max;
-  a.tiles_per_row = cand ? (n_cand * 8 + 255) / 256 : (n_max + 255) / 256;
+  a.steps_per_row = cand ? (int32_t)cdiv(n_cand, 8) : (int32_t)cdiv(n_max, 64);
   a.score_stride = cand ? (int64_t)n_cand * 8 : n_max;
-  a.bmax_stride = (n_max + 7) / 8;
+  a.bmax_stride = cdiv(n_max, 8);
+  a.max64_stride = cdiv(n_max, 64);
   a.scores = scores;
   a.block_max = bmax;
+  a.max64 = max64;
+  CSA2_SET_TRACE(a, 0);
   return hip_status(launch_index_score(a, cand != nullptr, head_w != nullptr, bmax != nullptr, st));
 }
 
-csa2_status do_topk(const float* scores, int64_t stride, const int32_t* row_seq, const int32_t* n_valid,
-                    int n_div, int R, int n_max, int k, const int32_t* cand_blocks, int cand_stride,
-                    int32_t* out, const TopkWs& tw, char* ws, hipStream_t st) {
+// ------------------------------------------------------------------ top-k --
+
+// Levels of maxima a Top-k over n values needs beyond level 0.
+int topk_levels_needed(int64_t n) {
+  if (n <= kSelCapHost) return 0;
+  if (cdiv(n, 8) <= kSelCapHost) return 1;
+  return 2;
+}
+
+struct TopkWs {
+  float* lv1;
+  float* lv2;
+};
+
+// Workspace for the levels of maxima a generic Top-k must build itself.
+TopkWs carve_topk(Bump& bp, int R, int64_t n_max) {
+  TopkWs t{nullptr, nullptr};
+  const int need = topk_levels_needed(n_max);
+  if (need >= 1) t.lv1 = bp.take<float>((size_t)R * cdiv(n_max, 8));
+  if (need >= 2) t.lv2 = bp.take<float>((size_t)R * cdiv(n_max, 64));
+  return t;
+}
+
+size_t topk_region(int R, int64_t n_max) {
+  Bump bp{nullptr, 0};
+  carve_topk(bp, R, n_max);
+  return bp.off;
+}
+
+TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, const int32_t* n_valid, int n_div,
+                   int R, int n_max, int k, int32_t* out) {
   TopkArgs a;
-  a.scores = scores;
-  a.row_stride = stride;
+  a.lv[0] = lv0;
+  a.lv[1] = a.lv[2] = nullptr;
+  a.lv_stride[0] = stride;
+  a.lv_stride[1] = cdiv(n_max, 8);
+  a.lv_stride[2] = cdiv(n_max, 64);
   a.row_seq = row_seq;
   a.n_valid = n_valid;
-  a.n_max = n_max;
   a.n_div = n_div;
+  a.n_max = n_max;
   a.R = R;
   a.k = k;
-  a.S_max = topk_segments(n_max);
-  a.kcap = topk_kcap(k);
-  a.cand_blocks = cand_blocks;
-  a.cand_stride = cand_stride;
+  a.cand_blocks = nullptr;
+  a.cand_stride = 0;
   a.out = out;
   a.out_stride = k;
-  a.cand_key = tw.cand_key;
-  a.cand_idx = tw.cand_idx;
-  a.seg_info = tw.seg_info;
-  a.ticket = (uint32_t*)(ws + kCtrlTopk);
+  return a;
+}
+
+// Builds the missing levels of maxima into the workspace, then selects.
+csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
+  const int need = topk_levels_needed(a.n_max);
+  for (int l = 1; l <= need; ++l) {
+    if (a.lv[l]) continue;
+    float* dst = (l == 1) ? tw.lv1 : tw.lv2;
+    MaximaArgs m;
+    m.in = a.lv[l - 1];
+    m.in_stride = a.lv_stride[l - 1];
+    m.out = dst;
+    m.out_stride = a.lv_stride[l];
+    m.n_out_max = a.lv_stride[l];
+    m.div_in = (l == 1) ? 1 : 8;
+    m.row_seq = a.row_seq;
+    m.n_valid = a.n_valid;
+    m.n_div = a.n_div;
+    m.n_max = a.n_max;
+    m.R = a.R;
+    hipError_t e = launch_maxima(m, st);
+    if (e != hipSuccess) return CSA2_ERR_HIP;
+    a.lv[l] = dst;
+  }
+  CSA2_SET_TRACE(a, 1);
   return hip_status(launch_topk(a, st));
 }
 
-csa2_status do_attn(const uint16_t* q, const csa2_cache* kv, const int32_t* row_seq,
-                    const int32_t* seq_len, const int32_t* idx, int32_t k, const uint16_t* swa_k,
-                    const uint16_t* swa_v, int32_t S, const int32_t* swa_start, const int32_t* swa_len,
-                    float sm_scale, int32_t R, float* out, float* lse, const AttnWs& aw, char* ws,
-                    hipStream_t st) {
+// -------------------------------------------------------------- attention --
+
+struct AttnWs {
+  float* part_o;
+  float* part_ml;
+  int n_blocks, cpb;
+};
+
+AttnWs carve_attn(Bump& bp, int R, int n_layers, int k) {
+  AttnWs w;
+  w.n_blocks = attn_blocks(k, R * n_layers, &w.cpb);
+  if (w.n_blocks > 1) {
+    w.part_o = bp.take<float>((size_t)n_layers * R * w.n_blocks * 16 * 512);
+    w.part_ml = bp.take<float>((size_t)n_layers * R * w.n_blocks * 32);
+  } else {
+    w.part_o = w.part_ml = nullptr;
+  }
+  return w;
+}
+
+size_t attn_region(int R, int n_layers, int k) {
+  Bump bp{nullptr, 0};
+  carve_attn(bp, R, n_layers, k);
+  return bp.off;
+}
+
+struct AttnLayerIn {
+  const uint16_t *q, *swa_k, *swa_v;
+  int32_t S;
+  const int32_t *swa_start, *swa_len;
+  float *out, *lse;
+  float sm_scale;
+};
+
+csa2_status do_attn(const AttnLayerIn* L, int n_layers, const csa2_cache* kv, const int32_t* row_seq,
+                    const int32_t* seq_len, const int32_t* idx, int32_t k, int32_t R,
+                    const AttnWs& aw, char* ws, hipStream_t st) {
   AttnArgs a;
-  a.q = (const uint4*)q;
+  for (int i = 0; i < n_layers; ++i) {
+    a.layer[i].q = (const uint4*)L[i].q;
+    a.layer[i].swa_k = (const uint4*)L[i].swa_k;
+    a.layer[i].swa_v = (const uint4*)L[i].swa_v;
+    a.layer[i].swa_start = L[i].swa_start;
+    a.layer[i].swa_len = L[i].swa_len;
+    a.layer[i].out = L[i].out;
+    a.layer[i].lse = L[i].lse;
+    a.layer[i].S = L[i].S;
+    a.layer[i].sm_scale = L[i].sm_scale;
+  }
+  a.n_layers = n_layers;
   a.kv = (const uint8_t*)kv->data;
   a.kv_scale = kv->scale;
   a.map = make_slot_map(*kv);
@@ -145,38 +217,102 @@ csa2_status do_attn(const uint16_t* q, const csa2_cache* kv, const int32_t* row_
   a.seq_len = seq_len;
   a.idx = idx;
   a.k = k;
-  a.swa_k = (const uint4*)swa_k;
-  a.swa_v = (const uint4*)swa_v;
-  a.S = S;
-  a.swa_start = swa_start;
-  a.swa_len = swa_len;
-  a.sm_scale = sm_scale;
   a.R = R;
-  a.out = out;
-  a.lse = lse;
+  a.n_blocks = aw.n_blocks;
+  a.steps_per_block = aw.cpb;
   a.part_o = aw.part_o;
   a.part_ml = aw.part_ml;
-  a.ticket = (uint32_t*)(ws + kCtrlAttn);
-  a.n_main_splits = aw.n_main;
-  a.n_splits = aw.n_splits;
+  CSA2_SET_TRACE(a, 2);
   return hip_status(launch_attn(a, st));
 }
 
-size_t topk_region(int R, int n_max, int k) {
+bool attn_layer_ok(const csa2_layer_args* a) {
+  return a->q && a->swa_k && a->swa_v && a->swa_start && a->swa_len && a->out && a->S >= 0;
+}
+
+AttnLayerIn layer_in(const csa2_layer_args* a) {
+  return AttnLayerIn{a->q, a->swa_k, a->swa_v, a->S, a->swa_start, a->swa_len, a->out, a->lse, a->sm_scale};
+}
+
+// ------------------------------------------------------- layer index part --
+
+// Workspace of the indexer part of a layer in `mode` (scores, maxima, Top-k levels).
+size_t index_region(csa2_mode mode, int R, int n_max, int hier) {
   Bump bp{nullptr, 0};
-  carve_topk(bp, R, n_max, k);
+  if (mode == CSA2_FULL || (mode == CSA2_REINDEX && !hier)) {
+    bp.take<float>((size_t)R * n_max);
+    bp.take<float>((size_t)R * cdiv(n_max, 8));
+    bp.take<float>((size_t)R * cdiv(n_max, 64));
+  } else if (mode == CSA2_REINDEX) {
+    bp.take<float>((size_t)R * CSA2_KEEP_BLOCKS * 8);
+  }
   return bp.off;
 }
 
-size_t attn_region(int R, int k) {
-  Bump bp{nullptr, 0};
-  carve_attn(bp, R, k);
-  return bp.off;
+// Scoring + selection of a Full or Reindex layer; leaves the Top-512 in
+// shared->topk_idx (and the candidate blocks of a hierarchical Full layer in
+// shared->cand_blocks).
+csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_shared* sh, Bump& bp, bool blocks_only,
+                      hipStream_t st) {
+  const int R = a->R, n_max = sh->n_max;
+  csa2_status s;
+  if (mode == CSA2_FULL || (mode == CSA2_REINDEX && !sh->hier)) {
+    float* scores = bp.take<float>((size_t)R * n_max);
+    float* bmax = bp.take<float>((size_t)R * cdiv(n_max, 8));
+    float* m64 = bp.take<float>((size_t)R * cdiv(n_max, 64));
+    s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max, scores,
+                       bmax, m64, st);
+    if (s) return s;
+    if (!blocks_only) {
+      TopkArgs t = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
+      t.lv[1] = bmax;
+      t.lv[2] = m64;
+      s = run_topk(t, TopkWs{nullptr, nullptr}, st);
+      if (s) return s;
+    }
+    if (mode == CSA2_FULL && sh->hier) {
+      const int nb = (int)cdiv(n_max, 8);
+      TopkArgs t = topk_args(bmax, nb, a->row_seq, sh->seq_len, 8, R, nb, CSA2_KEEP_BLOCKS, sh->cand_blocks);
+      t.lv[1] = m64;     // maxima of 8 block maxima
+      t.lv_stride[1] = cdiv(n_max, 64);
+      s = run_topk(t, TopkWs{nullptr, nullptr}, st);
+      if (s) return s;
+    }
+    return CSA2_OK;
+  }
+  // Reindex over the candidate blocks of the last (hierarchical) Full layer
+  const int nc = CSA2_KEEP_BLOCKS * 8;
+  float* scores = bp.take<float>((size_t)R * nc);
+  s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, sh->cand_blocks, CSA2_KEEP_BLOCKS,
+                     R, n_max, scores, nullptr, nullptr, st);
+  if (s) return s;
+  TopkArgs t = topk_args(scores, nc, nullptr, nullptr, 1, R, nc, CSA2_TOPK, sh->topk_idx);
+  t.cand_blocks = sh->cand_blocks;
+  t.cand_stride = CSA2_KEEP_BLOCKS;
+  return run_topk(t, TopkWs{nullptr, nullptr}, st);
+}
+
+csa2_status check_shared(const csa2_shared* sh, int R) {
+  if (!sh) return CSA2_ERR_NULL;
+  if (R < 1 || R > CSA2_MAX_ROWS || sh->n_max < 0 || sh->B < 1) return CSA2_ERR_SHAPE;
+  if (sh->n_max > kMaxTopkN) return CSA2_ERR_UNSUPPORTED;
+  if (!sh->seq_len || !sh->topk_idx) return CSA2_ERR_NULL;
+  if (!cache_ok(&sh->kv, true)) return CSA2_ERR_NULL;
+  if (sh->kv.n_slots > 0x7FFFFFFFll) return CSA2_ERR_UNSUPPORTED;
+  return CSA2_OK;
 }
 
 }  // namespace
 
 extern "C" {
+
+#ifdef CSA2_TRACE
+// Tuning builds only: device buffers that receive phase timestamps of the
+// scan (0), Top-k (1) and attention (2) kernels; NULL stops recording.
+void csa2_trace_set(int which, uint64_t* dev_buf) {
+  if (which >= 0 && which < 3) g_trace[which] = dev_buf;
+}
+#endif
 
 const char* csa2_status_string(csa2_status s) {
   switch (s) {
@@ -190,7 +326,7 @@ const char* csa2_status_string(csa2_status s) {
   return "unknown status";
 }
 
-const char* csa2_version(void) { return "csa2-gfx950 0.1"; }
+const char* csa2_version(void) { return "csa2-gfx950 0.2"; }
 
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!ws) return CSA2_ERR_NULL;
@@ -200,12 +336,12 @@ csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
 
 size_t csa2_topk_workspace_bytes(int32_t R, int32_t n_max, int32_t k) {
   if (R < 0 || n_max < 0 || k < 1) return 0;
-  return kCtrlBytes + topk_region(R, n_max, k);
+  return kCtrlBytes + topk_region(R, n_max);
 }
 
 size_t csa2_attn_workspace_bytes(int32_t R) {
   if (R < 0) return 0;
-  return kCtrlBytes + attn_region(R, CSA2_TOPK);
+  return kCtrlBytes + attn_region(R, 1, CSA2_TOPK);
 }
 
 csa2_status csa2_index_score(const uint16_t* q_idx, const float* head_w, const csa2_cache* k_idx,
@@ -219,8 +355,9 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* head_w, const c
     if (n_cand < 1 || n_cand > CSA2_KEEP_BLOCKS) return CSA2_ERR_SHAPE;
     if (block_max) return CSA2_ERR_UNSUPPORTED;
   }
-  return do_index_score(q_idx, head_w, k_idx, row_seq, seq_len, cand_blocks, n_cand, R, n_max, scores,
-                        block_max, stream);
+  if ((int64_t)R * (cand_blocks ? cdiv(n_cand, 8) : cdiv(n_max, 64)) > 0xFFFFFFFFll) return CSA2_ERR_SHAPE;
+  return do_index_score(q_idx, head_w, k_idx, row_seq, seq_len, cand_blocks, n_cand, R, n_max, scores, block_max,
+                        nullptr, stream);
 }
 
 csa2_status csa2_topk(const float* scores, int64_t row_stride, const int32_t* row_seq,
@@ -230,13 +367,17 @@ csa2_status csa2_topk(const float* scores, int64_t row_stride, const int32_t* ro
   if (!scores || !idx) return CSA2_ERR_NULL;
   if (R < 1 || R > CSA2_MAX_ROWS || n_max < 0 || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_SHAPE;
   if (row_stride < n_max) return CSA2_ERR_SHAPE;
+  if (n_max > kMaxTopkN) return CSA2_ERR_UNSUPPORTED;
   if (cand_blocks && n_max % 8) return CSA2_ERR_SHAPE;
+  if (cand_blocks && n_max > 8 * CSA2_KEEP_BLOCKS) return CSA2_ERR_UNSUPPORTED;
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_topk_workspace_bytes(R, n_max, k)) return CSA2_ERR_WORKSPACE;
   Bump bp{(char*)ws, kCtrlBytes};
-  TopkWs tw = carve_topk(bp, R, n_max, k);
-  return do_topk(scores, row_stride, row_seq, n_valid, 1, R, n_max, k, cand_blocks, n_max / 8, idx, tw,
-                 (char*)ws, stream);
+  const TopkWs tw = carve_topk(bp, R, n_max);
+  TopkArgs t = topk_args(scores, row_stride, row_seq, n_valid, 1, R, n_max, k, idx);
+  t.cand_blocks = cand_blocks;
+  t.cand_stride = n_max / 8;
+  return run_topk(t, tw, stream);
 }
 
 csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq, const int32_t* seq_len,
@@ -244,13 +385,13 @@ csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq,
                                  size_t ws_bytes, hipStream_t stream) {
   if (!block_max || !seq_len || !cand_blocks) return CSA2_ERR_NULL;
   if (R < 1 || R > CSA2_MAX_ROWS || n_max < 0 || keep < 1 || keep > CSA2_MAX_K) return CSA2_ERR_SHAPE;
-  const int nb = (n_max + 7) / 8;
+  if (n_max > kMaxTopkN) return CSA2_ERR_UNSUPPORTED;
+  const int nb = (int)cdiv(n_max, 8);
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_topk_workspace_bytes(R, nb, keep)) return CSA2_ERR_WORKSPACE;
   Bump bp{(char*)ws, kCtrlBytes};
-  TopkWs tw = carve_topk(bp, R, nb, keep);
-  return do_topk(block_max, nb, row_seq, seq_len, 8, R, nb, keep, nullptr, 0, cand_blocks, tw, (char*)ws,
-                 stream);
+  const TopkWs tw = carve_topk(bp, R, nb);
+  return run_topk(topk_args(block_max, nb, row_seq, seq_len, 8, R, nb, keep, cand_blocks), tw, stream);
 }
 
 csa2_status csa2_fp4_sparse_attn(const uint16_t* q, const csa2_cache* kv, const int32_t* row_seq,
@@ -262,12 +403,13 @@ csa2_status csa2_fp4_sparse_attn(const uint16_t* q, const csa2_cache* kv, const 
     return CSA2_ERR_NULL;
   if (!cache_ok(kv, true)) return CSA2_ERR_NULL;
   if (R < 1 || R > CSA2_MAX_ROWS || k < 1 || k > CSA2_TOPK || S < 0) return CSA2_ERR_SHAPE;
+  if (kv->n_slots > 0x7FFFFFFFll) return CSA2_ERR_UNSUPPORTED;
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_attn_workspace_bytes(R)) return CSA2_ERR_WORKSPACE;
   Bump bp{(char*)ws, kCtrlBytes};
-  AttnWs aw = carve_attn(bp, R, k);
-  return do_attn(q, kv, row_seq, seq_len, idx, k, swa_k, swa_v, S, swa_start, swa_len, sm_scale, R, out, lse,
-                 aw, (char*)ws, stream);
+  const AttnWs aw = carve_attn(bp, R, 1, k);
+  const AttnLayerIn L{q, swa_k, swa_v, S, swa_start, swa_len, out, lse, sm_scale};
+  return do_attn(&L, 1, kv, row_seq, seq_len, idx, k, R, aw, (char*)ws, stream);
 }
 
 csa2_status csa2_fp4_quantize(const float* x, int64_t n, const int64_t* dst_slot, uint8_t* fp4,
@@ -279,102 +421,62 @@ csa2_status csa2_fp4_quantize(const float* x, int64_t n, const int64_t* dst_slot
   return hip_status(launch_quant(x, n, dst_slot, fp4, scale, n_slots, stream));
 }
 
+size_t csa2_group_workspace_bytes(csa2_mode first_mode, int32_t n_layers, int32_t R, int32_t n_max, int32_t hier) {
+  if (R < 0 || n_max < 0 || n_layers < 1 || n_layers > CSA2_MAX_GROUP_LAYERS) return 0;
+  size_t off = kCtrlBytes;
+  off = align_up(off + index_region(first_mode, R, n_max, hier));
+  off = align_up(off + attn_region(R, n_layers, CSA2_TOPK));
+  return off;
+}
+
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t R, int32_t n_max, int32_t hier) {
-  if (R < 0 || n_max < 0) return 0;
-  Bump bp{nullptr, kCtrlBytes};
-  if (mode == CSA2_FULL) {
-    bp.take<float>((size_t)R * n_max);
-    if (hier) bp.take<float>((size_t)R * ((n_max + 7) / 8));
-    const size_t t1 = topk_region(R, n_max, CSA2_TOPK);
-    const size_t t2 = hier ? topk_region(R, (n_max + 7) / 8, CSA2_KEEP_BLOCKS) : 0;
-    bp.off = align_up(bp.off + std::max(t1, t2));
-  } else if (mode == CSA2_REINDEX) {
-    const int nc = hier ? CSA2_KEEP_BLOCKS * 8 : n_max;
-    bp.take<float>((size_t)R * nc);
-    bp.off = align_up(bp.off + topk_region(R, nc, CSA2_TOPK));
+  return csa2_group_workspace_bytes(mode, 1, R, n_max, hier);
+}
+
+csa2_status csa2_group_step(csa2_mode first_mode, int32_t n_layers, const csa2_layer_args* layers,
+                            const csa2_shared* sh, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!layers) return CSA2_ERR_NULL;
+  if (first_mode != CSA2_FULL && first_mode != CSA2_REINDEX && first_mode != CSA2_REUSE) return CSA2_ERR_UNSUPPORTED;
+  if (n_layers < 1 || n_layers > CSA2_MAX_GROUP_LAYERS) return CSA2_ERR_SHAPE;
+  const int R = layers[0].R;
+  csa2_status s = check_shared(sh, R);
+  if (s) return s;
+  const bool blocks_only = first_mode == CSA2_FULL && sh->hier && layers[0].blocks_only;
+  // attended layers: all, except a Full layer that only builds candidates
+  const int a0 = blocks_only ? 1 : 0;
+  for (int i = 0; i < n_layers; ++i) {
+    if (layers[i].R != R || layers[i].row_seq != layers[0].row_seq) return CSA2_ERR_SHAPE;
+    if (i >= a0 && !attn_layer_ok(&layers[i])) return CSA2_ERR_NULL;
   }
-  bp.off = align_up(bp.off + attn_region(R, CSA2_TOPK));
-  return bp.off;
+  if ((int64_t)R * n_layers > CSA2_MAX_ROWS) return CSA2_ERR_SHAPE;
+  if (first_mode != CSA2_REUSE) {
+    if (!layers[0].q_idx) return CSA2_ERR_NULL;
+    if (!cache_ok(&sh->k_idx, false)) return CSA2_ERR_NULL;
+    if (sh->hier && !sh->cand_blocks) return CSA2_ERR_NULL;
+  }
+  if (!ws) return CSA2_ERR_WORKSPACE;
+  if (ws_bytes < csa2_group_workspace_bytes(first_mode, n_layers, R, sh->n_max, sh->hier)) return CSA2_ERR_WORKSPACE;
+
+  char* w = (char*)ws;
+  Bump bp{w, kCtrlBytes};
+  if (first_mode != CSA2_REUSE) {
+    const size_t mark = bp.off;
+    s = run_index(first_mode, &layers[0], sh, bp, blocks_only, st);
+    if (s) return s;
+    bp.off = align_up(mark + index_region(first_mode, R, sh->n_max, sh->hier));
+  }
+  const int na = n_layers - a0;
+  if (na == 0) return CSA2_OK;
+  AttnLayerIn L[CSA2_MAX_GROUP_LAYERS];
+  for (int i = 0; i < na; ++i) L[i] = layer_in(&layers[a0 + i]);
+  const AttnWs aw = carve_attn(bp, R, na, CSA2_TOPK);
+  return do_attn(L, na, &sh->kv, layers[0].row_seq, sh->seq_len, sh->topk_idx, CSA2_TOPK, R, aw, w, st);
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, const csa2_shared* sh, void* ws,
                             size_t ws_bytes, hipStream_t st) {
   if (!a || !sh) return CSA2_ERR_NULL;
-  if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE) return CSA2_ERR_UNSUPPORTED;
-  const int R = a->R, n_max = sh->n_max;
-  if (R < 1 || R > CSA2_MAX_ROWS || n_max < 0 || sh->B < 1) return CSA2_ERR_SHAPE;
-  if (!sh->seq_len || !sh->topk_idx) return CSA2_ERR_NULL;
-  if (!cache_ok(&sh->kv, true)) return CSA2_ERR_NULL;
-  const bool blocks_only = mode == CSA2_FULL && sh->hier && a->blocks_only;
-  if (!blocks_only) {
-    if (!a->q || !a->swa_k || !a->swa_v || !a->swa_start || !a->swa_len || !a->out) return CSA2_ERR_NULL;
-    if (a->S < 0) return CSA2_ERR_SHAPE;
-  }
-  if (mode != CSA2_REUSE) {
-    if (!a->q_idx) return CSA2_ERR_NULL;
-    if (!cache_ok(&sh->k_idx, false)) return CSA2_ERR_NULL;
-  }
-  if (sh->hier && mode != CSA2_REUSE && !sh->cand_blocks) return CSA2_ERR_NULL;
-  if (!ws) return CSA2_ERR_WORKSPACE;
-  if (ws_bytes < csa2_workspace_bytes(mode, R, n_max, sh->hier)) return CSA2_ERR_WORKSPACE;
-
-  char* w = (char*)ws;
-  Bump bp{w, kCtrlBytes};
-  csa2_status s = CSA2_OK;
-  if (mode == CSA2_FULL) {
-    float* scores = bp.take<float>((size_t)R * n_max);
-    float* bmax = sh->hier ? bp.take<float>((size_t)R * ((n_max + 7) / 8)) : nullptr;
-    const size_t mark = bp.off;
-    s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max, scores,
-                       bmax, st);
-    if (s) return s;
-    if (!blocks_only) {
-      TopkWs tw = carve_topk(bp, R, n_max, CSA2_TOPK);
-      s = do_topk(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, nullptr, 0, sh->topk_idx, tw,
-                  w, st);
-      if (s) return s;
-    }
-    if (sh->hier) {
-      bp.off = mark;
-      const int nb = (n_max + 7) / 8;
-      TopkWs tw = carve_topk(bp, R, nb, CSA2_KEEP_BLOCKS);
-      s = do_topk(bmax, nb, a->row_seq, sh->seq_len, 8, R, nb, CSA2_KEEP_BLOCKS, nullptr, 0, sh->cand_blocks,
-                  tw, w, st);
-      if (s) return s;
-    }
-    bp.off = mark;
-    bp.off = align_up(bp.off + std::max(topk_region(R, n_max, CSA2_TOPK),
-                                        sh->hier ? topk_region(R, (n_max + 7) / 8, CSA2_KEEP_BLOCKS) : 0));
-    if (blocks_only) return CSA2_OK;
-  } else if (mode == CSA2_REINDEX) {
-    if (sh->hier) {
-      const int nc = CSA2_KEEP_BLOCKS * 8;
-      float* scores = bp.take<float>((size_t)R * nc);
-      s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, sh->cand_blocks,
-                         CSA2_KEEP_BLOCKS, R, n_max, scores, nullptr, st);
-      if (s) return s;
-      const size_t mark = bp.off;
-      TopkWs tw = carve_topk(bp, R, nc, CSA2_TOPK);
-      s = do_topk(scores, nc, nullptr, nullptr, 1, R, nc, CSA2_TOPK, sh->cand_blocks, CSA2_KEEP_BLOCKS,
-                  sh->topk_idx, tw, w, st);
-      if (s) return s;
-      bp.off = align_up(mark + topk_region(R, nc, CSA2_TOPK));
-    } else {
-      float* scores = bp.take<float>((size_t)R * n_max);
-      s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max,
-                         scores, nullptr, st);
-      if (s) return s;
-      const size_t mark = bp.off;
-      TopkWs tw = carve_topk(bp, R, n_max, CSA2_TOPK);
-      s = do_topk(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, nullptr, 0, sh->topk_idx, tw,
-                  w, st);
-      if (s) return s;
-      bp.off = align_up(mark + topk_region(R, n_max, CSA2_TOPK));
-    }
-  }
-  AttnWs aw = carve_attn(bp, R, CSA2_TOPK);
-  return do_attn(a->q, &sh->kv, a->row_seq, sh->seq_len, sh->topk_idx, CSA2_TOPK, a->swa_k, a->swa_v, a->S,
-                 a->swa_start, a->swa_len, a->sm_scale, R, a->out, a->lse, aw, w, st);
+  return csa2_group_step(mode, 1, a, sh, ws, ws_bytes, st);
 }
 
 }  // extern "C"

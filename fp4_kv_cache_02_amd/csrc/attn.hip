@@ -1,4 +1,4 @@
-// Sparse FP4 attention + sliding window (decode / generic rows).
+// Sparse FP4 attention + sliding window (decode rows and prefill-chunk rows).
 //
 // Every CSA2 layer combines global (sparse) attention over the selected Top-K
 // main-KV entries with a 128-token sliding window, using its own query
@@ -9,21 +9,35 @@
 // head over the union of both branches; the 512-d main-KV vector is both key
 // and value.
 //
-// Decomposition (flash-decoding): a block takes 16*NW keys of one row (main
-// keys or window keys, never mixed) and all 16 heads.  Per wave, 16 keys:
-//   S^T[16 keys x 16 heads] = K[16 x 512] * Q^T  with 16 MFMA 16x16x32 steps.
-//   Lane l loads key l%16, dims 128*(l/16) .. +127 (64 contiguous FP4 bytes +
-//   8 scale bytes, or 256 bytes of bf16); the K index of the MFMA walks those
-//   dims, and the query fragment uses the same dim order.
-// FP4 -> fp16 dequantisation is exact: the hardware E2M1 conversion (scale 1)
-// followed by an fp16 multiply by the E4M3 scale (products have <= 6
-// significant bits inside fp16's normal range).  Window keys stay bf16.
-// Softmax statistics per head over the block; P (fp32) is split into hi + lo
-// halves (fp16 for FP4 blocks, bf16 for window blocks) so that P*V keeps ~16+
-// bits; V^T is staged in LDS (dim-major, key column swizzled by dim/128) for
-// the P*V MFMA (O[16 heads x 512] = P[16 x keys] * V[keys x 512]).
-// Each block writes its unnormalised partial (O, max, sum); the last block of
-// a row (atomic ticket) merges all partials exactly as one softmax.
+// Work decomposition.  The keys of a (layer, row) are its k selected main-KV
+// entries followed by its window entries, cut into "steps" of 128 keys
+// (ceil(k/128) main steps, one window step).  A block of 4 waves processes
+// steps of one (layer, row):
+//   1. wave w computes the logits of keys 32w .. 32w+31 of the step for all 16
+//      heads: S^T[32 keys x 16 heads] = K Q^T as two 16-key MFMA groups
+//      (16x16x32, 16 steps over the 512 dims; lane (c, g) = (l % 16, l / 16)
+//      loads key 16u + c, dims 128g .. 128g+127, and reads the query fragment
+//      of head c from LDS);
+//   2. the block's softmax statistics per head are combined through LDS and
+//      P (split into hi + lo halves, so the product keeps ~22 (fp16) or 16
+//      (bf16) bits) is written to LDS as [16 heads x 128 keys];
+//   3. wave w computes O[16 heads x dims 128w .. 128w+127] = P V over all 128
+//      keys: 4 K-steps of 32 keys, 8 output tiles, tile j covering dims
+//      {128w + 8c + j : c = 0..15}, so lane (c, g) needs one 8-dim word of
+//      each of its 8 keys -- V is read straight from the cache in that layout.
+// A block that covers every step of its row (many rows) keeps an online
+// softmax over the steps and writes the output; otherwise (few rows: decode)
+// each block takes one step and writes a partial (O, max, sum), and
+// attn_merge_kernel combines the partials of each row as one softmax.  (A
+// cross-block hand-off inside one kernel would need a device-scope release,
+// which on this chip writes back the whole L2 of the issuing XCD.)  Several
+// layers that share the Top-K (a Full or Reindex layer and its Reuse layers)
+// run in one launch.
+//
+// FP4 -> fp16 is exact: the hardware E2M1 conversion at unit scale (the
+// conversion's own scale operand applies only a power of two), then an fp16
+// multiply by the E4M3 scale (products have <= 6 significant bits within
+// fp16's normal range).  Window steps use bf16 throughout.
 #include "kernels.h"
 
 namespace csa2 {
@@ -33,275 +47,444 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kAttnWaves = 4;
+constexpr int kStepKeys = 128;                  // keys per step (32 per wave)
+constexpr int kQRow = 65;                       // uint4 per head row of Q in LDS (64 + 1 pad)
+constexpr int kPRow = kStepKeys + 8;            // halves per head row of P in LDS
 
-CSA2_DEV half8_t dequant8(uint32_t word, uint32_t scale_byte) {
-  const _Float16 s = (_Float16)e4m3_to_float(scale_byte);
-  const half2_t sv = {s, s};
-  half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sv;
-  half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sv;
-  half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sv;
-  half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sv;
+struct AttnSmem {
+  uint4 qb[16 * kQRow];        // query, bf16
+  uint4 qh[16 * kQRow];        // query, fp16
+  uint16_t p_hi[16 * kPRow];
+  uint16_t p_lo[16 * kPRow];
+  int32_t slot[kStepKeys];     // slot of each main key of the step (-1: absent)
+  float red_m[kAttnWaves][16];
+  float red_l[kAttnWaves][16];
+};
+
+// byte `sel` of `word` (two E2M1 codes, low nibble first) as fp16 at unit scale;
+// sel is a compile-time constant after unrolling
+CSA2_DEV half2_t fp4x2(uint32_t word, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3);
+  }
+}
+CSA2_DEV uint32_t h2u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+CSA2_DEV uint32_t pack_lo(uint32_t x, uint32_t y) { return (x & 0xFFFFu) | (y << 16); }
+CSA2_DEV uint32_t pack_hi(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xFFFF0000u); }
+CSA2_DEV half2_t scale_h2(uint32_t code) {
+  const _Float16 s = (_Float16)e4m3_to_float(code);
+  return half2_t{s, s};
+}
+
+// 8 consecutive FP4 codes (one dword) times one E4M3 scale, as fp16 (exact).
+CSA2_DEV half8_t dequant8(uint32_t word, half2_t sv) {
+  const half2_t h0 = fp4x2(word, 0) * sv, h1 = fp4x2(word, 1) * sv;
+  const half2_t h2 = fp4x2(word, 2) * sv, h3 = fp4x2(word, 3) * sv;
   half8_t r;
   r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
   r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
   return r;
 }
 
-CSA2_DEV half8_t bf16x8_to_half8(uint4 v) {
+CSA2_DEV uint4 bf16x8_to_f16x8(uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  half8_t r;
+  uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[2 * i] = (_Float16)bf16_lo(w[i]);
-    r[2 * i + 1] = (_Float16)bf16_hi(w[i]);
+    const half2_t h = {(_Float16)bf16_lo(w[i]), (_Float16)bf16_hi(w[i])};
+    o[i] = h2u(h);
   }
-  return r;
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
-
 CSA2_DEV bf8_t as_bf8(uint4 v) { return __builtin_bit_cast(bf8_t, v); }
-CSA2_DEV uint16_t f32_to_bf16_rne(float f) {
+CSA2_DEV half8_t as_h8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
+CSA2_DEV uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return u >> 16;
+}
+CSA2_DEV float pick4(const float (&v)[4], int i) {
+  return (i == 0) ? v[0] : (i == 1) ? v[1] : (i == 2) ? v[2] : v[3];
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void fp4_attn_kernel(AttnArgs a) {
-  constexpr int KEYS = NW * 16;
-  constexpr int VTS = KEYS + 8;       // halves per V^T row (padding keeps 16-B alignment)
-  constexpr int PS = KEYS + 8;        // halves per P row
-  constexpr int TILES_PER_WAVE = 32 / NW;
-  __shared__ __attribute__((aligned(16))) uint16_t vt[512 * VTS];
-  __shared__ __attribute__((aligned(16))) uint16_t p_hi[16 * PS];
-  __shared__ __attribute__((aligned(16))) uint16_t p_lo[16 * PS];
-  __shared__ float red_m[NW][16];
-  __shared__ float red_l[NW][16];
-  __shared__ float ml[2][16];
-  __shared__ uint32_t s_last;
+// Per-wave running state over the steps of one (layer, row).
+struct RowState {
+  f32x4 o[8];      // O[head 4g+i][dim 128w + 8c + j] in o[j][i]
+  float m[4];      // running max of heads 4g+i (block-wide)
+  float l[4];      // running sum of heads 4g+i
+};
 
-  const int split = blockIdx.x, r = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-  const int b = a.row_seq ? a.row_seq[r] : r;
-  const int L = a.seq_len[b];
-  const bool is_main = split < a.n_main_splits;
-  const int key_local = w * 16 + c;
-
-  // query fragment: head c, dims 128g + 8t .. +7
-  const uint4* qrow = a.q + ((int64_t)r * 16 + c) * 64 + g * 16;
-  uint4 qf[16];
+// ---- phase 1: logits of this wave's 32 keys (lane (c, g): head c, keys sigma(g, e)) ----
+// sigma(g, e) = 4g + e (e < 4), 16 + 4g + e - 4 (e >= 4)
+CSA2_DEV void qk_main(const AttnArgs& a, const AttnSmem& sm, int slot, int c, int g, float (&s)[8]) {
+  const uint4* qrow = sm.qh + c * kQRow + 16 * g;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) qf[t] = qrow[t];
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  bool valid;
-  const int vcol = ((w ^ g) << 4) + c;   // swizzled V^T column of this lane's key
-  if (is_main) {
-    const int kk = split * KEYS + key_local;
-    const int pos = kk < a.k ? a.idx[(int64_t)r * a.k + kk] : -1;
-    const int64_t slot = (pos >= 0 && pos < L) ? a.map(b, pos) : -1;
-    valid = slot >= 0;
+  for (int u = 0; u < 2; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int32_t su = __shfl(slot, 16 * u + c, 64);
     uint4 raw[4];
     uint2 sc;
-    if (valid) {
-      const uint4* src = (const uint4*)(a.kv + slot * 256 + g * 64);
+    if (su >= 0) {
+      const uint4* src = (const uint4*)(a.kv + (int64_t)su * 256 + g * 64);
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[i] = src[i];
-      sc = *(const uint2*)(a.kv_scale + slot * 32 + g * 8);
+      sc = *(const uint2*)(a.kv_scale + (int64_t)su * 32 + g * 8);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[i] = make_uint4(0, 0, 0, 0);
       sc = make_uint2(0, 0);
     }
-    const uint32_t rw[16] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y,
-                             raw[1].z, raw[1].w, raw[2].x, raw[2].y, raw[2].z, raw[2].w,
-                             raw[3].x, raw[3].y, raw[3].z, raw[3].w};
+    const uint32_t rw[16] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w,
+                             raw[2].x, raw[2].y, raw[2].z, raw[2].w, raw[3].x, raw[3].y, raw[3].z, raw[3].w};
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const uint32_t sbyte = ((t < 8 ? sc.x : sc.y) >> (8 * ((t >> 1) & 3))) & 0xFFu;
-      const half8_t kf = dequant8(rw[t], sbyte);
-      const half8_t qh = bf16x8_to_half8(qf[t]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qh, acc, 0, 0, 0);
-      // V^T: rows 128g + 8t + i, this key's column
-      const uint4 kb = __builtin_bit_cast(uint4, kf);
-      const uint32_t kw[4] = {kb.x, kb.y, kb.z, kb.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vt[(128 * g + 8 * t + 2 * i) * VTS + vcol] = (uint16_t)(kw[i] & 0xFFFFu);
-        vt[(128 * g + 8 * t + 2 * i + 1) * VTS + vcol] = (uint16_t)(kw[i] >> 16);
-      }
-    }
-  } else {
-    const int wpos0 = a.swa_start[r];
-    const int wl = a.swa_len[r];
-    const int kk = (split - a.n_main_splits) * KEYS + key_local;
-    valid = kk < wl && kk < CSA2_MAX_WINDOW && wpos0 >= 0 && (int64_t)wpos0 + kk < a.S;
-    const int64_t rowoff = ((int64_t)b * a.S + wpos0 + (valid ? kk : 0)) * 64 + g * 16;
-    uint4 kr[16], vr[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      kr[t] = valid ? a.swa_k[rowoff + t] : make_uint4(0, 0, 0, 0);
-      vr[t] = valid ? a.swa_v[rowoff + t] : make_uint4(0, 0, 0, 0);
+      const half8_t kf = dequant8(rw[t], scale_h2(sbyte));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, as_h8(qrow[t]), acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint32_t vw[4] = {vr[t].x, vr[t].y, vr[t].z, vr[t].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vt[(128 * g + 8 * t + 2 * i) * VTS + vcol] = (uint16_t)(vw[i] & 0xFFFFu);
-        vt[(128 * g + 8 * t + 2 * i + 1) * VTS + vcol] = (uint16_t)(vw[i] >> 16);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr[t]), as_bf8(qf[t]), acc, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
   }
-
-  // ---- scores and softmax statistics (lane: keys 4g..4g+3 of this wave, head c) ----
-  const uint64_t vm = __ballot(valid);
-  float s[4];
-  float mloc = -__builtin_inff();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool kv_ok = (vm >> (4 * g + i)) & 1ull;
-    s[i] = kv_ok ? acc[i] * a.sm_scale : -__builtin_inff();
-    mloc = fmaxf(mloc, s[i]);
-  }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-  if (g == 0) red_m[w][c] = mloc;
-  __syncthreads();
-  float m = red_m[0][c];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) m = fmaxf(m, red_m[i][c]);
-  float p[4], lsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = (m == -__builtin_inff()) ? 0.f : __expf(s[i] - m);
-    lsum += p[i];
-  }
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (g == 0) red_l[w][c] = lsum;
-  // P hi/lo into LDS: P[head c][key w*16 + 4g + i]
-  {
-    uint16_t hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (is_main) {
-        const _Float16 h = (_Float16)p[i];
-        const _Float16 e = (_Float16)(p[i] - (float)h);
-        hi[i] = __builtin_bit_cast(uint16_t, h);
-        lo[i] = __builtin_bit_cast(uint16_t, e);
-      } else {
-        const uint16_t h = f32_to_bf16_rne(p[i]);
-        const float hf = __uint_as_float((uint32_t)h << 16);
-        hi[i] = h;
-        lo[i] = f32_to_bf16_rne(p[i] - hf);
-      }
-    }
-    const int off = c * PS + w * 16 + 4 * g;
-    *(uint2*)&p_hi[off] = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-    *(uint2*)&p_lo[off] = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
-  }
-  __syncthreads();
-  float lt = red_l[0][c];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) lt += red_l[i][c];
-
-  // ---- O[16 heads x 512] = P[16 x KEYS] * V[KEYS x 512] ----
-  f32x4 o[TILES_PER_WAVE];
-#pragma unroll
-  for (int n = 0; n < TILES_PER_WAVE; ++n) o[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < KEYS / 32; ++ks) {
-    const uint4 ah = *(const uint4*)&p_hi[c * PS + ks * 32 + 8 * g];
-    const uint4 al = *(const uint4*)&p_lo[c * PS + ks * 32 + 8 * g];
-#pragma unroll
-    for (int n = 0; n < TILES_PER_WAVE; ++n) {
-      const int dim = (w * TILES_PER_WAVE + n) * 16 + c;
-      const int col = (ks * 32 + 8 * g) ^ (((dim >> 7) & 3) << 4);
-      const uint4 bv = *(const uint4*)&vt[dim * VTS + col];
-      if (is_main) {
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah),
-                                                      __builtin_bit_cast(half8_t, bv), o[n], 0, 0, 0);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al),
-                                                      __builtin_bit_cast(half8_t, bv), o[n], 0, 0, 0);
-      } else {
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ah), as_bf8(bv), o[n], 0, 0, 0);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(al), as_bf8(bv), o[n], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- partial results: O[head 4g+i][dim], max and sum per head ----
-  const int64_t pbase = (int64_t)r * a.n_splits + split;
-  float* po = a.part_o + pbase * (16 * 512);
-#pragma unroll
-  for (int n = 0; n < TILES_PER_WAVE; ++n) {
-    const int dim = (w * TILES_PER_WAVE + n) * 16 + c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) po[(4 * g + i) * 512 + dim] = o[n][i];
-  }
-  if (tid < 16) {
-    a.part_ml[pbase * 32 + tid * 2 + 0] = m;
-    a.part_ml[pbase * 32 + tid * 2 + 1] = lt;
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.ticket[r], 1u) == (uint32_t)(a.n_splits - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // ---- merge (last block of the row) ----
-  if (tid < 16) {
-    float M = -__builtin_inff();
-    for (int j = 0; j < a.n_splits; ++j)
-      M = fmaxf(M, a.part_ml[((int64_t)r * a.n_splits + j) * 32 + tid * 2]);
-    float Lsum = 0.f;
-    for (int j = 0; j < a.n_splits; ++j) {
-      const float mj = a.part_ml[((int64_t)r * a.n_splits + j) * 32 + tid * 2];
-      const float lj = a.part_ml[((int64_t)r * a.n_splits + j) * 32 + tid * 2 + 1];
-      Lsum += (mj == -__builtin_inff()) ? 0.f : __expf(mj - M) * lj;
-    }
-    ml[0][tid] = M;
-    ml[1][tid] = Lsum;
-    if (a.lse) a.lse[(int64_t)r * 16 + tid] = (Lsum > 0.f) ? M + __logf(Lsum) : -__builtin_inff();
-  }
-  __syncthreads();
-  // each thread: 4 consecutive dims of some heads
-  for (int e4 = tid; e4 < 16 * 128; e4 += NW * 64) {
-    const int h = e4 >> 7, d4 = (e4 & 127) * 4;
-    const float M = ml[0][h], Lsum = ml[1][h];
-    float4 accv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (Lsum > 0.f) {
-      for (int j = 0; j < a.n_splits; ++j) {
-        const int64_t pj = (int64_t)r * a.n_splits + j;
-        const float mj = a.part_ml[pj * 32 + h * 2];
-        if (mj == -__builtin_inff()) continue;
-        const float wj = __expf(mj - M);
-        const float4 v = *(const float4*)&a.part_o[pj * (16 * 512) + h * 512 + d4];
-        accv.x += wj * v.x; accv.y += wj * v.y; accv.z += wj * v.z; accv.w += wj * v.w;
-      }
-      const float inv = 1.0f / Lsum;
-      accv.x *= inv; accv.y *= inv; accv.z *= inv; accv.w *= inv;
-    }
-    *(float4*)&a.out[((int64_t)r * 16 + h) * 512 + d4] = accv;
-  }
-  if (tid == 0) a.ticket[r] = 0u;
 }
 
-constexpr int kAttnWaves = 4;
-constexpr int kAttnKeys = kAttnWaves * 16;
+CSA2_DEV void qk_win(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int kk0, int c, int g,
+                     float (&s)[8]) {
+  const uint4* qrow = sm.qb + c * kQRow + 16 * g;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int kk = kk0 + 16 * u + c;
+    const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
+    const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint4 kr = ok ? src[t] : make_uint4(0, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr), as_bf8(qrow[t]), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
+  }
+}
 
-int attn_splits(int k, int* n_main) {
-  const int nm = (k + kAttnKeys - 1) / kAttnKeys;
-  const int ns = (CSA2_MAX_WINDOW + kAttnKeys - 1) / kAttnKeys;
-  if (n_main) *n_main = nm;
-  return nm + ns;
+// ---- phase 3: O[16 heads x dims 128w .. 128w+127] += P V over the step's 128 keys ----
+CSA2_DEV void pv_main(const AttnArgs& a, const AttnSmem& sm, RowState& st, int w, int c, int g) {
+#pragma unroll 1
+  for (int ks = 0; ks < 4; ++ks) {
+    const int key0 = 32 * ks + 8 * g;
+    uint32_t dw[8];
+    half2_t sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int32_t sl = sm.slot[key0 + i];
+      uint32_t code = 0, sb = 0;
+      if (sl >= 0) {
+        code = *(const uint32_t*)(a.kv + (int64_t)sl * 256 + 64 * w + 4 * c);
+        sb = a.kv_scale[(int64_t)sl * 32 + 8 * w + (c >> 1)];
+      }
+      dw[i] = code;
+      sv[i] = scale_h2(sb);
+    }
+    const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
+    const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
+#pragma unroll
+    for (int sel = 0; sel < 4; ++sel) {
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = h2u(fp4x2(dw[i], sel) * sv[i]);
+      const uint4 b0 = make_uint4(pack_lo(h[0], h[1]), pack_lo(h[2], h[3]), pack_lo(h[4], h[5]), pack_lo(h[6], h[7]));
+      const uint4 b1 = make_uint4(pack_hi(h[0], h[1]), pack_hi(h[2], h[3]), pack_hi(h[4], h[5]), pack_hi(h[6], h[7]));
+      st.o[2 * sel] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(ph), as_h8(b0), st.o[2 * sel], 0, 0, 0);
+      st.o[2 * sel] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(pl), as_h8(b0), st.o[2 * sel], 0, 0, 0);
+      st.o[2 * sel + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(ph), as_h8(b1), st.o[2 * sel + 1], 0, 0, 0);
+      st.o[2 * sel + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(pl), as_h8(b1), st.o[2 * sel + 1], 0, 0, 0);
+    }
+  }
+}
+
+CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int w, int c,
+                     int g) {
+#pragma unroll 1
+  for (int ks = 0; ks < 4; ++ks) {
+    const int key0 = 32 * ks + 8 * g;
+    uint4 vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = key0 + i;
+      const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
+      vr[i] = ok ? Ly.swa_v[((int64_t)b * Ly.S + wst + kk) * 64 + 16 * w + c] : make_uint4(0, 0, 0, 0);
+    }
+    const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
+    const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (m == 0) ? vr[i].x : (m == 1) ? vr[i].y : (m == 2) ? vr[i].z : vr[i].w;
+      const uint4 b0 = make_uint4(pack_lo(x[0], x[1]), pack_lo(x[2], x[3]), pack_lo(x[4], x[5]), pack_lo(x[6], x[7]));
+      const uint4 b1 = make_uint4(pack_hi(x[0], x[1]), pack_hi(x[2], x[3]), pack_hi(x[4], x[5]), pack_hi(x[6], x[7]));
+      st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b0), st.o[2 * m], 0, 0, 0);
+      st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), as_bf8(b0), st.o[2 * m], 0, 0, 0);
+      st.o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b1), st.o[2 * m + 1], 0, 0, 0);
+      st.o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), as_bf8(b1), st.o[2 * m + 1], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kAttnWaves * 64) void fp4_attn_kernel(AttnArgs a) {
+  __shared__ AttnSmem sm;
+  // flat grid: block id = (li * R + r) * n_blocks + blk
+  const int blk = blockIdx.x % a.n_blocks;
+  const int lr = blockIdx.x / a.n_blocks;
+  const int li = lr / a.R, r = lr - li * a.R;
+  const AttnLayer& Ly = a.layer[li];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c = lane & 15, g = lane >> 4;
+  const int b = a.row_seq ? a.row_seq[r] : r;
+  const int L = a.seq_len[b];
+  const int n_main = (a.k + kStepKeys - 1) / kStepKeys;
+  const int st0 = blk * a.steps_per_block;
+  const int st1 = min(n_main + 1, st0 + a.steps_per_block);
+  const int32_t* idx_row = a.idx + (int64_t)r * a.k;
+  const int wst = Ly.swa_start[r];
+  const int wl = min(Ly.swa_len[r], CSA2_MAX_WINDOW);
+  CSA2_MARK(a, 0);
+
+  // query of the row into LDS, bf16 and fp16
+  {
+    const uint4* q = Ly.q + (int64_t)r * 16 * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;          // uint4 index: head e / 64, piece e % 64
+      const uint4 v = q[e];
+      const int h = e >> 6, p = e & 63;
+      sm.qb[h * kQRow + p] = v;
+      sm.qh[h * kQRow + p] = bf16x8_to_f16x8(v);
+    }
+  }
+
+  RowState st;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.m[i] = -__builtin_inff();
+    st.l[i] = 0.f;
+  }
+
+  for (int step = st0; step < st1; ++step) {
+    const bool is_main = step < n_main;
+    // ---- keys of this wave: 32w .. 32w+31 of the step ----
+    const int kk = step * kStepKeys + 32 * w + (lane & 31);    // main: index into idx
+    int32_t slot = -1;
+    bool valid;
+    if (is_main) {
+      const int pos = kk < a.k ? idx_row[kk] : -1;
+      slot = (pos >= 0 && pos < L) ? (int32_t)a.map(b, pos) : -1;
+      valid = slot >= 0;
+      if (lane < 32) sm.slot[32 * w + lane] = slot;
+    } else {
+      const int e = 32 * w + (lane & 31);
+      valid = e < wl && wst >= 0 && (int64_t)wst + e < Ly.S;
+    }
+    const uint64_t vmask = __ballot(valid);
+    __syncthreads();    // query (first step) and slots visible
+    CSA2_MARK(a, 1);
+    float s[8];
+    if (is_main)
+      qk_main(a, sm, slot, c, g, s);
+    else
+      qk_win(Ly, sm, b, wst, wl, 32 * w, c, g, s);
+    CSA2_MARK(a, 2);
+
+    // ---- softmax statistics of the step (head c) ----
+    const float sm_scale = Ly.sm_scale;
+    float cmax = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
+      const bool ok = (vmask >> key) & 1ull;
+      s[e] = ok ? s[e] * sm_scale : -__builtin_inff();
+      cmax = fmaxf(cmax, s[e]);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    if (g == 0) sm.red_m[w][c] = cmax;
+    __syncthreads();
+    float mstep = sm.red_m[0][c];
+#pragma unroll
+    for (int v = 1; v < kAttnWaves; ++v) mstep = fmaxf(mstep, sm.red_m[v][c]);
+    // running max of head c before this step: kept in st.m[c & 3] by the lanes
+    // of group c >> 2 (lane 16 * (c >> 2) + c evaluates pick4 with its own c)
+    const float mold_c = __shfl(pick4(st.m, c & 3), 16 * (c >> 2) + c, 64);
+    const float mnew_c = fmaxf(mold_c, mstep);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = (mnew_c == -__builtin_inff()) ? 0.f : __expf(s[e] - mnew_c);
+      psum += p[e];
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    if (g == 0) sm.red_l[w][c] = psum;
+    // P hi/lo -> LDS [head c][key 32w + sigma(g, e)]
+    {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t h0, h1, l0, l1;
+        if (is_main) {
+          const _Float16 a0 = (_Float16)p[e], a1 = (_Float16)p[e + 1];
+          h0 = __builtin_bit_cast(uint16_t, a0);
+          h1 = __builtin_bit_cast(uint16_t, a1);
+          l0 = __builtin_bit_cast(uint16_t, (_Float16)(p[e] - (float)a0));
+          l1 = __builtin_bit_cast(uint16_t, (_Float16)(p[e + 1] - (float)a1));
+        } else {
+          h0 = f32_to_bf16_rne(p[e]);
+          h1 = f32_to_bf16_rne(p[e + 1]);
+          l0 = f32_to_bf16_rne(p[e] - __uint_as_float(h0 << 16));
+          l1 = f32_to_bf16_rne(p[e + 1] - __uint_as_float(h1 << 16));
+        }
+        hw[e / 2] = h0 | (h1 << 16);
+        lw[e / 2] = l0 | (l1 << 16);
+      }
+      uint16_t* ph = &sm.p_hi[c * kPRow + 32 * w];
+      uint16_t* pl = &sm.p_lo[c * kPRow + 32 * w];
+      *(uint2*)(ph + 4 * g) = make_uint2(hw[0], hw[1]);
+      *(uint2*)(ph + 16 + 4 * g) = make_uint2(hw[2], hw[3]);
+      *(uint2*)(pl + 4 * g) = make_uint2(lw[0], lw[1]);
+      *(uint2*)(pl + 16 + 4 * g) = make_uint2(lw[2], lw[3]);
+    }
+    __syncthreads();
+    // running statistics of this lane's output heads 4g+i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      float mh = sm.red_m[0][h], lh = sm.red_l[0][h];
+#pragma unroll
+      for (int v = 1; v < kAttnWaves; ++v) {
+        mh = fmaxf(mh, sm.red_m[v][h]);
+        lh += sm.red_l[v][h];
+      }
+      const float mn = fmaxf(st.m[i], mh);
+      const float alpha = (st.m[i] == -__builtin_inff()) ? 0.f : __expf(st.m[i] - mn);
+      st.l[i] = st.l[i] * alpha + lh;
+      st.m[i] = mn;
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.o[j][i] *= alpha;
+      }
+    }
+    CSA2_MARK(a, 3);
+    if (is_main)
+      pv_main(a, sm, st, w, c, g);
+    else
+      pv_win(Ly, sm, st, b, wst, wl, w, c, g);
+    CSA2_MARK(a, 4);
+    __syncthreads();    // P, slots and statistics may be overwritten by the next step
+  }
+
+  // ---- output (one block per row) or partial ----
+  if (a.n_blocks == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      const float inv = (st.l[i] > 0.f) ? 1.0f / st.l[i] : 0.f;
+      float* dst = Ly.out + ((int64_t)r * 16 + h) * 512 + 128 * w + 8 * c;
+      *(float4*)dst = make_float4(st.o[0][i] * inv, st.o[1][i] * inv, st.o[2][i] * inv, st.o[3][i] * inv);
+      *(float4*)(dst + 4) = make_float4(st.o[4][i] * inv, st.o[5][i] * inv, st.o[6][i] * inv, st.o[7][i] * inv);
+      if (Ly.lse && w == 0 && c == 0)
+        Ly.lse[(int64_t)r * 16 + h] = (st.l[i] > 0.f) ? st.m[i] + __logf(st.l[i]) : -__builtin_inff();
+    }
+    return;
+  }
+  const int64_t pidx = (int64_t)lr * a.n_blocks + blk;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    float* dst = a.part_o + pidx * (16 * 512) + h * 512 + 128 * w + 8 * c;
+    *(float4*)dst = make_float4(st.o[0][i], st.o[1][i], st.o[2][i], st.o[3][i]);
+    *(float4*)(dst + 4) = make_float4(st.o[4][i], st.o[5][i], st.o[6][i], st.o[7][i]);
+    if (w == 0 && c == 0) {
+      a.part_ml[pidx * 32 + h * 2 + 0] = st.m[i];
+      a.part_ml[pidx * 32 + h * 2 + 1] = st.l[i];
+    }
+  }
+  CSA2_MARK(a, 5);
+}
+
+// One block per (layer, row): out = sum_j w_j O_j / sum_j w_j l_j with
+// w_j = exp(m_j - max_j m_j), the partials of the row's blocks merged as one
+// softmax; lse = max + log(sum).
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const int lr = blockIdx.x;                 // li * R + r
+  const int li = lr / a.R, r = lr - li * a.R;
+  const AttnLayer& Ly = a.layer[li];
+  const int tid = threadIdx.x, th = tid >> 4, tc = tid & 15;
+  const int64_t prow = (int64_t)lr * a.n_blocks;
+  float mj[kMaxAttnBlocks], lj[kMaxAttnBlocks];
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kMaxAttnBlocks; ++j) {
+    if (j < a.n_blocks) {
+      mj[j] = a.part_ml[(prow + j) * 32 + th * 2 + 0];
+      lj[j] = a.part_ml[(prow + j) * 32 + th * 2 + 1];
+    } else {
+      mj[j] = -__builtin_inff();
+      lj[j] = 0.f;
+    }
+    M = fmaxf(M, mj[j]);
+  }
+  float Lsum = 0.f, wj[kMaxAttnBlocks];
+#pragma unroll
+  for (int j = 0; j < kMaxAttnBlocks; ++j) {
+    wj[j] = (mj[j] == -__builtin_inff()) ? 0.f : __expf(mj[j] - M);
+    Lsum += wj[j] * lj[j];
+  }
+  float4 acc[8];
+#pragma unroll
+  for (int q4 = 0; q4 < 8; ++q4) acc[q4] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kMaxAttnBlocks; ++j) {
+    if (j < a.n_blocks) {
+      const float* po = a.part_o + (prow + j) * (16 * 512) + th * 512 + tc * 32;
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const float4 v = *(const float4*)(po + 4 * q4);
+        acc[q4].x += wj[j] * v.x;
+        acc[q4].y += wj[j] * v.y;
+        acc[q4].z += wj[j] * v.z;
+        acc[q4].w += wj[j] * v.w;
+      }
+    }
+  }
+  const float inv = (Lsum > 0.f) ? 1.0f / Lsum : 0.f;
+  float* out_row = Ly.out + ((int64_t)r * 16 + th) * 512 + tc * 32;
+#pragma unroll
+  for (int q4 = 0; q4 < 8; ++q4)
+    *(float4*)(out_row + 4 * q4) = make_float4(acc[q4].x * inv, acc[q4].y * inv, acc[q4].z * inv, acc[q4].w * inv);
+  if (Ly.lse && tc == 0) Ly.lse[(int64_t)r * 16 + th] = (Lsum > 0.f) ? M + __logf(Lsum) : -__builtin_inff();
+}
+
+int attn_steps(int k) { return (k + kStepKeys - 1) / kStepKeys + 1; }
+
+int attn_blocks(int k, int rows_x_layers, int* steps_per_block) {
+  const int n_steps = attn_steps(k);
+  // few row-layers: one step per block (partials + merge); many: one block
+  // per row-layer writes its output directly
+  const int spb = (rows_x_layers >= 512) ? n_steps : 1;
+  if (steps_per_block) *steps_per_block = spb;
+  return (n_steps + spb - 1) / spb;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
-  if (a.R == 0) return hipSuccess;
-  hipLaunchKernelGGL(fp4_attn_kernel<kAttnWaves>, dim3(a.n_splits, a.R), dim3(kAttnWaves * 64), 0, st, a);
+  if (a.R == 0 || a.n_layers == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp4_attn_kernel, dim3(a.n_blocks * a.R * a.n_layers), dim3(kAttnWaves * 64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_blocks == 1) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_layers * a.R), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -67,4 +67,36 @@ CSA2_DEV float e4m3_to_float(uint32_t c) {
 
 CSA2_DEV int lane_id() { return __lane_id(); }
 
+// Phase timestamps for kernel tuning: only a build with -DCSA2_TRACE records
+// them (thread 0 of the block with all block indices 0 writes the 100 MHz
+// wall clock into slot i of the trace buffer set by csa2_trace_set).
+#ifdef CSA2_TRACE
+#define CSA2_TRACE_ARG uint64_t* trace;
+#define CSA2_MARK(a, i)                                                                       \
+  do {                                                                                         \
+    if ((a).trace && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) { \
+      (a).trace[(i)] = wall_clock64();                                                         \
+      (a).trace[32 + (i)] = __builtin_amdgcn_s_memtime();                                      \
+    }                                                                                          \
+  } while (0)
+// inner marks: a trace pointer passed down explicitly
+#define CSA2_MARKP(tr, i)                                                                        \
+  do {                                                                                           \
+    if ((tr) && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {     \
+      (tr)[(i)] = wall_clock64();                                                                \
+      (tr)[32 + (i)] = __builtin_amdgcn_s_memtime();                                             \
+    }                                                                                            \
+  } while (0)
+#define CSA2_TRACE_PTR(a) (a).trace
+#else
+#define CSA2_TRACE_ARG
+#define CSA2_MARK(a, i) \
+  do {                  \
+  } while (0)
+#define CSA2_MARKP(tr, i) \
+  do {                    \
+  } while (0)
+#define CSA2_TRACE_PTR(a) ((uint64_t*)nullptr)
+#endif
+
 }  // namespace csa2

@@ -10,155 +10,191 @@
 // product of head h evaluated as eight fused-multiply-add chains over channels
 // 8j..8j+7 (from +0, channel order) combined as ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)).
 //
-// Layout of the work: a tile is 256 positions (32 KiB of bf16 keys).  The tile
-// is read from HBM with fully coalesced 16-byte loads (thread t loads piece
-// i*256+t), written to LDS with an XOR swizzle of the 16-byte chunks
-// (chunk j of row p at slot j ^ (p & 7)) so that both the writes and the
-// per-position reads are bank-conflict free, and then each thread scores one
-// position from LDS.  The next tile's loads are issued before the current tile
-// is scored.  The query (4 x 64) is uniform over the block and is read through
-// the scalar cache.  Persistent grid: each block walks work items (row, tile)
-// with a stride of gridDim.x.
+// Work layout (no LDS): a wave scores one "step" of 64 positions at a time.
+// Lane l = 8g + j owns channel chunk j (channels 8j..8j+7, one 16-byte load)
+// of the eight positions of group g; register i of the lane holds position
+// (step base) + 8g + i.  One load instruction therefore reads eight whole
+// 128-byte key rows, and the eight instructions of a step read 8 KiB.
+// Each lane forms its chunk's partial c_j for the four heads with eight FMAs;
+// the tree over the eight chunks is a three-level DPP butterfly inside each
+// group of eight lanes (xor 1, xor 2, then the other half of the group), which
+// reproduces ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)) exactly (IEEE addition is
+// commutative).  Loads of the next step are issued register by register as the
+// current step consumes them, so each wave keeps 8 KiB in flight.
+//
+// Epilogue: lane 8g + j writes the score of position base + 8g + j (256
+// contiguous bytes per wave).  In scan mode the wave also emits the maxima the
+// Top-K selection descends through: the maximum of each block of 8 positions
+// (the hierarchical indexer's block score) and of the 64-position step.
 #include "kernels.h"
 
 namespace csa2 {
 
-constexpr int kTile = 256;           // positions per tile (one per thread)
+constexpr int kScanWaves = 4;            // waves per block
 
+#define CSA2_DPP(v, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
 
-template <bool CAND, bool HAS_W, bool BMAX>
-__global__ __launch_bounds__(256) void index_score_kernel(IdxArgs a, const uint32_t* __restrict__ q32,
-                                                          const uint4* __restrict__ kdata,
-                                                          float* __restrict__ scores,
-                                                          float* __restrict__ block_max) {
-  __shared__ uint4 lds[kTile * 8];
-  const int tid = threadIdx.x;
-  const int64_t n_items = (int64_t)a.R * a.tiles_per_row;
+// per-lane geometry of one step
+struct StepGeo {
+  int r;          // query row
+  int b;          // sequence
+  int64_t pos0;   // first position of this lane's group (scan: 64t + 8g)
+  int64_t s0;     // slot of pos0 (-1: the group is absent)
+  int nv;         // positions i < nv of the group are present
+  int L;          // visible positions of the row
+  int t;          // step index within the row
+};
 
-  // per-thread piece geometry: piece i covers position P = i*32 + tid/8, chunk tid%8
-  const int pchunk = tid & 7;
-  uint4 regs[8];
-
-  auto load_item = [&](int64_t item) {
-    const int r = (int)(item / a.tiles_per_row);
-    const int t = (int)(item % a.tiles_per_row);
-    const int b = a.row_seq ? a.row_seq[r] : r;
-    const int L = min(a.seq_len[b], a.n_max);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int P = i * 32 + (tid >> 3);
-      int64_t pos;
-      bool ok;
-      if (CAND) {
-        const int ci = t * kTile + P;
-        const int blk = (ci < a.n_cand * 8) ? a.cand[(int64_t)r * a.n_cand + (ci >> 3)] : -1;
-        pos = (int64_t)blk * 8 + (ci & 7);
-        ok = blk >= 0 && pos < L;
-      } else {
-        pos = (int64_t)t * kTile + P;
-        ok = pos < L;
-      }
-      int64_t slot = ok ? a.map(b, pos) : -1;
-      ok = slot >= 0;
-      regs[i] = ok ? kdata[slot * 8 + pchunk] : make_uint4(0, 0, 0, 0);
+template <bool CAND>
+CSA2_DEV StepGeo step_geo(const IdxArgs& a, uint32_t item, int g) {
+  StepGeo s;
+  s.r = (int)(item / (uint32_t)a.steps_per_row);
+  s.t = (int)(item - (uint32_t)s.r * (uint32_t)a.steps_per_row);
+  s.b = a.row_seq ? a.row_seq[s.r] : s.r;
+  s.L = min(a.seq_len[s.b], a.n_max);
+  int64_t pos0;
+  if (CAND) {
+    const int ci = s.t * 8 + g;
+    const int blk = ci < a.n_cand ? a.cand[(int64_t)s.r * a.n_cand + ci] : -1;
+    pos0 = blk >= 0 ? (int64_t)blk * 8 : (int64_t)1 << 40;
+  } else {
+    pos0 = (int64_t)s.t * 64 + g * 8;
+  }
+  s.pos0 = pos0;
+  int64_t s0 = -1;
+  int nv = 0;
+  if (pos0 < s.L) {
+    s0 = a.map(s.b, pos0);    // a group of 8 never straddles a page (pages are 64)
+    if (s0 >= 0) {
+      const int64_t lim = min((int64_t)s.L - pos0, a.map.n_slots - s0);
+      nv = (int)min(lim, (int64_t)8);
     }
-  };
+  }
+  s.s0 = s0;
+  s.nv = nv;
+  return s;
+}
 
-  int64_t item = blockIdx.x;
+template <bool CAND, bool HAS_W, bool MAXIMA>
+__global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 3, j = lane & 7;
+  const uint32_t W = gridDim.x * kScanWaves;
+  const uint32_t n_items = (uint32_t)a.R * (uint32_t)a.steps_per_row;
+  uint32_t item = blockIdx.x * kScanWaves + (threadIdx.x >> 6);
   if (item >= n_items) return;
-  load_item(item);
 
-  for (; item < n_items; item += gridDim.x) {
-    __syncthreads();  // previous tile fully consumed
+  const uint4* __restrict__ kd = a.kdata;
+  uint4 regs[8];
+  StepGeo cur = step_geo<CAND>(a, item, g);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int P = i * 32 + (tid >> 3);
-      lds[P * 8 + (pchunk ^ (P & 7))] = regs[i];
-    }
-    __syncthreads();
-    const int64_t next = item + gridDim.x;
-    const int r = (int)(item / a.tiles_per_row);
-    const int t = (int)(item % a.tiles_per_row);
-    if (next < n_items) load_item(next);
+  for (int i = 0; i < 8; ++i)
+    regs[i] = (i < cur.nv) ? kd[(cur.s0 + i) * 8 + j] : make_uint4(0, 0, 0, 0);
 
-    // ---- score position p = tile*256 + tid ----
-    const int b = a.row_seq ? a.row_seq[r] : r;
-    const int L = min(a.seq_len[b], a.n_max);
-    int64_t pos;
-    bool ok;
-    if (CAND) {
-      const int ci = t * kTile + tid;
-      const int blk = (ci < a.n_cand * 8) ? a.cand[(int64_t)r * a.n_cand + (ci >> 3)] : -1;
-      pos = (int64_t)blk * 8 + (ci & 7);
-      ok = blk >= 0 && pos < L && a.map(b, pos) >= 0;
-    } else {
-      pos = (int64_t)t * kTile + tid;
-      ok = pos < L && a.map(b, pos) >= 0;
-    }
-    const uint32_t* q = q32 + (int64_t)r * 128;
-    float c[4][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 kw = lds[tid * 8 + (j ^ (tid & 7))];
-      const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
-                           bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+  int qrow = -1;
+  float qf[4][8];
+  float w[4] = {1.f, 1.f, 1.f, 1.f};
+
+  for (;;) {
+    if (cur.r != qrow) {
+      qrow = cur.r;
+      const uint4* qp = (const uint4*)(a.q32 + (int64_t)qrow * 128);
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const uint32_t q0 = q[h * 32 + j * 4 + 0], q1 = q[h * 32 + j * 4 + 1];
-        const uint32_t q2 = q[h * 32 + j * 4 + 2], q3 = q[h * 32 + j * 4 + 3];
-        float acc = 0.0f;
-        acc = __builtin_fmaf(kf[0], bf16_lo(q0), acc);
-        acc = __builtin_fmaf(kf[1], bf16_hi(q0), acc);
-        acc = __builtin_fmaf(kf[2], bf16_lo(q1), acc);
-        acc = __builtin_fmaf(kf[3], bf16_hi(q1), acc);
-        acc = __builtin_fmaf(kf[4], bf16_lo(q2), acc);
-        acc = __builtin_fmaf(kf[5], bf16_hi(q2), acc);
-        acc = __builtin_fmaf(kf[6], bf16_lo(q3), acc);
-        acc = __builtin_fmaf(kf[7], bf16_hi(q3), acc);
-        c[h][j] = acc;
+        const uint4 v = qp[h * 8 + j];
+        qf[h][0] = bf16_lo(v.x); qf[h][1] = bf16_hi(v.x);
+        qf[h][2] = bf16_lo(v.y); qf[h][3] = bf16_hi(v.y);
+        qf[h][4] = bf16_lo(v.z); qf[h][5] = bf16_hi(v.z);
+        qf[h][6] = bf16_lo(v.w); qf[h][7] = bf16_hi(v.w);
       }
-    }
-    float rr[4];
+      if (HAS_W) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float d = ((c[h][0] + c[h][1]) + (c[h][2] + c[h][3])) +
-                      ((c[h][4] + c[h][5]) + (c[h][6] + c[h][7]));
-      rr[h] = (d > 0.0f) ? d : 0.0f;
-    }
-    float s;
-    if (HAS_W) {
-      const float* w = a.head_w + (int64_t)r * 4;
-      const float p0 = w[0] * rr[0], p1 = w[1] * rr[1], p2 = w[2] * rr[2], p3 = w[3] * rr[3];
-      s = (p0 + p1) + (p2 + p3);
-    } else {
-      s = (rr[0] + rr[1]) + (rr[2] + rr[3]);
-    }
-    if (CAND) {
-      const int64_t ci = (int64_t)t * kTile + tid;
-      if (ci < a.score_stride) scores[(int64_t)r * a.score_stride + ci] = ok ? s : -__builtin_inff();
-    } else {
-      if (ok) scores[(int64_t)r * a.score_stride + pos] = s;
-      if (BMAX) {
-        uint32_t k = ok ? order_key(s) : 0u;
-        k = max(k, (uint32_t)__shfl_xor((int)k, 1, kWave));
-        k = max(k, (uint32_t)__shfl_xor((int)k, 2, kWave));
-        k = max(k, (uint32_t)__shfl_xor((int)k, 4, kWave));
-        if ((tid & 7) == 0 && k != 0u) block_max[(int64_t)r * a.bmax_stride + (pos >> 3)] = key_to_float(k);
+        for (int h = 0; h < 4; ++h) w[h] = a.head_w[(int64_t)qrow * 4 + h];
       }
     }
+    const uint32_t next = item + W;
+    const bool has_next = next < n_items;
+    StepGeo nxt;
+    if (has_next) nxt = step_geo<CAND>(a, next, g);
+
+    float mine = 0.f;          // score of position pos0 + j (this lane's output)
+    uint32_t kmax = 0u;        // order key of the group's best present score
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 kw = regs[i];
+      if (has_next) regs[i] = (i < nxt.nv) ? kd[(nxt.s0 + i) * 8 + j] : make_uint4(0, 0, 0, 0);
+      const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
+                           bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+      float d[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(kf[e], qf[h][e], acc);
+        d[h] = acc;
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h) d[h] = d[h] + CSA2_DPP(d[h], 0xB1);    // c_j + c_{j^1}
+#pragma unroll
+      for (int h = 0; h < 4; ++h) d[h] = d[h] + CSA2_DPP(d[h], 0x4E);    // + the other pair
+#pragma unroll
+      for (int h = 0; h < 4; ++h) d[h] = d[h] + CSA2_DPP(d[h], 0x141);   // + the other quad
+      float rr[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) rr[h] = (d[h] > 0.0f) ? d[h] : 0.0f;
+      float s;
+      if (HAS_W) {
+        const float p0 = w[0] * rr[0], p1 = w[1] * rr[1], p2 = w[2] * rr[2], p3 = w[3] * rr[3];
+        s = (p0 + p1) + (p2 + p3);
+      } else {
+        s = (rr[0] + rr[1]) + (rr[2] + rr[3]);
+      }
+      mine = (j == i) ? s : mine;
+      if (MAXIMA) {
+        const uint32_t k = (i < cur.nv) ? order_key(s) : 0u;
+        kmax = max(kmax, k);
+      }
+    }
+
+    // ---- outputs of the step ----
+    if (CAND) {
+      const int64_t ci8 = (int64_t)cur.t * 64 + lane;     // 8 * candidate index + j
+      if (ci8 < (int64_t)a.n_cand * 8)
+        a.scores[(int64_t)cur.r * a.score_stride + ci8] = (j < cur.nv) ? mine : -__builtin_inff();
+    } else {
+      const int64_t p = cur.pos0 + j;
+      if (p < cur.L) a.scores[(int64_t)cur.r * a.score_stride + p] = (j < cur.nv) ? mine : -__builtin_inff();
+      if (MAXIMA) {
+        if (j == 0 && cur.pos0 < cur.L)
+          a.block_max[(int64_t)cur.r * a.bmax_stride + (cur.pos0 >> 3)] =
+              kmax ? key_to_float(kmax) : -__builtin_inff();
+        uint32_t k2 = kmax;
+        k2 = max(k2, (uint32_t)__shfl_xor((int)k2, 8, 64));
+        k2 = max(k2, (uint32_t)__shfl_xor((int)k2, 16, 64));
+        k2 = max(k2, (uint32_t)__shfl_xor((int)k2, 32, 64));
+        if (lane == 0 && a.max64 && (int64_t)cur.t * 64 < cur.L)
+          a.max64[(int64_t)cur.r * a.max64_stride + cur.t] = k2 ? key_to_float(k2) : -__builtin_inff();
+      }
+    }
+    if (!has_next) break;
+    item = next;
+    cur = nxt;
   }
 }
 
-hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool bmax, hipStream_t st) {
-  const int64_t items = (int64_t)a.R * a.tiles_per_row;
+hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxima, hipStream_t st) {
+  const int64_t items = (int64_t)a.R * a.steps_per_row;
   if (items == 0) return hipSuccess;
-  const int grid = (int)(items < 2048 ? items : 2048);
-#define CSA2_IDX_LAUNCH(C, W, M) \
-  hipLaunchKernelGGL((index_score_kernel<C, W, M>), dim3(grid), dim3(256), 0, st, a, a.q32, a.kdata, \
-                     a.scores, a.block_max)
+  if (items > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  int64_t blocks = (items + kScanWaves - 1) / kScanWaves;
+  const int64_t cap = 256 * 6;           // ~6 resident blocks of 4 waves per CU
+  if (blocks > cap) blocks = cap;
+#define CSA2_IDX_LAUNCH(C, Wt, M) \
+  hipLaunchKernelGGL((index_scan_kernel<C, Wt, M>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a)
   if (cand) {
     if (has_w) CSA2_IDX_LAUNCH(true, true, false); else CSA2_IDX_LAUNCH(true, false, false);
-  } else if (bmax) {
+  } else if (maxima) {
     if (has_w) CSA2_IDX_LAUNCH(false, true, true); else CSA2_IDX_LAUNCH(false, false, true);
   } else {
     if (has_w) CSA2_IDX_LAUNCH(false, true, false); else CSA2_IDX_LAUNCH(false, false, false);

@@ -16,67 +16,88 @@ struct IdxArgs {
   int32_t n_cand;
   int32_t R;
   int32_t n_max;
-  int32_t tiles_per_row;      // ceil(n_max/256) (scan) or n_cand/32 (Reindex)
+  int32_t steps_per_row;      // 64-position steps: ceil(n_max/64) (scan) or ceil(n_cand/8) (Reindex)
   int64_t score_stride;
   int64_t bmax_stride;
+  int64_t max64_stride;
   float* scores;
-  float* block_max;
+  float* block_max;           // [R][ceil(n_max/8)] maxima of 8 positions (scan, optional)
+  float* max64;               // [R][ceil(n_max/64)] maxima of 64 positions (scan, optional)
+  CSA2_TRACE_ARG
 };
 
+// Top-k over level 0 of a tree of maxima (level l+1 = maxima of 8 of level l).
 struct TopkArgs {
-  const float* scores;
-  int64_t row_stride;
+  const float* lv[3];         // level arrays (lv[1], lv[2] may be null when not needed)
+  int64_t lv_stride[3];
   const int32_t* row_seq;
-  const int32_t* n_valid;
-  int32_t n_max;
-  int32_t n_div;       // n = ceil(n_valid / n_div)
+  const int32_t* n_valid;     // per sequence, or null (n = n_max)
+  int32_t n_div;              // level-0 count = ceil(n_valid / n_div)
+  int32_t n_max;              // level-0 count cap
   int32_t R;
   int32_t k;
-  int32_t S_max;        // segments per row at n_max
-  int32_t kcap;         // candidate slots per segment = min(k, kSeg)
-  const int32_t* cand_blocks;   // optional index -> position map
+  const int32_t* cand_blocks; // optional index -> position map of the output
   int32_t cand_stride;
   int32_t* out;
   int32_t out_stride;
-  uint32_t* cand_key;   // [R][S_max*kcap]
-  int32_t* cand_idx;    // [R][S_max*kcap]
-  int32_t* seg_info;    // [R][S_max][4]: truncated, worst key, worst index
-  uint32_t* ticket;     // [R], zero between calls
+  CSA2_TRACE_ARG
+};
+
+struct MaximaArgs {
+  const float* in;
+  int64_t in_stride;
+  float* out;
+  int64_t out_stride;
+  int64_t n_out_max;          // groups per row at the largest row
+  int64_t div_in;             // this input level holds ceil(n0 / div_in) values
+  const int32_t* row_seq;
+  const int32_t* n_valid;
+  int32_t n_div;
+  int32_t n_max;              // level-0 count cap
+  int32_t R;
+};
+
+constexpr int kMaxAttnLayers = CSA2_MAX_GROUP_LAYERS;
+constexpr int kMaxAttnBlocks = 5;
+
+struct AttnLayer {
+  const uint4* q;               // [R][16][64] uint4 (8 bf16 each)
+  const uint4* swa_k;           // [B][S][64] uint4
+  const uint4* swa_v;
+  const int32_t* swa_start;     // [R]
+  const int32_t* swa_len;       // [R]
+  float* out;                   // [R][16][512]
+  float* lse;                   // [R][16] or null
+  int32_t S;
+  float sm_scale;
 };
 
 struct AttnArgs {
-  const uint4* q;               // [R][16][64] uint4 (8 bf16 each)
+  AttnLayer layer[kMaxAttnLayers];
+  int32_t n_layers;
   const uint8_t* kv;            // [n_slots][256]
   const uint8_t* kv_scale;      // [n_slots][32]
   SlotMap map;
   const int32_t* row_seq;
   const int32_t* seq_len;
-  const int32_t* idx;           // [R][k]
+  const int32_t* idx;           // [R][k], shared by every layer of the launch
   int32_t k;
-  const uint4* swa_k;           // [B][S][64] uint4
-  const uint4* swa_v;
-  int32_t S;
-  const int32_t* swa_start;
-  const int32_t* swa_len;
-  float sm_scale;
   int32_t R;
-  float* out;                   // [R][16][512]
-  float* lse;                   // [R][16] or null
-  float* part_o;                // [R][n_splits][16][512]
-  float* part_ml;               // [R][n_splits][16][2]
-  uint32_t* ticket;             // [R]
-  int32_t n_main_splits;
-  int32_t n_splits;
+  int32_t n_blocks;             // blocks per (layer, row)
+  int32_t steps_per_block;    // 128-key steps per block
+  float* part_o;                // [n_layers][R][n_blocks][16][512]
+  float* part_ml;               // [n_layers][R][n_blocks][16][2]
+  CSA2_TRACE_ARG
 };
 
-hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool bmax, hipStream_t st);
+hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxima, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_maxima(const MaximaArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,
                         int64_t n_slots, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
-int topk_segments(int n_max);
-int topk_kcap(int k);
-int attn_splits(int k, int* n_main);
+int attn_steps(int k);
+int attn_blocks(int k, int rows_x_layers, int* steps_per_block);
 
 }  // namespace csa2

@@ -1,43 +1,137 @@
-// Block-wide exact selection primitives (radix select on order-preserving
-// uint32 keys, order-preserving compaction).  Used by the Top-K kernels.
+// Block-wide exact selection on order-preserving uint32 keys (key 0 = absent).
 //
-// Ordering everywhere: key descending, index ascending.  Key 0 = absent.
+// A block (kSelThreads threads) selects among keys held either in registers
+// (RegKeys: kRegPer keys per thread, thread t holding elements
+// kRegPer*t .. kRegPer*t+kRegPer-1) or in LDS (LdsKeys: up to kSelCap keys,
+// element e at a skewed index so that per-thread contiguous runs are read
+// with few bank conflicts, padded with absent keys to a multiple of kSelPad).
+//
+// The k-th largest key is found by a radix search over an adaptive key range:
+// each pass histograms (key - lo) >> shift into kSelBins LDS bins, the shift
+// chosen so the current range fills the bins, which keeps same-bin collisions
+// (and LDS atomic serialisation) low even when the keys share their top bits.
+// A search may stop early once the keys at or above a bin edge are few enough
+// (a superset of the top k).
+//
+// Cost model (one CU per row): every pass touches every key a few times at 64
+// lanes per cycle, so the callers keep the key sets they search small.
 #pragma once
 #include "common.h"
 
 namespace csa2 {
 
-// Threads own contiguous runs of PER elements ("chunk" = NT*PER elements);
-// element e of a chunk belongs to thread e / PER.
-template <int NT>
-struct SelectSmem {
-  uint32_t hist[4096];
-  uint32_t wtot[NT / kWave];
-  uint32_t bcast[8];
-  unsigned long long last;   // 1 + largest kept tie index (0: none)
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelCap = 16384;                 // keys an LDS key set may hold
+constexpr int kSelBins = 2048;
+constexpr int kSelBinsPerThread = kSelBins / kSelThreads;
+constexpr int kRegPer = 4;                     // keys per thread of a register key set
+constexpr int kRegCap = kSelThreads * kRegPer; // 2048
+
+CSA2_DEV int skew(int e) { return e + (e >> 5); }
+constexpr int kSelKeyWords = kSelCap + kSelCap / 32;
+
+struct SelSmem {
+  uint32_t key[kSelKeyWords];
+  uint32_t bins[kSelBins];
+  uint32_t wa[kSelWaves];
+  uint32_t wb[kSelWaves];
+  uint32_t wc[kSelWaves];
+  uint32_t bc[4];
 };
 
-CSA2_DEV uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = lane_id();
+// LDS key sets are read in batches of kSelBatch independent reads without
+// bounds tests (a test per read would make the compiler wait on each read).
+constexpr int kSelBatch = 8;
+constexpr int kSelPad = kSelBatch * kSelThreads;    // 4096
+CSA2_DEV int sel_padded(int n) { return (n + kSelPad - 1) / kSelPad * kSelPad; }
+
+// Keys in registers: thread t holds elements kRegPer*t + j.
+struct RegKeys {
+  uint32_t v[kRegPer];
+  template <class F>
+  CSA2_DEV void each(const F& f) const {
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
+    for (int j = 0; j < kRegPer; ++j) f(v[j]);
   }
+  template <class F>
+  CSA2_DEV void each_owned(const F& f) const {       // contiguous, in element order
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) f(v[j], kRegPer * (int)threadIdx.x + j);
+  }
+};
+
+// Keys in LDS: sm.key[skew(e)] for e < n (n a multiple of kSelPad).
+struct LdsKeys {
+  const SelSmem* sm;
+  int n;
+  template <class F>
+  CSA2_DEV void each(const F& f) const {
+    for (int e0 = threadIdx.x; e0 < n; e0 += kSelPad) {
+      uint32_t v[kSelBatch];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) v[j] = sm->key[skew(e0 + j * kSelThreads)];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) f(v[j]);
+    }
+  }
+  template <class F>
+  CSA2_DEV void each_owned(const F& f) const {       // thread t: elements [t*C, (t+1)*C)
+    const int C = n / kSelThreads;                    // a multiple of kSelBatch
+    const int e0 = (int)threadIdx.x * C;
+    for (int b = e0; b < e0 + C; b += kSelBatch) {
+      uint32_t v[kSelBatch];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) v[j] = sm->key[skew(b + j)];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) f(v[j], b + j);
+    }
+  }
+};
+
+// Wave-wide inclusive scan and reductions through DPP lane shifts (no LDS
+// round trips): shifts by 1, 2, 4, 8 within each row of 16 lanes, then the
+// last lane of a row is broadcast into the next row(s).  Lanes whose source
+// lies outside the row receive 0 (the `old` operand).
+#define CSA2_DPP_U(v, ctrl, rmask) \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), (rmask), 0xF, false))
+CSA2_DEV uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += CSA2_DPP_U(v, 0x111, 0xF);   // row_shr:1
+  v += CSA2_DPP_U(v, 0x112, 0xF);   // row_shr:2
+  v += CSA2_DPP_U(v, 0x114, 0xF);   // row_shr:4
+  v += CSA2_DPP_U(v, 0x118, 0xF);   // row_shr:8
+  v += CSA2_DPP_U(v, 0x142, 0xA);   // row_bcast:15 into rows 1, 3
+  v += CSA2_DPP_U(v, 0x143, 0xC);   // row_bcast:31 into rows 2, 3
   return v;
 }
+// max / min / sum over the wave, valid in every lane
+CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, CSA2_DPP_U(v, 0x111, 0xF));
+  v = max(v, CSA2_DPP_U(v, 0x112, 0xF));
+  v = max(v, CSA2_DPP_U(v, 0x114, 0xF));
+  v = max(v, CSA2_DPP_U(v, 0x118, 0xF));
+  v = max(v, CSA2_DPP_U(v, 0x142, 0xA));
+  v = max(v, CSA2_DPP_U(v, 0x143, 0xC));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+CSA2_DEV uint32_t wave_min_u32(uint32_t v) {
+  // shifted-in zeros must not win: complement, take the max, complement back
+  return ~wave_max_u32(~v);
+}
+CSA2_DEV uint32_t wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(v), 63);
+}
 
-// Exclusive prefix sum of v over the block (thread order); also returns the total.
-template <int NT>
-CSA2_DEV uint32_t block_excl_scan(SelectSmem<NT>& sm, uint32_t v, uint32_t& total) {
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  uint32_t inc = wave_incl_scan(v);
-  if (lane == kWave - 1) sm.wtot[w] = inc;
+// Exclusive prefix sum of v in thread order; total returned through `total`.
+CSA2_DEV uint32_t block_excl_scan(SelSmem& sm, uint32_t v, uint32_t& total) {
+  const int tid = threadIdx.x, w = tid / kWave;
+  const uint32_t inc = wave_incl_scan_u32(v);
+  if (lane_id() == kWave - 1) sm.wa[w] = inc;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < NT / kWave; ++i) {
-    uint32_t t = sm.wtot[i];
+  for (int i = 0; i < kSelWaves; ++i) {
+    const uint32_t t = sm.wa[i];
     before += (i < w) ? t : 0u;
     tot += t;
   }
@@ -46,122 +140,161 @@ CSA2_DEV uint32_t block_excl_scan(SelectSmem<NT>& sm, uint32_t v, uint32_t& tota
   return before + inc - v;
 }
 
-// Source of keys: a functor load(chunk_base, tid, out[PER]) filling the PER keys
-// of thread tid for elements chunk_base + tid*PER + j (absent -> 0).
-
-// Radix select: the kth largest present key among n elements.
-// Returns T (0 if fewer than kth keys are present) and sets cnt_gt to the number
-// of present keys > T and cnt_eq to the number equal to T (both exact).
-template <int NT, int PER, class Src>
-CSA2_DEV uint32_t radix_select(SelectSmem<NT>& sm, const Src& src, int64_t n, uint32_t kth,
-                               uint32_t& cnt_gt, uint32_t& cnt_eq) {
-  const int tid = threadIdx.x;
-  constexpr int CH = NT * PER;
-  uint32_t prefix = 0, mask = 0, remaining = kth;
-  const int shifts[3] = {20, 8, 0};
-  const int nbins[3] = {4096, 4096, 256};
-  uint32_t last_count = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass], nb = nbins[pass];
-    for (int b = tid; b < nb; b += NT) sm.hist[b] = 0;
-    __syncthreads();
-    for (int64_t base = 0; base < n; base += CH) {
-      uint32_t k[PER];
-      src.load(base, tid, k);
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (k[j] != 0u && (k[j] & mask) == prefix) atomicAdd(&sm.hist[(k[j] >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    // thread t covers bins from the top: [nb - (t+1)*bpt, nb - t*bpt)
-    const int bpt = (nb + NT - 1) / NT;
-    const int hi = nb - tid * bpt;            // exclusive upper bound
-    const int lo = hi - bpt < 0 ? 0 : hi - bpt;
-    uint32_t mine = 0;
-    for (int b = lo; b < hi; ++b) mine += sm.hist[b];
-    uint32_t total;
-    uint32_t above = block_excl_scan<NT>(sm, hi > 0 ? mine : 0u, total);
-    if (pass == 0 && total < remaining) {
-      // fewer present keys than kth: everything present is "greater than" T = 0
-      cnt_gt = total;
-      cnt_eq = 0;
-      return 0u;
-    }
-    if (hi > 0 && above < remaining && above + mine >= remaining) {
-      uint32_t acc = above;
-      for (int b = hi - 1; b >= lo; --b) {
-        uint32_t h = sm.hist[b];
-        if (acc + h >= remaining) {
-          sm.bcast[0] = (uint32_t)b;
-          sm.bcast[1] = acc;
-          sm.bcast[2] = h;
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-    const uint32_t d = sm.bcast[0], acc = sm.bcast[1];
-    last_count = sm.bcast[2];
-    __syncthreads();
-    remaining -= acc;
-    prefix |= d << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
+// Minimum and maximum present key, and the number of present keys.
+template <class Keys>
+CSA2_DEV void block_range(SelSmem& sm, const Keys& ks, uint32_t& kmin, uint32_t& kmax, uint32_t& count) {
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u, c = 0u;
+  ks.each([&](uint32_t v) {
+    mn = v ? min(mn, v) : mn;
+    mx = max(mx, v);
+    c += v ? 1u : 0u;
+  });
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  c = wave_sum_u32(c);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    sm.wa[w] = mn;
+    sm.wb[w] = mx;
+    sm.wc[w] = c;
   }
-  cnt_gt = kth - remaining;
-  cnt_eq = last_count;
-  return prefix;
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+  c = 0u;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    mn = min(mn, sm.wa[i]);
+    mx = max(mx, sm.wb[i]);
+    c += sm.wc[i];
+  }
+  __syncthreads();
+  kmin = mn;
+  kmax = mx;
+  count = c;
 }
 
-// Order-preserving compaction of the selection {key > T} U {the first need_eq
-// keys == T in index order}; T == 0 keeps every present key.  For each kept
-// element calls emit(out_pos, key, element_index).  Returns the number kept.
-// Also reports the index of the last kept element equal to T (or -1).
-template <int NT, int PER, class Src, class Emit>
-CSA2_DEV uint32_t compact(SelectSmem<NT>& sm, const Src& src, int64_t n, uint32_t T,
-                          uint32_t need_eq, const Emit& emit, int64_t& last_tie_idx) {
+struct SelResult {
+  uint32_t T;       // threshold key: keep keys > T, and keys == T as below
+  uint32_t n_gt;    // present keys > T
+  uint32_t n_eq;    // present keys == T
+  bool exact;       // T is the k-th largest key (ties at T must be cut by element order)
+};
+
+// The k-th largest present key (exact = true), or, when `cap` > 0, an earlier
+// bin edge T such that k <= #{keys >= T} <= cap (exact = false; keep every
+// key >= T).  With at most k present keys: T = 0, n_gt = count (keep all).
+template <class Keys>
+CSA2_DEV SelResult block_select(SelSmem& sm, const Keys& ks, uint32_t kth, uint32_t cap, uint64_t* tr = nullptr) {
   const int tid = threadIdx.x;
-  constexpr int CH = NT * PER;
-  uint32_t out_before = 0, eq_before = 0;
-  int64_t last_tie = -1;
-  for (int64_t base = 0; base < n; base += CH) {
-    uint32_t k[PER];
-    src.load(base, tid, k);
-    uint32_t n_eq = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) n_eq += (T != 0u && k[j] == T) ? 1u : 0u;
-    uint32_t eq_tot;
-    uint32_t eq_rank = eq_before + block_excl_scan<NT>(sm, n_eq, eq_tot);
-    bool keep[PER];
-    uint32_t n_keep = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      bool gt = (T == 0u) ? (k[j] != 0u) : (k[j] > T);
-      bool eq = (T != 0u) && (k[j] == T);
-      bool kt = eq && (eq_rank < need_eq);
-      if (eq) {
-        if (kt) last_tie = base + (int64_t)tid * PER + j;
-        ++eq_rank;
-      }
-      keep[j] = gt || kt;
-      n_keep += keep[j] ? 1u : 0u;
-    }
-    uint32_t keep_tot;
-    uint32_t pos = out_before + block_excl_scan<NT>(sm, n_keep, keep_tot);
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (keep[j]) emit(pos++, k[j], base + (int64_t)tid * PER + j);
-    out_before += keep_tot;
-    eq_before += eq_tot;
+  uint32_t lo, hi, count;
+  block_range(sm, ks, lo, hi, count);
+  CSA2_MARKP(tr, 0);
+  int pass = 0;
+  SelResult res;
+  if (count <= kth) {
+    res.T = 0u;
+    res.n_gt = count;
+    res.n_eq = 0u;
+    res.exact = true;
+    return res;
   }
-  // largest index among kept ties (the worst kept element)
-  if (tid == 0) sm.last = 0ull;
-  __syncthreads();
-  if (last_tie >= 0) atomicMax(&sm.last, (unsigned long long)(last_tie + 1));
-  __syncthreads();
-  last_tie_idx = (int64_t)sm.last - 1;
-  __syncthreads();
-  return out_before;
+  uint32_t above = 0u;   // keys > hi
+  for (;;) {
+    // the range [lo, hi] holds the k-th largest; `above` keys lie above it
+    const uint32_t width = hi - lo;
+    int shift = 0;
+    while (shift < 32 && (width >> shift) >= (uint32_t)kSelBins) ++shift;
+#pragma unroll
+    for (int i = 0; i < kSelBinsPerThread; ++i) sm.bins[tid + i * kSelThreads] = 0u;
+    __syncthreads();
+    ks.each([&](uint32_t v) {
+      if (v >= lo && v <= hi && v != 0u) atomicAdd(&sm.bins[(v - lo) >> shift], 1u);
+    });
+    __syncthreads();
+    // thread t owns the kSelBinsPerThread bins just below B - BPT*t, scanned from the top
+    const int top = kSelBins - kSelBinsPerThread * tid;
+    uint32_t hb[kSelBinsPerThread];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kSelBinsPerThread; ++i) {
+      hb[i] = sm.bins[top - 1 - i];
+      cnt += hb[i];
+    }
+    uint32_t tot;
+    const uint32_t before = above + block_excl_scan(sm, cnt, tot);
+    if (before < kth && before + cnt >= kth) {
+      uint32_t acc = before;
+#pragma unroll
+      for (int i = 0; i < kSelBinsPerThread; ++i) {
+        if (acc < kth && acc + hb[i] >= kth) {
+          sm.bc[0] = (uint32_t)(top - 1 - i);
+          sm.bc[1] = acc;
+          sm.bc[2] = hb[i];
+        }
+        acc += hb[i];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sm.bc[0], acc = sm.bc[1], h = sm.bc[2];
+    __syncthreads();
+    CSA2_MARKP(tr, 1 + (pass++));
+    const uint32_t blo = lo + (bin << shift);
+    const uint32_t bhi =
+        (shift == 0) ? blo : (uint32_t)min((uint64_t)hi, (uint64_t)blo + ((1ull << shift) - 1ull));
+    if (cap && acc + h <= cap) {
+      res.T = blo;
+      res.n_gt = acc + h;
+      res.n_eq = 0u;
+      res.exact = false;
+      return res;
+    }
+    if (blo == bhi) {
+      res.T = blo;
+      res.n_gt = acc;
+      res.n_eq = h;
+      res.exact = true;
+      return res;
+    }
+    above = acc;
+    lo = blo;
+    hi = bhi;
+  }
+}
+
+// Order-preserving compaction of the selection described by `s` with k
+// wanted: keys > T, plus (exact) the first k - n_gt keys == T in element
+// order, or (not exact) every key >= T.  emit(out_pos, element) is called for
+// each kept element; returns the number kept.
+template <class Keys, class Emit>
+CSA2_DEV uint32_t block_compact(SelSmem& sm, const Keys& ks, const SelResult& s, uint32_t kth, const Emit& emit) {
+  const uint32_t need_eq = s.exact ? (kth > s.n_gt ? kth - s.n_gt : 0u) : 0u;
+  const bool keep_all = (s.T == 0u);
+  const uint32_t T = s.T;
+  const bool cut_eq = !keep_all && s.exact;
+  // keep-all: every present key; exact: keys > T (ties separately); superset: keys >= T
+  const uint32_t gt_lo = keep_all ? 1u : (s.exact ? T + 1u : T);
+  const bool none_gt = s.exact && !keep_all && T == 0xFFFFFFFFu;
+  uint32_t n_keep = 0, n_eq = 0;
+  ks.each_owned([&](uint32_t v, int) {
+    n_keep += (!none_gt && v >= gt_lo) ? 1u : 0u;
+    n_eq += (cut_eq && v == T) ? 1u : 0u;
+  });
+  // one scan of both counts (each total <= kSelCap < 2^16)
+  uint32_t tot;
+  const uint32_t pre = block_excl_scan(sm, n_keep | (n_eq << 16), tot);
+  uint32_t eq_rank = pre >> 16;
+  uint32_t pos = (pre & 0xFFFFu) + min(eq_rank, need_eq);
+  ks.each_owned([&](uint32_t v, int e) {
+    bool keep = !none_gt && v >= gt_lo;
+    if (cut_eq && v == T) {
+      keep = eq_rank < need_eq;
+      ++eq_rank;
+    }
+    if (keep) emit(pos++, e);
+  });
+  const uint32_t total_gt = tot & 0xFFFFu, total_eq = tot >> 16;
+  return total_gt + min(total_eq, need_eq);
 }
 
 }  // namespace csa2

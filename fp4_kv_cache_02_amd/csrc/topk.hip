@@ -2,181 +2,318 @@
 // the 2048 candidate blocks of the hierarchical indexer: conexaotc.com.br page
 // "DeepSeek lança V4.1-Flash...", paragraph on CSA2).
 //
-// Order: score descending, index ascending (-0 below +0); -inf = absent;
+// Order: value descending, index ascending (-0 below +0); -inf = absent;
 // output ascending indices, -1 padding.
 //
-// Two stages in one launch.  Grid (rows, segments); a segment is 4096 scores.
-//  1. Every segment block selects its local top-kloc exactly (radix select on
-//     order-preserving keys) and writes it, in index order, to a padded slot
-//     of the row's candidate array (unused entries: key 0 = absent).
-//     kloc is sized from k*4096/n (expected share plus margin).
-//  2. The last segment block of a row to finish (atomic ticket) selects the
-//     top-k of the candidate union.  The union holds the true top-k unless a
-//     segment that dropped elements kept a worst element that ranks above the
-//     k-th selected one; that is checked, and in that case the row is
-//     re-selected exactly from all its scores.
+// One block per row descends a tree of maxima.  Level 0 holds the n values;
+// level l+1 holds the maximum of each group of 8 consecutive level-l values
+// (the indexer scan emits levels 1 and 2 as it scores; `maxima_kernel` builds
+// them for other callers).  The descent rests on one fact: if a group holds an
+// element of the top k of its level, the group's maximum is in the top k of
+// the level above.  (Were k groups ranked above it, each would contain an
+// element ranked above that element -- with equal values the group with the
+// lower index holds the lower element indices -- so it would not be in the top
+// k.)  Hence, starting at the coarsest level with at most 16384 values:
+//   * keep a superset of the level's top-k groups: every group whose maximum
+//     is at or above a bin edge T with k <= #{>= T} <= 2048 (a radix search
+//     that stops early) -- or, when ties prevent that, the exact top k;
+//   * the children of the kept groups (at most 2048 * 8 = 16384 values, in
+//     index order) are the candidates one level down;
+//   * at level 0 the exact top k is taken (ties cut by index) and written in
+//     index order.
 #include "select.h"
 #include "kernels.h"
 
 namespace csa2 {
 
-constexpr int kSeg = 4096;
-constexpr int kTopkThreads = 512;
-constexpr int kPer = kSeg / kTopkThreads;   // 8
-
-
-struct ScoreSrc {
-  const float* p;
-  int64_t n;
-  CSA2_DEV void load(int64_t base, int tid, uint32_t (&k)[kPer]) const {
-    const int64_t e0 = base + (int64_t)tid * kPer;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) k[j] = (e0 + j < n) ? order_key(p[e0 + j]) : 0u;
-  }
-};
-
-struct KeySrc {
-  const uint32_t* p;
-  int64_t n;
-  CSA2_DEV void load(int64_t base, int tid, uint32_t (&k)[kPer]) const {
-    const int64_t e0 = base + (int64_t)tid * kPer;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) k[j] = (e0 + j < n) ? p[e0 + j] : 0u;
-  }
-};
-
-CSA2_DEV int row_n(const TopkArgs& a, int r) {
-  int n = a.n_max;
+CSA2_DEV int64_t row_count(const TopkArgs& a, int r) {
+  int64_t n = a.n_max;
   if (a.n_valid) {
-    const int v = a.n_valid[a.row_seq ? a.row_seq[r] : r];
+    const int64_t v = a.n_valid[a.row_seq ? a.row_seq[r] : r];
     n = v <= 0 ? 0 : (v + a.n_div - 1) / a.n_div;
   }
   return n > a.n_max ? a.n_max : n;
 }
 
-CSA2_DEV int kloc_for(int k, int n, int S) {
-  if (S <= 1) return k < kSeg ? k : kSeg;
-  const float mu = (float)k * (float)kSeg / (float)n;
-  const float v = mu + 4.0f * sqrtf(mu) + 8.0f;
-  int kl = 16;
-  while ((float)kl < v) kl <<= 1;
-  const int cap = k < kSeg ? k : kSeg;
-  return kl > cap ? cap : kl;
+
+// Threshold path.  tau = the k-th largest value of the top level T (the
+// lowest level with at most kRegCap values, taken as maxima of 8 of level T-1
+// when level T is not stored).  By the fact above applied level by level,
+// tau <= the k-th largest value of every level below, so the top k of level
+// 0 lie among the positions whose value is >= tau, and those are found by
+// descending through the groups whose value is >= tau.  Only two selections
+// run (at the top and among the final survivors), each over at most kRegCap
+// keys held in registers.  Returns false -- the row then takes the general
+// path -- when a level or the survivors would exceed kRegCap.
+CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, int32_t (*par)[kSelCap / 8],
+                             const int32_t* cmap, int32_t* out) {
+  const int tid = threadIdx.x;
+  const uint32_t K = (uint32_t)a.k;
+  int64_t nl[4];
+  nl[0] = n0;
+  for (int l = 1; l < 4; ++l) nl[l] = (nl[l - 1] + 7) / 8;
+  int T = 0;
+  while (T < 3 && nl[T] > kRegCap) ++T;
+  if (nl[T] > kRegCap) return false;
+  const bool direct = (T == 0) || (T <= 2 && a.lv[T] != nullptr);
+  if (!direct && (T - 1 > 2 || a.lv[T - 1] == nullptr)) return false;
+  for (int l = 0; l < T; ++l)
+    if (l > 2 || a.lv[l] == nullptr) return false;
+
+  // ---- top level: 4 values per thread ----
+  RegKeys top;
+  if (direct) {
+    const float* base = a.lv[T] + (int64_t)r * a.lv_stride[T];
+    float v[kRegPer];
+    if (((uintptr_t)base & 15u) == 0 && kRegPer * tid + kRegPer <= nl[T]) {
+      const float4 x = *(const float4*)(base + kRegPer * tid);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j) v[j] = base[min((int64_t)(kRegPer * tid + j), nl[T] - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) top.v[j] = (kRegPer * tid + j < nl[T]) ? order_key(v[j]) : 0u;
+  } else {
+    const float* base = a.lv[T - 1] + (int64_t)r * a.lv_stride[T - 1];
+    const int64_t nb = nl[T - 1];
+    float v[kRegPer * 8];
+    if (((uintptr_t)base & 15u) == 0 && 8 * kRegPer * tid + 8 * kRegPer <= nb) {
+#pragma unroll
+      for (int q = 0; q < 2 * kRegPer; ++q) {
+        const float4 x = *(const float4*)(base + 8 * kRegPer * tid + 4 * q);
+        v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRegPer * 8; ++j) v[j] = base[min((int64_t)(8 * kRegPer * tid + j), nb - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        m = max(m, (8 * (kRegPer * tid + j) + c < nb) ? order_key(v[8 * j + c]) : 0u);
+      top.v[j] = m;
+    }
+  }
+  CSA2_MARK(a, 9);
+  const SelResult s = block_select(sm, top, K, 0u, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 10 : nullptr);
+  CSA2_MARK(a, 1);
+  if (T == 0) {
+    const uint32_t m = block_compact(sm, top, s, K, [&](uint32_t pos, int e) {
+      out[pos] = a.cand_blocks ? cmap[e >> 3] * 8 + (e & 7) : e;
+    });
+    for (int i = (int)m + tid; i < (int)K; i += kSelThreads) out[i] = -1;
+    return true;
+  }
+  const uint32_t tau = max(s.T, 1u);     // s.T == 0: fewer than k present, all present qualify
+  SelResult ge;
+  ge.T = tau;
+  ge.n_gt = 0;
+  ge.n_eq = 0;
+  ge.exact = false;
+  int cur = 0;
+  int n_par = (int)block_compact(sm, top, ge, K, [&](uint32_t pos, int e) { par[0][pos] = e; });
+  __syncthreads();
+
+  // ---- descend: children of the kept groups with value >= tau ----
+  for (int l = T - 1; l >= 0; --l) {
+    const float* base = a.lv[l] + (int64_t)r * a.lv_stride[l];
+    const int64_t n = nl[l];
+    // children of this thread's parents kRegPer*t .. +kRegPer-1: two 16-byte
+    // loads per parent when the row is 16-byte aligned and the group is whole
+    const bool al16 = ((uintptr_t)base & 15u) == 0;
+    int64_t idx[kRegPer * 8];
+    float v[kRegPer * 8];
+#pragma unroll
+    for (int p = 0; p < kRegPer; ++p) {
+      const int pi = kRegPer * tid + p;
+      const int64_t g = (pi < n_par) ? (int64_t)par[cur][pi] : -1;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) idx[8 * p + c] = (g >= 0 && g * 8 + c < n) ? g * 8 + c : -1;
+      if (g >= 0 && al16 && g * 8 + 8 <= n) {
+        const float4 x = *(const float4*)(base + g * 8), y = *(const float4*)(base + g * 8 + 4);
+        v[8 * p + 0] = x.x; v[8 * p + 1] = x.y; v[8 * p + 2] = x.z; v[8 * p + 3] = x.w;
+        v[8 * p + 4] = y.x; v[8 * p + 5] = y.y; v[8 * p + 6] = y.z; v[8 * p + 7] = y.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[8 * p + c] = base[idx[8 * p + c] >= 0 ? idx[8 * p + c] : 0];
+      }
+    }
+    uint32_t cnt = 0;
+    uint32_t keepm = 0;           // bit j: child j kept
+#pragma unroll
+    for (int j = 0; j < kRegPer * 8; ++j) {
+      const bool kp = idx[j] >= 0 && order_key(v[j]) >= tau;
+      keepm |= kp ? (1u << j) : 0u;
+      cnt += kp ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_scan(sm, cnt, tot);
+    if (tot > (uint32_t)kRegCap) return false;      // uniform: every thread sees the same total
+    int32_t* dst = par[cur ^ 1];
+    if (l > 0) {
+#pragma unroll
+      for (int j = 0; j < kRegPer * 8; ++j)
+        if ((keepm >> j) & 1u) dst[pos++] = (int32_t)idx[j];
+      __syncthreads();
+      cur ^= 1;
+      n_par = (int)tot;
+      CSA2_MARK(a, 2 + l);
+      continue;
+    }
+    // level 0: survivors (key, position) in index order, then the exact top k
+#pragma unroll
+    for (int j = 0; j < kRegPer * 8; ++j)
+      if ((keepm >> j) & 1u) {
+        dst[pos] = (int32_t)idx[j];
+        sm.key[pos] = order_key(v[j]);
+        ++pos;
+      }
+    __syncthreads();
+    RegKeys sv;
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      const int e = kRegPer * tid + j;
+      sv.v[j] = (e < (int)tot) ? sm.key[e] : 0u;
+    }
+    const SelResult f = block_select(sm, sv, K, 0u);
+    CSA2_MARK(a, 6);
+    const uint32_t m = block_compact(sm, sv, f, K, [&](uint32_t o, int e) {
+      const int32_t i = dst[e];
+      out[o] = a.cand_blocks ? cmap[i >> 3] * 8 + (i & 7) : i;
+    });
+    for (int i = (int)m + tid; i < (int)K; i += kSelThreads) out[i] = -1;
+    CSA2_MARK(a, 7);
+    return true;
+  }
+  return true;
 }
 
-CSA2_DEV int32_t map_index(const TopkArgs& a, int r, int64_t i) {
-  if (!a.cand_blocks) return (int32_t)i;
-  const int32_t blk = a.cand_blocks[(int64_t)r * a.cand_stride + (i >> 3)];
-  return blk * 8 + (int32_t)(i & 7);
+// General path: at each level keep a superset of the top-k groups bounded by
+// 2048 (a radix search that stops early, or the exact top k when ties prevent
+// that), descending to the exact top k at level 0.  Handles any value
+// distribution; the keys of a level are staged in LDS.
+CSA2_DEV void topk_general(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, int32_t (*par)[kSelCap / 8],
+                           const int32_t* cmap, int32_t* out) {
+  const int tid = threadIdx.x;
+  const int64_t nl[3] = {n0, (n0 + 7) / 8, (n0 + 63) / 64};
+  int level = 0;
+  if (n0 > kSelCap) level = (nl[1] > kSelCap) ? 2 : 1;
+  bool all = true;     // candidates = every index of the level
+  int n_par = 0;       // otherwise: children of par[cur][0 .. n_par)
+  int cur = 0;
+  for (;;) {
+    const float* base = a.lv[level] + (int64_t)r * a.lv_stride[level];
+    const int64_t n = nl[level];
+    const int n_elem = all ? (int)n : 8 * n_par;
+    // candidates of this level into LDS in index order, padded with absent
+    // keys to a multiple of kSelPad; every read is in bounds (an absent
+    // candidate reads element 0 of the row, which exists when n_elem > 0)
+    const int n_pad = sel_padded(n_elem);
+    for (int e0 = tid; e0 < n_pad; e0 += kSelPad) {
+      int64_t src[kSelBatch];
+      bool ok[kSelBatch];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) {
+        const int e = e0 + j * kSelThreads;
+        const int ec = min(e, max(n_elem - 1, 0));
+        const int64_t i = all ? (int64_t)ec : (int64_t)par[cur][ec >> 3] * 8 + (ec & 7);
+        ok[j] = e < n_elem && i < n;
+        src[j] = ok[j] ? i : 0;
+      }
+      float v[kSelBatch];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) v[j] = base[src[j]];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) sm.key[skew(e0 + j * kSelThreads)] = ok[j] ? order_key(v[j]) : 0u;
+    }
+    __syncthreads();
+    const LdsKeys ks{&sm, n_pad};
+    auto index_of = [&](int e) -> int64_t {
+      return all ? (int64_t)e : (int64_t)par[cur][e >> 3] * 8 + (e & 7);
+    };
+    if (level > 0) {
+      const SelResult s = block_select(sm, ks, (uint32_t)a.k, kSelCap / 8);
+      int32_t* dst = par[cur ^ 1];
+      const uint32_t m = block_compact(sm, ks, s, (uint32_t)a.k, [&](uint32_t pos, int e) { dst[pos] = (int32_t)index_of(e); });
+      __syncthreads();
+      all = false;
+      n_par = (int)m;
+      cur ^= 1;
+      --level;
+    } else {
+      const SelResult s = block_select(sm, ks, (uint32_t)a.k, 0u);
+      const uint32_t m = block_compact(sm, ks, s, (uint32_t)a.k, [&](uint32_t pos, int e) {
+        const int64_t i = index_of(e);
+        out[pos] = a.cand_blocks ? cmap[i >> 3] * 8 + (int32_t)(i & 7) : (int32_t)i;
+      });
+      for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
+      return;
+    }
+  }
 }
 
-// Exact top-k of a whole row from its scores, written to the output.
-CSA2_DEV uint32_t select_row_direct(SelectSmem<kTopkThreads>& sm, const TopkArgs& a, int r,
-                                    const float* row, int64_t n) {
-  ScoreSrc src{row, n};
-  uint32_t gt, eq;
-  const uint32_t T = radix_select<kTopkThreads, kPer>(sm, src, n, (uint32_t)a.k, gt, eq);
-  const uint32_t need_eq = T ? (uint32_t)a.k - gt : 0u;
+__global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
+  __shared__ SelSmem sm;
+  __shared__ int32_t par[2][kSelCap / 8];
+  __shared__ int32_t cmap[kSelCap / 8];     // the row's candidate blocks (output index map)
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (a.cand_blocks)
+    for (int i = tid; i < a.cand_stride; i += kSelThreads) cmap[i] = a.cand_blocks[(int64_t)r * a.cand_stride + i];
+  const int64_t n0 = row_count(a, r);
   int32_t* out = a.out + (int64_t)r * a.out_stride;
-  int64_t last;
-  return compact<kTopkThreads, kPer>(
-      sm, src, n, T, need_eq,
-      [&](uint32_t pos, uint32_t, int64_t e) { out[pos] = map_index(a, r, e); }, last);
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ SelectSmem<kTopkThreads> sm;
-  const int r = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
-  const int n = row_n(a, r);
-  const int S = n > kSeg ? (n + kSeg - 1) / kSeg : 1;
-  if (s >= S) return;
-  const float* row = a.scores + (int64_t)r * a.row_stride;
-  int32_t* out = a.out + (int64_t)r * a.out_stride;
-
-  if (S == 1) {
-    const uint32_t m = select_row_direct(sm, a, r, row, n);
-    for (int i = (int)m + tid; i < a.k; i += kTopkThreads) out[i] = -1;
+  CSA2_MARK(a, 0);
+  if (n0 == 0) {
+    for (int i = tid; i < a.k; i += kSelThreads) out[i] = -1;
     return;
   }
-
-  // ---- stage 1: local selection of this segment ----
-  const int kloc = kloc_for(a.k, n, S);
-  const int64_t base = (int64_t)s * kSeg;
-  const int64_t cnt = (n - base) < kSeg ? (n - base) : kSeg;
-  ScoreSrc src{row + base, cnt};
-  uint32_t gt, eq;
-  const uint32_t T = radix_select<kTopkThreads, kPer>(sm, src, cnt, (uint32_t)kloc, gt, eq);
-  const uint32_t need_eq = T ? (uint32_t)kloc - gt : 0u;
-  const int64_t row_cbase = (int64_t)r * a.S_max * a.kcap;
-  uint32_t* ck = a.cand_key + row_cbase + (int64_t)s * kloc;
-  int32_t* ci = a.cand_idx + row_cbase + (int64_t)s * kloc;
-  int64_t last_tie;
-  const uint32_t m = compact<kTopkThreads, kPer>(
-      sm, src, cnt, T, need_eq,
-      [&](uint32_t pos, uint32_t key, int64_t e) { ck[pos] = key; ci[pos] = (int32_t)(base + e); },
-      last_tie);
-  for (int i = (int)m + tid; i < kloc; i += kTopkThreads) ck[i] = 0u;
-  if (tid == 0) {
-    // A segment with T != 0 kept exactly kloc elements and may have dropped
-    // others ("truncated"); record its worst kept element: key T, and the
-    // largest index among its kept elements equal to T.
-    int32_t* info = a.seg_info + ((int64_t)r * a.S_max + s) * 4;
-    info[0] = T != 0u ? 1 : 0;
-    info[1] = (int32_t)T;
-    info[2] = (int32_t)(base + last_tie);
-    info[3] = (int32_t)m;
+  __syncthreads();   // cmap visible
+  if (!topk_threshold(a, r, n0, sm, par, cmap, out)) {
+    __syncthreads();
+    topk_general(a, r, n0, sm, par, cmap, out);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&a.ticket[r], 1u);
-    sm.bcast[4] = (old == (uint32_t)(S - 1)) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (sm.bcast[4] == 0u) return;
-  __threadfence();
+  CSA2_MARK(a, 8);
+}
 
-  // ---- stage 2: the last block of the row selects from the union ----
-  const int64_t un = (int64_t)S * kloc;
-  KeySrc usrc{a.cand_key + row_cbase, un};
-  const int32_t* uidx = a.cand_idx + row_cbase;
-  uint32_t ugt, ueq;
-  const uint32_t UT = radix_select<kTopkThreads, kPer>(sm, usrc, un, (uint32_t)a.k, ugt, ueq);
-  const uint32_t uneed = UT ? (uint32_t)a.k - ugt : 0u;
-  int64_t ulast;
-  uint32_t um = compact<kTopkThreads, kPer>(
-      sm, usrc, un, UT, uneed,
-      [&](uint32_t pos, uint32_t, int64_t e) { out[pos] = map_index(a, r, uidx[e]); }, ulast);
-  const int64_t tk_idx = (UT != 0u && ulast >= 0) ? (int64_t)uidx[ulast] : -1;
-
-  // safety check: a segment that kept exactly kloc of more present elements is
-  // "truncated"; its worst kept element must not rank above the k-th selected.
-  uint32_t unsafe = 0;
-  for (int seg = tid; seg < S; seg += kTopkThreads) {
-    const int32_t* info = a.seg_info + ((int64_t)r * a.S_max + seg) * 4;
-    if (info[0] == 0) continue;               // kept every present element
-    if (UT == 0u) { unsafe = 1; continue; }   // union has < k present but a segment dropped some
-    const uint32_t Ts = (uint32_t)info[1];
-    const int64_t ws_idx = info[2];
-    if (Ts > UT || (Ts == UT && ws_idx < tk_idx)) unsafe = 1;
+// out[r][g] = maximum (in the Top-k order) of in[r][8g .. 8g+7] below the
+// row's count, -inf when none is present.  The row's count at this level is
+// ceil(n0 / div) with n0 the level-0 count of the row.
+__global__ __launch_bounds__(256) void maxima_kernel(MaximaArgs a) {
+  const int64_t total = (int64_t)a.R * a.n_out_max;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(t / a.n_out_max);
+    const int64_t g = t - (int64_t)r * a.n_out_max;
+    int64_t n0 = a.n_max;
+    if (a.n_valid) {
+      const int64_t v = a.n_valid[a.row_seq ? a.row_seq[r] : r];
+      n0 = v <= 0 ? 0 : (v + a.n_div - 1) / a.n_div;
+      if (n0 > a.n_max) n0 = a.n_max;
+    }
+    const int64_t n_in = (n0 + a.div_in - 1) / a.div_in;
+    if (g * 8 >= n_in) continue;
+    const float* src = a.in + (int64_t)r * a.in_stride + g * 8;
+    uint32_t k = 0u;
+    for (int c = 0; c < 8 && g * 8 + c < n_in; ++c) k = max(k, order_key(src[c]));
+    a.out[(int64_t)r * a.out_stride + g] = k ? key_to_float(k) : -__builtin_inff();
   }
-  if (tid == 0) sm.bcast[5] = 0u;
-  __syncthreads();
-  if (unsafe) atomicOr(&sm.bcast[5], 1u);
-  __syncthreads();
-  if (sm.bcast[5]) um = select_row_direct(sm, a, r, row, n);
-  for (int i = (int)um + tid; i < a.k; i += kTopkThreads) out[i] = -1;
-  if (tid == 0) a.ticket[r] = 0u;
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
-  dim3 grid(a.R, a.S_max > 0 ? a.S_max : 1);
-  hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, st, a);
+  hipLaunchKernelGGL(topk_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 
-int topk_segments(int n_max) { return n_max > kSeg ? (n_max + kSeg - 1) / kSeg : 1; }
-int topk_kcap(int k) { return k < kSeg ? k : kSeg; }
+hipError_t launch_maxima(const MaximaArgs& a, hipStream_t st) {
+  const int64_t total = (int64_t)a.R * a.n_out_max;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(maxima_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 }  // namespace csa2

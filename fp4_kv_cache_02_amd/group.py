@@ -120,6 +120,20 @@ def build_inputs(w: synth.Workload, kv_fp4=None, kv_scale=None, device="cuda") -
                        layers=layer_inputs_from_synth(w, device))
 
 
+def split_groups(schedule: str):
+    """(first layer, layer count) of each group: a Full or Reindex layer and
+    the Reuse layers after it (a leading run of Reuse layers is a group too).
+    A Full layer that only builds candidates forms a group of its own when a
+    Reindex layer follows it."""
+    groups = []
+    for li, m in enumerate(schedule):
+        if li == 0 or m in "FI" or groups[-1][1] >= csa2.MAX_GROUP_LAYERS:
+            groups.append([li, 1])
+        else:
+            groups[-1][1] += 1
+    return [tuple(g) for g in groups]
+
+
 class GroupRunner:
     """Owns the outputs, the shared Top-K / candidate buffers and the workspace
     of one layer group; ``step()`` runs every layer of the schedule once."""
@@ -134,7 +148,11 @@ class GroupRunner:
         self.cand = torch.full((R, csa2.KEEP_BLOCKS), -1, dtype=torch.int32, device=device)
         self.shared = csa2.make_shared(self.kv, self.kidx, inp.seq_len, w.n_max, self.topk_idx, self.cand,
                                        hier=w.hier)
+        self.groups = split_groups(w.schedule)
         ws_bytes = max(csa2.csa2_workspace_bytes(m, R, w.n_max, w.hier) for m in (0, 1, 2))
+        for li0, n in self.groups:
+            ws_bytes = max(ws_bytes, csa2.csa2_group_workspace_bytes(synth.MODES[w.schedule[li0]], n, R, w.n_max,
+                                                                     w.hier))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         csa2.csa2_workspace_init(self.ws)
         self.out = [torch.zeros((R, 16, 512), dtype=torch.float32, device=device) for _ in w.schedule]
@@ -147,12 +165,21 @@ class GroupRunner:
                                                   self.out[li], self.lse[li], q_idx=L.q_idx, row_seq=inp.row_seq,
                                                   blocks_only=blocks_only, R=R))
 
+        self.group_args = [csa2.make_layer_array(self.args[li0:li0 + n]) for li0, n in self.groups]
+
     def step_layer(self, li: int, stream=None):
+        """One layer on its own (csa2_layer_step)."""
         csa2.csa2_layer_step(synth.MODES[self.w.schedule[li]], self.args[li], self.shared, self.ws, stream)
 
+    def step_group(self, gi: int, stream=None):
+        """One group: a Full/Reindex layer and the Reuse layers after it (csa2_group_step)."""
+        li0, _ = self.groups[gi]
+        csa2.csa2_group_step(synth.MODES[self.w.schedule[li0]], self.group_args[gi], self.shared, self.ws, stream)
+
     def step(self, stream=None):
-        for li in range(len(self.w.schedule)):
-            self.step_layer(li, stream)
+        """Every layer of the schedule once, one group call per group."""
+        for gi in range(len(self.groups)):
+            self.step_group(gi, stream)
 
     def attended_layers(self) -> List[int]:
         return [li for li, m in enumerate(self.w.schedule)

@@ -58,6 +58,7 @@ typedef struct ihipStream_t* hipStream_t;
 #define CSA2_MAX_K 2048      /* largest k accepted by csa2_topk                     */
 #define CSA2_PAGE 64         /* positions per page of a paged cache                 */
 #define CSA2_MAX_ROWS 65536  /* largest number of query rows per call               */
+#define CSA2_MAX_GROUP_LAYERS 8 /* layers one csa2_group_step call may run          */
 
 typedef enum {
   CSA2_OK = 0,
@@ -107,9 +108,10 @@ typedef struct {
  * (w0*r0 + w1*r1) + (w2*r2 + w3*r3) with each product rounded on its own.
  *
  * cand_blocks == NULL (scan):  scores[r][p] for p < L (entries p >= L are not
- *   written); if block_max != NULL, block_max[r][j] = the largest score of
- *   block j (positions 8j..8j+7 below L) for j < ceil(L/8) (larger score =
- *   later in the order where -0 < +0).
+ *   written; a position below L whose slot is absent scores -inf); if
+ *   block_max != NULL, block_max[r][j] = the largest score of block j
+ *   (positions 8j..8j+7 below L, -0 below +0) for j < ceil(L/8), -inf when
+ *   the block has no present position.
  * cand_blocks != NULL (Reindex): cand_blocks[r][0..n_cand) are block ids
  *   (-1 = none); scores[r][8i + t] is the score of position 8*cand[i] + t, or
  *   -inf when the block is -1 or that position is >= L.  block_max must be NULL.
@@ -128,10 +130,12 @@ csa2_status csa2_index_score(const uint16_t* q_idx /* [R][4][64] */, const float
  * n = n_valid[row_seq ? row_seq[r] : r] (n_valid NULL: n = n_max), entries equal
  * to -inf being absent, keep the first min(k, present) in the order (score
  * descending, index ascending; -0 below +0) and write their indices in
- * ascending order to idx[r][0..k), padding with -1.  If cand_blocks is given,
- * index i is written as the position 8*cand_blocks[r][i/8] + i%8 instead.
+ * ascending order to idx[r][0..k), padding with -1.  If cand_blocks is given
+ * ([R][n_max/8], n_max a multiple of 8 and at most 8*CSA2_KEEP_BLOCKS), index
+ * i is written as the position 8*cand_blocks[r][i/8] + i%8 instead.
  * The result is exact.  Row stride of scores is `row_stride` elements.
- * Requires 1 <= k <= CSA2_MAX_K, n_max >= 0, workspace of at least
+ * Requires 1 <= k <= CSA2_MAX_K, 0 <= n_max <= 1048576 (larger:
+ * CSA2_ERR_UNSUPPORTED), workspace of at least
  * csa2_topk_workspace_bytes(R, n_max, k) bytes (prepared by
  * csa2_workspace_init).
  */
@@ -147,8 +151,8 @@ size_t csa2_topk_workspace_bytes(int32_t R, int32_t n_max, int32_t k);
  * score descending, block id ascending) and write their block ids ascending
  * to cand_blocks[r][0..keep), padding with -1.  Row stride of block_max is
  * ceil(n_max/8).  With keep >= 512 the candidate positions contain the Full
- * layer's Top-512.  Requires 1 <= keep <= CSA2_MAX_K and workspace as for
- * csa2_topk(R, ceil(n_max/8), keep).
+ * layer's Top-512.  Requires 1 <= keep <= CSA2_MAX_K, n_max <= 1048576, and
+ * workspace as for csa2_topk(R, ceil(n_max/8), keep).
  */
 csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq,
                                  const int32_t* seq_len, int32_t R, int32_t n_max, int32_t keep,
@@ -166,9 +170,10 @@ csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq,
  * and value; window entries use swa_k[b][w] as key and swa_v[b][w] as value
  * ([B][S][512] bf16).  One softmax per head over the union (no de-duplication
  * between the two branches).  A row with no entries gets out = 0, lse = -inf.
- * idx entries < 0 or >= L are skipped.  Requires 1 <= k <= CSA2_TOPK,
- * 0 <= swa_len <= 128, 0 <= swa_start, swa_start + swa_len <= S, queries with
- * |q| < 65504.  Accumulation in float32; output float32.
+ * idx entries < 0 or >= L are skipped, and so are window entries outside
+ * [0, S).  Requires 1 <= k <= CSA2_TOPK, swa_len <= 128 (longer windows are
+ * cut to 128 entries), kv->n_slots < 2^31, queries with |q| < 65504.
+ * Accumulation in float32; output float32.
  * Workspace: csa2_attn_workspace_bytes(R).
  */
 csa2_status csa2_fp4_sparse_attn(const uint16_t* q /* [R][16][512] */, const csa2_cache* kv,
@@ -224,6 +229,23 @@ typedef struct {
   float* out;              /* [R][16][512]                                         */
   float* lse;              /* [R][16] or NULL                                      */
 } csa2_layer_args;
+
+/*
+ * A group of layers that share one Top-K: layers[0] runs in first_mode
+ * (Full, Reindex or Reuse) and layers[1 .. n_layers) run as Reuse layers over
+ * the Top-K it leaves in shared->topk_idx -- the decoder's Full + 3 Reuse or
+ * Reindex + 3 Reuse, the encoder's Full + 5 Reuse (conexaotc.com.br page,
+ * paragraph on CSA2; 7minutos.es page, section "Atención escasa comprimida 2
+ * (CSA2)").  Results equal n_layers csa2_layer_step calls; the attention of
+ * every layer of the group runs in one launch.  All layers must have the same
+ * R and row_seq.  Requires 1 <= n_layers <= CSA2_MAX_GROUP_LAYERS,
+ * R * n_layers <= CSA2_MAX_ROWS, shared->n_max <= 1048576, workspace of
+ * csa2_group_workspace_bytes(first_mode, n_layers, R, n_max, hier) bytes.
+ */
+csa2_status csa2_group_step(csa2_mode first_mode, int32_t n_layers, const csa2_layer_args* layers,
+                            const csa2_shared* shared, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t csa2_group_workspace_bytes(csa2_mode first_mode, int32_t n_layers, int32_t R, int32_t n_max,
+                                  int32_t hier);
 
 /*
  * One CSA2 layer:

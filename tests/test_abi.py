@@ -42,7 +42,7 @@ def test_workspace_sizes_are_monotone(C):
     a = C.csa2_workspace_bytes(C.FULL, 8, 131072, False)
     b = C.csa2_workspace_bytes(C.FULL, 8, 131072, True)
     c = C.csa2_workspace_bytes(C.REUSE, 8, 131072, False)
-    assert 0 < c < a < b
+    assert 0 < c < a <= b
     assert C.csa2_workspace_bytes(C.FULL, 16, 131072, False) > a
     assert C.csa2_topk_workspace_bytes(8, 131072, 512) > C.csa2_topk_workspace_bytes(8, 4096, 512)
     assert C.csa2_attn_workspace_bytes(16) > C.csa2_attn_workspace_bytes(8)
@@ -110,6 +110,30 @@ def test_host_validation_errors(C):
     assert C._layer(C.REUSE, ctypes.byref(a), ctypes.byref(s), fake, 100, None) == 4
     # Full needs an indexer query
     assert C._layer(C.FULL, ctypes.byref(a), ctypes.byref(s), fake, 1 << 40, None) == 1
+    # group step: layer count out of range, rows differing between layers,
+    # rows x layers above the limit, context above the Top-k limit
+    arr = C.make_layer_array([a, a])
+    assert C._group(C.REUSE, 0, ctypes.cast(arr, ctypes.c_void_p), ctypes.byref(s), fake, 1 << 40, None) == 2
+    assert C._group(C.REUSE, C.MAX_GROUP_LAYERS + 1, ctypes.cast(arr, ctypes.c_void_p), ctypes.byref(s), fake,
+                    1 << 40, None) == 2
+    b2 = C.csa2_layer_args()
+    ctypes.pointer(b2)[0] = a
+    b2.R = 2
+    arr2 = C.make_layer_array([a, b2])
+    assert C._group(C.REUSE, 2, ctypes.cast(arr2, ctypes.c_void_p), ctypes.byref(s), fake, 1 << 40, None) == 2
+    big = C.csa2_layer_args()
+    ctypes.pointer(big)[0] = a
+    big.R = C.MAX_ROWS // 2 + 1
+    arr3 = C.make_layer_array([big, big])
+    assert C._group(C.REUSE, 2, ctypes.cast(arr3, ctypes.c_void_p), ctypes.byref(s), fake, 1 << 40, None) == 2
+    s.n_max = (1 << 20) + 1
+    assert C._group(C.REUSE, 2, ctypes.cast(arr, ctypes.c_void_p), ctypes.byref(s), fake, 1 << 40, None) == 3
+    s.n_max = 16
+    assert C._topk(fake, (1 << 20) + 1, None, None, 1, (1 << 20) + 1, 8, None, fake, fake, 1 << 40, None) == 3
+    # the group workspace grows with the layer count
+    assert C.csa2_group_workspace_bytes(C.FULL, 4, 8, 131072, False) > \
+        C.csa2_group_workspace_bytes(C.FULL, 1, 8, 131072, False)
+    assert C.csa2_group_workspace_bytes(C.FULL, 9, 8, 131072, False) == 0
     # quantiser: negative count; workspace init with a tiny buffer
     assert C._quant(fake, -1, None, fake, fake, 16, None) == 2
     assert C._quant(fake, 32, None, fake, fake, 16, None) == 2

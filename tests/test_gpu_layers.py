@@ -1,7 +1,10 @@
-"""End-to-end parity of CSA2 layer groups (csa2_layer_step) against the oracle,
-on the five workloads at reduced sizes (same structure: schedules, planted
-keys, hierarchical candidates, paging, prefill rows).  Indices and candidate
-blocks bit-exact after every layer; outputs within 2e-3."""
+"""End-to-end parity of CSA2 layer groups against the oracle, on the five
+workloads at reduced sizes (same structure: schedules, planted keys,
+hierarchical candidates, paging, prefill rows), through both entry points:
+csa2_layer_step (one layer per call) and csa2_group_step (a Full/Reindex
+layer and its Reuse layers per call, attention of the whole group in one
+launch).  Indices and candidate blocks bit-exact after every group; outputs
+within 2e-3."""
 import numpy as np
 import pytest
 import torch
@@ -32,7 +35,7 @@ def numpy_caches(w):
     return P, S, K, pt, n_slots
 
 
-def run_and_compare(w, check_rows=None):
+def run_and_compare(w, by_group: bool, check_rows=None):
     from fp4_kv_cache_02_amd import group
     P, S, K, pt, n_slots = numpy_caches(w)
     inp = group.build_inputs(w, kv_fp4=P, kv_scale=S)
@@ -41,35 +44,55 @@ def run_and_compare(w, check_rows=None):
     row_seq = np.zeros(w.R, np.int64) if w.prefill_rows else np.arange(w.R)
     state = O.GroupState(w.R)
     rows = list(range(w.R)) if check_rows is None else check_rows
-    for li, m in enumerate(w.schedule):
-        say(w.name, "layer", li, m)
-        run.step_layer(li)
+    units = run.groups if by_group else [(li, 1) for li in range(len(w.schedule))]
+    for ui, (li0, n) in enumerate(units):
+        say(w.name, "group" if by_group else "layer", li0, n, w.schedule[li0:li0 + n])
+        if by_group:
+            run.step_group(ui)
+        else:
+            run.step_layer(li0)
         torch.cuda.synchronize()
-        k, v, _, st, ln = synth.gen_swa(w, li)
-        qi = synth.gen_q_idx(w, li) if m in "FI" else None
-        q = synth.gen_q(w, li)
-        blocks_only = m == "F" and w.hier and w.full_blocks_only
-        res = O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln, group.SM_SCALE,
-                           hier=w.hier, blocks_only=blocks_only, rows=rows)
-        if m == "F" and w.hier:
-            gc = host(run.cand)
+        for li in range(li0, li0 + n):
+            m = w.schedule[li]
+            k, v, _, st, ln = synth.gen_swa(w, li)
+            qi = synth.gen_q_idx(w, li) if m in "FI" else None
+            q = synth.gen_q(w, li)
+            blocks_only = m == "F" and w.hier and w.full_blocks_only
+            res = O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln, group.SM_SCALE,
+                               hier=w.hier, blocks_only=blocks_only, rows=rows)
+            if m == "F" and w.hier:
+                gc = host(run.cand)
+                for r in rows:
+                    assert np.array_equal(gc[r], state.cand[r]), (w.name, li, r)
+            if blocks_only:
+                continue
+            gt = host(run.topk_idx)
+            go, gl = host(run.out[li]), host(run.lse[li])
             for r in rows:
-                assert np.array_equal(gc[r], state.cand[r]), (w.name, li, r)
-        if blocks_only:
-            continue
-        gt = host(run.topk_idx)
-        go, gl = host(run.out[li]), host(run.lse[li])
-        for r in rows:
-            assert np.array_equal(gt[r], state.topk[r]), (w.name, li, r)
-            e = rel_err(go[r], res[r][0])
-            assert np.all(e <= ATTN_TOL), (w.name, li, r, e.max())
-            assert lse_ok(gl[r], res[r][1]), (w.name, li, r)
+                assert np.array_equal(gt[r], state.topk[r]), (w.name, li, r)
+                e = rel_err(go[r], res[r][0])
+                assert np.all(e <= ATTN_TOL), (w.name, li, r, e.max())
+                assert lse_ok(gl[r], res[r][1]), (w.name, li, r)
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 4])
-def test_group_reduced(cfg):
-    run_and_compare(synth.workload(cfg, reduced=True))
+def test_group_reduced_by_layer(cfg):
+    run_and_compare(synth.workload(cfg, reduced=True), by_group=False)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
+def test_group_reduced_by_group(cfg):
+    run_and_compare(synth.workload(cfg, reduced=True), by_group=True)
 
 
 def test_group_prefill_reduced():
-    run_and_compare(synth.workload(3, reduced=True))
+    run_and_compare(synth.workload(3, reduced=True), by_group=True)
+
+
+def test_group_prefill_rows_mode():
+    """Enough rows x layers (128 x 6) that every (layer, row) is one block
+    writing its output directly (no partials)."""
+    w = synth.workload(3, reduced=True)
+    w = synth.Workload("cfg3_reduced_prefill_F5R_C128_E8192", w.seed, [8192], "FRRRRR", prefill_rows=128,
+                       prefill_pos=16384, raw_fp4=True)
+    run_and_compare(w, by_group=True, check_rows=list(range(0, 128, 9)) + [127])
