@@ -351,6 +351,7 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* head_w, const c
   if (!q_idx || !k_idx || !seq_len || !scores) return CSA2_ERR_NULL;
   if (!cache_ok(k_idx, false)) return CSA2_ERR_NULL;
   if (R < 1 || R > CSA2_MAX_ROWS || n_max < 0) return CSA2_ERR_SHAPE;
+  if (k_idx->n_slots < 1 || k_idx->n_slots > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
   if (cand_blocks) {
     if (n_cand < 1 || n_cand > CSA2_KEEP_BLOCKS) return CSA2_ERR_SHAPE;
     if (block_max) return CSA2_ERR_UNSUPPORTED;
@@ -452,6 +453,7 @@ csa2_status csa2_group_step(csa2_mode first_mode, int32_t n_layers, const csa2_l
   if (first_mode != CSA2_REUSE) {
     if (!layers[0].q_idx) return CSA2_ERR_NULL;
     if (!cache_ok(&sh->k_idx, false)) return CSA2_ERR_NULL;
+    if (sh->k_idx.n_slots < 1 || sh->k_idx.n_slots > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
     if (sh->hier && !sh->cand_blocks) return CSA2_ERR_NULL;
   }
   if (!ws) return CSA2_ERR_WORKSPACE;

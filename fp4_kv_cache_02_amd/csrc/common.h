@@ -67,6 +67,21 @@ CSA2_DEV float e4m3_to_float(uint32_t c) {
 
 CSA2_DEV int lane_id() { return __lane_id(); }
 
+// Maximum over the wave through DPP lane shifts (rows of 16 lanes, then row
+// broadcasts); shifted-in lanes contribute 0.  Result valid in every lane.
+CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
+#define CSA2_DPPMAX(ctrl, rmask) \
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, (ctrl), (rmask), 0xF, false))
+  CSA2_DPPMAX(0x111, 0xF);   // row_shr:1
+  CSA2_DPPMAX(0x112, 0xF);   // row_shr:2
+  CSA2_DPPMAX(0x114, 0xF);   // row_shr:4
+  CSA2_DPPMAX(0x118, 0xF);   // row_shr:8
+  CSA2_DPPMAX(0x142, 0xA);   // row_bcast:15
+  CSA2_DPPMAX(0x143, 0xC);   // row_bcast:31
+#undef CSA2_DPPMAX
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Phase timestamps for kernel tuning: only a build with -DCSA2_TRACE records
 // them (thread 0 of the block with all block indices 0 writes the 100 MHz
 // wall clock into slot i of the trace buffer set by csa2_trace_set).

@@ -15,17 +15,21 @@
 // of the eight positions of group g; register i of the lane holds position
 // (step base) + 8g + i.  One load instruction therefore reads eight whole
 // 128-byte key rows, and the eight instructions of a step read 8 KiB.
-// Each lane forms its chunk's partial c_j for the four heads with eight FMAs;
-// the tree over the eight chunks is a three-level DPP butterfly inside each
-// group of eight lanes (xor 1, xor 2, then the other half of the group), which
-// reproduces ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)) exactly (IEEE addition is
-// commutative).  Loads of the next step are issued register by register as the
-// current step consumes them, so each wave keeps 8 KiB in flight.
+// Each lane forms its chunk's partial c_j of every position for the four heads
+// with eight FMAs each; the tree over the eight chunks is a three-level
+// reduce-scatter inside the group of eight lanes: at each level a lane keeps
+// half of its positions, adds the partner's partials of those positions (DPP
+// lane exchange: partner j^1, then j^2, then 7-j) and hands over the other
+// half, so the pairs combined are exactly ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7))
+// (IEEE addition is commutative) and every lane ends with one position whose
+// score it finishes alone.  Loads of the next step are issued register by
+// register as the current step consumes them (unconditional loads: an absent
+// position reads slot 0), so each wave keeps 8 KiB in flight.
 //
-// Epilogue: lane 8g + j writes the score of position base + 8g + j (256
-// contiguous bytes per wave).  In scan mode the wave also emits the maxima the
-// Top-K selection descends through: the maximum of each block of 8 positions
-// (the hierarchical indexer's block score) and of the 64-position step.
+// Epilogue: each lane writes its position's score (32 contiguous bytes per
+// group).  In scan mode the wave also emits the maxima the Top-K selection
+// descends through: the maximum of each block of 8 positions (the
+// hierarchical indexer's block score) and of the 64-position step.
 #include "kernels.h"
 
 namespace csa2 {
@@ -35,22 +39,23 @@ constexpr int kScanWaves = 4;            // waves per block
 #define CSA2_DPP(v, ctrl) \
   __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
 
-// per-lane geometry of one step
+// Geometry of one step: the row is wave-uniform (scalar registers), the
+// position group and its slot are per lane.
 struct StepGeo {
   int r;          // query row
   int b;          // sequence
-  int64_t pos0;   // first position of this lane's group (scan: 64t + 8g)
-  int64_t s0;     // slot of pos0 (-1: the group is absent)
-  int nv;         // positions i < nv of the group are present
   int L;          // visible positions of the row
   int t;          // step index within the row
+  int64_t pos0;   // first position of this lane's group (scan: 64t + 8g)
+  int64_t s0;     // slot of pos0 (0 when the group is absent: a safe address)
+  int nv;         // positions i < nv of the group are present
 };
 
 template <bool CAND>
 CSA2_DEV StepGeo step_geo(const IdxArgs& a, uint32_t item, int g) {
   StepGeo s;
-  s.r = (int)(item / (uint32_t)a.steps_per_row);
-  s.t = (int)(item - (uint32_t)s.r * (uint32_t)a.steps_per_row);
+  s.r = __builtin_amdgcn_readfirstlane((int)(item / (uint32_t)a.steps_per_row));
+  s.t = __builtin_amdgcn_readfirstlane((int)(item - (uint32_t)s.r * (uint32_t)a.steps_per_row));
   s.b = a.row_seq ? a.row_seq[s.r] : s.r;
   s.L = min(a.seq_len[s.b], a.n_max);
   int64_t pos0;
@@ -71,26 +76,37 @@ CSA2_DEV StepGeo step_geo(const IdxArgs& a, uint32_t item, int g) {
       nv = (int)min(lim, (int64_t)8);
     }
   }
-  s.s0 = s0;
+  s.s0 = nv > 0 ? s0 : 0;
   s.nv = nv;
   return s;
+}
+
+// The 16-byte chunk j of the key of position i of the group (slot 0 stands
+// in for absent positions: every load is unconditional and in bounds).
+CSA2_DEV uint4 key_chunk(const uint4* __restrict__ kd, const StepGeo& s, int i, int j) {
+  const int64_t slot = (i < s.nv) ? s.s0 + i : 0;
+  return kd[slot * 8 + j];
 }
 
 template <bool CAND, bool HAS_W, bool MAXIMA>
 __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 3, j = lane & 7;
+  // reduce-scatter roles: lanes j and 7-j play the same part in the two
+  // quads; lane j finishes position pj of its group
+  const int vj = (j < 4) ? j : 7 - j;
+  const int pj = (j < 4) ? j : 11 - j;
+  const bool b0 = vj & 1, b1 = (vj >> 1) & 1, upper = j >= 4;
   const uint32_t W = gridDim.x * kScanWaves;
   const uint32_t n_items = (uint32_t)a.R * (uint32_t)a.steps_per_row;
-  uint32_t item = blockIdx.x * kScanWaves + (threadIdx.x >> 6);
+  uint32_t item = __builtin_amdgcn_readfirstlane(blockIdx.x * kScanWaves + (threadIdx.x >> 6));
   if (item >= n_items) return;
 
   const uint4* __restrict__ kd = a.kdata;
   uint4 regs[8];
   StepGeo cur = step_geo<CAND>(a, item, g);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    regs[i] = (i < cur.nv) ? kd[(cur.s0 + i) * 8 + j] : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 8; ++i) regs[i] = key_chunk(kd, cur, i, j);
 
   int qrow = -1;
   float qf[4][8];
@@ -115,66 +131,81 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
     }
     const uint32_t next = item + W;
     const bool has_next = next < n_items;
-    StepGeo nxt;
+    StepGeo nxt = cur;
     if (has_next) nxt = step_geo<CAND>(a, next, g);
 
-    float mine = 0.f;          // score of position pos0 + j (this lane's output)
-    uint32_t kmax = 0u;        // order key of the group's best present score
+    // chunk partials c_j of the eight positions, four heads
+    float P[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint4 kw = regs[i];
-      if (has_next) regs[i] = (i < nxt.nv) ? kd[(nxt.s0 + i) * 8 + j] : make_uint4(0, 0, 0, 0);
+      if (has_next) regs[i] = key_chunk(kd, nxt, i, j);
       const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
                            bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
-      float d[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         float acc = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(kf[e], qf[h][e], acc);
-        d[h] = acc;
-      }
-#pragma unroll
-      for (int h = 0; h < 4; ++h) d[h] = d[h] + CSA2_DPP(d[h], 0xB1);    // c_j + c_{j^1}
-#pragma unroll
-      for (int h = 0; h < 4; ++h) d[h] = d[h] + CSA2_DPP(d[h], 0x4E);    // + the other pair
-#pragma unroll
-      for (int h = 0; h < 4; ++h) d[h] = d[h] + CSA2_DPP(d[h], 0x141);   // + the other quad
-      float rr[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) rr[h] = (d[h] > 0.0f) ? d[h] : 0.0f;
-      float s;
-      if (HAS_W) {
-        const float p0 = w[0] * rr[0], p1 = w[1] * rr[1], p2 = w[2] * rr[2], p3 = w[3] * rr[3];
-        s = (p0 + p1) + (p2 + p3);
-      } else {
-        s = (rr[0] + rr[1]) + (rr[2] + rr[3]);
-      }
-      mine = (j == i) ? s : mine;
-      if (MAXIMA) {
-        const uint32_t k = (i < cur.nv) ? order_key(s) : 0u;
-        kmax = max(kmax, k);
+        P[i][h] = acc;
       }
     }
+    // reduce-scatter over the 8 lanes of the group
+    float Q[4][4], Rr[2][4], d[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float keep = b0 ? P[2 * r + 1][h] : P[2 * r][h];
+        const float send = b0 ? P[2 * r][h] : P[2 * r + 1][h];
+        Q[r][h] = keep + CSA2_DPP(send, 0xB1);          // partner j ^ 1
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float keep = b1 ? Q[2 * s2 + 1][h] : Q[2 * s2][h];
+        const float send = b1 ? Q[2 * s2][h] : Q[2 * s2 + 1][h];
+        Rr[s2][h] = keep + CSA2_DPP(send, 0x4E);        // partner j ^ 2
+      }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float keep = upper ? Rr[1][h] : Rr[0][h];
+      const float send = upper ? Rr[0][h] : Rr[1][h];
+      d[h] = keep + CSA2_DPP(send, 0x141);              // partner 7 - j
+    }
+    float rr[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) rr[h] = (d[h] > 0.0f) ? d[h] : 0.0f;
+    float sc;
+    if (HAS_W) {
+      const float p0 = w[0] * rr[0], p1 = w[1] * rr[1], p2 = w[2] * rr[2], p3 = w[3] * rr[3];
+      sc = (p0 + p1) + (p2 + p3);
+    } else {
+      sc = (rr[0] + rr[1]) + (rr[2] + rr[3]);
+    }
+    const bool present = pj < cur.nv;
 
     // ---- outputs of the step ----
     if (CAND) {
-      const int64_t ci8 = (int64_t)cur.t * 64 + lane;     // 8 * candidate index + j
+      const int64_t ci8 = (int64_t)cur.t * 64 + g * 8 + pj;     // 8 * candidate index + pj
       if (ci8 < (int64_t)a.n_cand * 8)
-        a.scores[(int64_t)cur.r * a.score_stride + ci8] = (j < cur.nv) ? mine : -__builtin_inff();
+        a.scores[(int64_t)cur.r * a.score_stride + ci8] = present ? sc : -__builtin_inff();
     } else {
-      const int64_t p = cur.pos0 + j;
-      if (p < cur.L) a.scores[(int64_t)cur.r * a.score_stride + p] = (j < cur.nv) ? mine : -__builtin_inff();
+      const int64_t p = cur.pos0 + pj;
+      if (p < cur.L) a.scores[(int64_t)cur.r * a.score_stride + p] = present ? sc : -__builtin_inff();
       if (MAXIMA) {
+        uint32_t k = present ? order_key(sc) : 0u;
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x141, 0xF, 0xF, false));
         if (j == 0 && cur.pos0 < cur.L)
-          a.block_max[(int64_t)cur.r * a.bmax_stride + (cur.pos0 >> 3)] =
-              kmax ? key_to_float(kmax) : -__builtin_inff();
-        uint32_t k2 = kmax;
-        k2 = max(k2, (uint32_t)__shfl_xor((int)k2, 8, 64));
-        k2 = max(k2, (uint32_t)__shfl_xor((int)k2, 16, 64));
-        k2 = max(k2, (uint32_t)__shfl_xor((int)k2, 32, 64));
-        if (lane == 0 && a.max64 && (int64_t)cur.t * 64 < cur.L)
-          a.max64[(int64_t)cur.r * a.max64_stride + cur.t] = k2 ? key_to_float(k2) : -__builtin_inff();
+          a.block_max[(int64_t)cur.r * a.bmax_stride + (cur.pos0 >> 3)] = k ? key_to_float(k) : -__builtin_inff();
+        if (a.max64) {
+          const uint32_t k2 = wave_max_u32(k);
+          if (lane == 0 && (int64_t)cur.t * 64 < cur.L)
+            a.max64[(int64_t)cur.r * a.max64_stride + cur.t] = k2 ? key_to_float(k2) : -__builtin_inff();
+        }
       }
     }
     if (!has_next) break;

@@ -104,16 +104,7 @@ CSA2_DEV uint32_t wave_incl_scan_u32(uint32_t v) {
   v += CSA2_DPP_U(v, 0x143, 0xC);   // row_bcast:31 into rows 2, 3
   return v;
 }
-// max / min / sum over the wave, valid in every lane
-CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, CSA2_DPP_U(v, 0x111, 0xF));
-  v = max(v, CSA2_DPP_U(v, 0x112, 0xF));
-  v = max(v, CSA2_DPP_U(v, 0x114, 0xF));
-  v = max(v, CSA2_DPP_U(v, 0x118, 0xF));
-  v = max(v, CSA2_DPP_U(v, 0x142, 0xA));
-  v = max(v, CSA2_DPP_U(v, 0x143, 0xC));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
+// min / sum over the wave, valid in every lane (max: common.h)
 CSA2_DEV uint32_t wave_min_u32(uint32_t v) {
   // shifted-in zeros must not win: complement, take the max, complement back
   return ~wave_max_u32(~v);
