@@ -80,6 +80,8 @@ csa2_status do_index_score(const uint16_t* q_idx, const float* head_w, const csa
   a.scores = scores;
   a.block_max = bmax;
   a.max64 = max64;
+  a.row_list = nullptr;
+  a.row_list_count = nullptr;
   CSA2_SET_TRACE(a, 0);
   return hip_status(launch_index_score(a, cand != nullptr, head_w != nullptr, bmax != nullptr, st));
 }
@@ -131,6 +133,8 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
   a.cand_stride = 0;
   a.out = out;
   a.out_stride = k;
+  a.row_list = nullptr;
+  a.row_list_count = nullptr;
   return a;
 }
 
@@ -236,6 +240,35 @@ AttnLayerIn layer_in(const csa2_layer_args* a) {
 
 // ------------------------------------------------------- layer index part --
 
+// Rows of a prefill chunk (all rows score one sequence) that are many enough
+// for the matrix-core indexer; the caller also requires a single sequence.
+bool prefill_shape(csa2_mode mode, int R, int n_max, int hier) {
+  return (mode == CSA2_FULL || mode == CSA2_REINDEX) && !hier && R >= kPrefMinRows && n_max >= kPrefMinN &&
+         n_max <= kPrefMaxN;
+}
+
+struct PrefWs {
+  float* gmax;
+  float* kmax_part;
+  float* theta;
+  uint32_t* cand_count;
+  int32_t* cand;
+  int32_t* fb_list;
+  uint32_t* fb_count;
+};
+
+PrefWs carve_prefill(Bump& bp, int R, int n_max) {
+  PrefWs p;
+  p.gmax = bp.take<float>((size_t)R * cdiv(n_max, 64));
+  p.kmax_part = bp.take<float>((size_t)cdiv(n_max, 2048));
+  p.theta = bp.take<float>((size_t)R);
+  p.cand_count = bp.take<uint32_t>((size_t)R);
+  p.cand = bp.take<int32_t>((size_t)R * kPrefCap);
+  p.fb_list = bp.take<int32_t>((size_t)R);
+  p.fb_count = bp.take<uint32_t>(1);
+  return p;
+}
+
 // Workspace of the indexer part of a layer in `mode` (scores, maxima, Top-k levels).
 size_t index_region(csa2_mode mode, int R, int n_max, int hier) {
   Bump bp{nullptr, 0};
@@ -243,6 +276,7 @@ size_t index_region(csa2_mode mode, int R, int n_max, int hier) {
     bp.take<float>((size_t)R * n_max);
     bp.take<float>((size_t)R * cdiv(n_max, 8));
     bp.take<float>((size_t)R * cdiv(n_max, 64));
+    if (prefill_shape(mode, R, n_max, hier)) carve_prefill(bp, R, n_max);
   } else if (mode == CSA2_REINDEX) {
     bp.take<float>((size_t)R * CSA2_KEEP_BLOCKS * 8);
   }
@@ -260,6 +294,62 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
     float* scores = bp.take<float>((size_t)R * n_max);
     float* bmax = bp.take<float>((size_t)R * cdiv(n_max, 8));
     float* m64 = bp.take<float>((size_t)R * cdiv(n_max, 64));
+    // (one sequence: every row's row_seq entry is 0)
+    if (sh->B == 1 && a->row_seq && !blocks_only && prefill_shape(mode, R, n_max, sh->hier)) {
+      // prefill chunk: matrix-core indexer with exact selection; the rows it
+      // lists (too many candidates) take the exact scan and Top-k below
+      const PrefWs pw = carve_prefill(bp, R, n_max);
+      PrefArgs p;
+      p.q32 = (const uint32_t*)a->q_idx;
+      p.head_w = a->head_w;
+      p.kdata = (const uint4*)sh->k_idx.data;
+      p.map = make_slot_map(sh->k_idx);
+      p.seq_len = sh->seq_len;
+      p.R = R;
+      p.n_max = n_max;
+      p.k = CSA2_TOPK;
+      p.gmax = pw.gmax;
+      p.gmax_stride = cdiv(n_max, 64);
+      p.kmax_part = pw.kmax_part;
+      p.theta = pw.theta;
+      p.cand_count = pw.cand_count;
+      p.cand = pw.cand;
+      p.cap = kPrefCap;
+      p.fb_list = pw.fb_list;
+      p.fb_count = pw.fb_count;
+      p.out = sh->topk_idx;
+      hipError_t e = launch_prefill_index(p, a->head_w != nullptr, st);
+      if (e != hipSuccess) return CSA2_ERR_HIP;
+      IdxArgs ia;
+      ia.q32 = p.q32;
+      ia.head_w = a->head_w;
+      ia.kdata = p.kdata;
+      ia.map = p.map;
+      ia.row_seq = a->row_seq;
+      ia.seq_len = sh->seq_len;
+      ia.cand = nullptr;
+      ia.n_cand = 0;
+      ia.R = R;
+      ia.n_max = n_max;
+      ia.steps_per_row = (int32_t)cdiv(n_max, 64);
+      ia.score_stride = n_max;
+      ia.bmax_stride = cdiv(n_max, 8);
+      ia.max64_stride = cdiv(n_max, 64);
+      ia.scores = scores;
+      ia.block_max = bmax;
+      ia.max64 = m64;
+      ia.row_list = pw.fb_list;
+      ia.row_list_count = pw.fb_count;
+      CSA2_SET_TRACE(ia, 0);
+      e = launch_index_score(ia, false, a->head_w != nullptr, true, st);
+      if (e != hipSuccess) return CSA2_ERR_HIP;
+      TopkArgs t = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
+      t.lv[1] = bmax;
+      t.lv[2] = m64;
+      t.row_list = pw.fb_list;
+      t.row_list_count = pw.fb_count;
+      return run_topk(t, TopkWs{nullptr, nullptr}, st);
+    }
     s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max, scores,
                        bmax, m64, st);
     if (s) return s;

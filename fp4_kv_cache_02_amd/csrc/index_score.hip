@@ -56,6 +56,7 @@ CSA2_DEV StepGeo step_geo(const IdxArgs& a, uint32_t item, int g) {
   StepGeo s;
   s.r = __builtin_amdgcn_readfirstlane((int)(item / (uint32_t)a.steps_per_row));
   s.t = __builtin_amdgcn_readfirstlane((int)(item - (uint32_t)s.r * (uint32_t)a.steps_per_row));
+  if (a.row_list) s.r = __builtin_amdgcn_readfirstlane(a.row_list[s.r]);
   s.b = a.row_seq ? a.row_seq[s.r] : s.r;
   s.L = min(a.seq_len[s.b], a.n_max);
   int64_t pos0;
@@ -98,7 +99,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
   const int pj = (j < 4) ? j : 11 - j;
   const bool b0 = vj & 1, b1 = (vj >> 1) & 1, upper = j >= 4;
   const uint32_t W = gridDim.x * kScanWaves;
-  const uint32_t n_items = (uint32_t)a.R * (uint32_t)a.steps_per_row;
+  const uint32_t n_rows = a.row_list ? min(*a.row_list_count, (uint32_t)a.R) : (uint32_t)a.R;
+  const uint32_t n_items = n_rows * (uint32_t)a.steps_per_row;
   uint32_t item = __builtin_amdgcn_readfirstlane(blockIdx.x * kScanWaves + (threadIdx.x >> 6));
   if (item >= n_items) return;
 

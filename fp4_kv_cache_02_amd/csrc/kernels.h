@@ -23,6 +23,8 @@ struct IdxArgs {
   float* scores;
   float* block_max;           // [R][ceil(n_max/8)] maxima of 8 positions (scan, optional)
   float* max64;               // [R][ceil(n_max/64)] maxima of 64 positions (scan, optional)
+  const int32_t* row_list;    // optional: score only rows row_list[0 .. *row_list_count)
+  const uint32_t* row_list_count;
   CSA2_TRACE_ARG
 };
 
@@ -40,7 +42,32 @@ struct TopkArgs {
   int32_t cand_stride;
   int32_t* out;
   int32_t out_stride;
+  const int32_t* row_list;    // optional: select only rows row_list[0 .. *row_list_count)
+  const uint32_t* row_list_count;
   CSA2_TRACE_ARG
+};
+
+// Prefill-chunk indexer on MFMA: every query row sees the positions of one
+// sequence (sequence 0).
+struct PrefArgs {
+  const uint32_t* q32;        // [R][4][32] bf16 pairs
+  const float* head_w;        // [R][4] or null
+  const uint4* kdata;         // indexer keys
+  SlotMap map;
+  const int32_t* seq_len;     // seq_len[0]: visible positions
+  int32_t R;
+  int32_t n_max;
+  int32_t k;
+  float* gmax;                // [R][ceil(n_max/64)] maxima of the approximate scores per 64 positions
+  int64_t gmax_stride;
+  float* kmax_part;           // [ceil(n_max/2048)] largest |key element| per chunk of 2048 positions
+  float* theta;               // [R] candidate threshold
+  uint32_t* cand_count;       // [R]
+  int32_t* cand;              // [R][cap] candidate positions
+  int32_t cap;
+  int32_t* fb_list;           // [R] rows whose candidates overflowed
+  uint32_t* fb_count;         // [1]
+  int32_t* out;               // [R][k] Top-k positions
 };
 
 struct MaximaArgs {
@@ -97,6 +124,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,
                         int64_t n_slots, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+hipError_t launch_prefill_index(const PrefArgs& a, bool has_w, hipStream_t st);
+constexpr int kPrefMinRows = 256;        // rows from which the MFMA prefill indexer is used
+constexpr int kPrefMinN = 128 * CSA2_TOPK;  // positions from which it is used (>= 2k groups of 64)
+constexpr int kPrefMaxN = 262144;        // positions it supports
+constexpr int kPrefCap = 4096;           // candidate positions kept per row
 int attn_steps(int k);
 int attn_blocks(int k, int rows_x_layers, int* steps_per_block);
 

@@ -1,0 +1,485 @@
+// Indexer of a prefill chunk on the matrix cores, with the exact Top-k.
+//
+// In a prefill chunk every query row of the layer scores the same context
+// positions (the encoder prefill of a CSA2 layer group: 7minutos.es page,
+// section "Atención escasa comprimida 2 (CSA2)"), so the indexer is a dense
+// product [rows x 4 heads x 64] . [64 x positions] followed by ReLU and the
+// head sum.  The selection must equal the one made on the canonical score
+// (eight fused-multiply-add chains per head, see index_score.hip), which the
+// matrix cores do not reproduce bit for bit.  The matrix-core score s~ is
+// therefore only used to find, for each row, a small superset of the Top-k,
+// with a proven error band, and the superset is then rescored exactly:
+//
+//   1. pass 0 (MFMA): s~ for every (row, position); per row and group of 64
+//      positions the maximum of s~ (gmax); the largest |key| element (kmax).
+//   2. threshold: tau = (a lower bound of) the k-th largest gmax of the row.
+//      At least k groups hold a position with s~ >= tau, so at least k
+//      positions have a canonical score >= tau - D, where D bounds |s~ - s|;
+//      hence every position of the exact Top-k has s >= tau - D and
+//      s~ >= theta = tau - 2D.
+//   3. pass 1 (MFMA): the positions with s~ >= theta are the candidates
+//      (groups whose gmax is below theta are skipped: the same arithmetic
+//      produced gmax).
+//   4. select: the candidates are put in position order, rescored with the
+//      canonical arithmetic and the exact Top-k (ties to the lower position)
+//      is written in ascending position order.
+//   A row with more than kPrefCap candidates (near-constant scores) is listed
+//   and scored by the exact scan + Top-k kernels instead.
+//
+// The band D.  For head h let M_h = sum_c |q_hc k_c| <= |q_h|_1 * kmax.
+// The canonical dot product makes at most 11 roundings in float32
+// (u = 2^-24): |d_h - e_h| <= 11u M_h (1 + O(u)), e_h the exact value.  The
+// matrix core multiplies bf16 values exactly and adds 64 products in float32;
+// the order and the rounding of its additions are not specified, so its error
+// is taken as at most 73 u' M_h with u' = 2^-20 (four bits fewer than float32
+// rounding to nearest).  ReLU does not increase a difference, and the head
+// sums of s and s~ each round three times.  With w = head weights:
+//   |s~ - s| <= sum_h |w_h| M_h (11u + 73u' + 6u)(1 + 2^-10) =: D,
+// and a subnormal product the hardware might flush adds at most 2^-120.
+#include "select.h"
+#include "kernels.h"
+
+namespace csa2 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+CSA2_DEV bf16x8_t to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+constexpr int kPWaves = 4;                  // waves per workgroup of the MFMA passes
+constexpr int kPRows = 16 * kPWaves;        // query rows per workgroup (16 per wave)
+constexpr int kPChunk = 2048;               // positions per workgroup
+constexpr int kPStage = 128;                // positions per LDS stage
+constexpr int kPGroup = 64;                 // positions per gmax group
+constexpr int kPGroupsWG = kPChunk / kPGroup;
+constexpr int kPLdsCand = 32;               // candidates per row buffered in LDS (pass 1)
+
+// DPP lane patterns inside a row of 16 lanes
+#define PF_DPP(v, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
+constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;     // lane i <-> 7 - i within 8
+constexpr int kMirror = 0x140;         // lane i <-> 15 - i within 16
+
+// maximum over the 16 lanes of a DPP row, in every lane of the row
+CSA2_DEV float row16_max(float v) {
+  v = fmaxf(v, PF_DPP(v, kQuadSwap1));
+  v = fmaxf(v, PF_DPP(v, kQuadSwap2));
+  v = fmaxf(v, PF_DPP(v, kHalfMirror));
+  v = fmaxf(v, PF_DPP(v, kMirror));
+  return v;
+}
+CSA2_DEV float row16_sum(float v) {
+  v += PF_DPP(v, kQuadSwap1);
+  v += PF_DPP(v, kQuadSwap2);
+  v += PF_DPP(v, kHalfMirror);
+  v += PF_DPP(v, kMirror);
+  return v;
+}
+
+struct PassSmem {
+  uint4 keys[kPStage * 8];            // chunk c of stage position p at p*8 + (c ^ (p & 7))
+  uint32_t present[kPStage + kPWaves * 64];   // [kPStage, ...): sink of the non-writing lanes
+  uint32_t cnt[kPRows];               // pass 1: candidates found per row
+  uint32_t base[kPRows];
+  int32_t buf[kPRows][kPLdsCand];
+  uint32_t kmax[kPWaves];
+  uint64_t act[kPWaves][kPGroupsWG / 4];
+};
+
+// Pass 0 (PASS = 0) and pass 1 (PASS = 1).  Workgroup (x, y): positions
+// [2048x, 2048x + 2048) of rows [64y, 64y + 64); wave w owns rows 64y + 16w
+// .. +15 as four MFMA row tiles of 4 rows x 4 heads.
+//
+// MFMA 16x16x32 bf16 operand layout (lane l, c = l % 16, g = l / 16):
+//   A (query): row m = c of the tile = (row 4mt + c/4, head c%4), elements
+//     k = 8g .. 8g+7 of the 32-wide K slice;
+//   B (keys): column n = c = position, elements k = 8g .. 8g+7;
+//   D: lane holds rows 4g .. 4g+3 of column c = the four heads of row 4mt+g
+//     at position c, so each lane finishes one (row, position) score.
+template <int PASS, bool HAS_W>
+__global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
+  __shared__ PassSmem sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int L = min(a.seq_len[0], a.n_max);
+  const int64_t x0 = (int64_t)blockIdx.x * kPChunk;
+  if (x0 >= L) return;
+  const int n_here = (int)min((int64_t)kPChunk, (int64_t)L - x0);
+  const int n_stage = (n_here + kPStage - 1) / kPStage;
+  const int rw0 = blockIdx.y * kPRows + 16 * wave;     // first row of the wave
+
+  // query fragments (rows past R read row R-1; their results are dropped)
+  bf16x8_t A[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int row = min(rw0 + 4 * mt + (c >> 2), a.R - 1);
+    const uint4* qp = (const uint4*)(a.q32 + ((int64_t)row * 4 + (c & 3)) * 32);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) A[mt][kh] = to_bf16x8(qp[4 * kh + g]);
+  }
+  // this lane's output rows
+  int orow[4];
+  float w[4][4];
+  float th[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    orow[mt] = rw0 + 4 * mt + g;
+    const int rr = min(orow[mt], a.R - 1);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w[mt][h] = HAS_W ? a.head_w[(int64_t)rr * 4 + h] : 1.0f;
+    th[mt] = (PASS == 1 && orow[mt] < a.R) ? a.theta[orow[mt]] : __builtin_inff();
+  }
+  // pass 1: which (4-row tile, group) pairs can hold a candidate.  Lane l
+  // tests row rw0 + (l & 15) at groups (l >> 4) + 4i; ballot i then holds the
+  // 16 row bits of group 4i + q in bits [16q, 16q + 16).
+  if (PASS == 1) {
+    const int row = rw0 + c;
+    const float t = row < a.R ? a.theta[row] : __builtin_inff();
+    const int rr = min(row, a.R - 1);
+#pragma unroll
+    for (int i = 0; i < kPGroupsWG / 4; ++i) {
+      const int64_t grp = x0 / kPGroup + g + 4 * i;
+      const bool ok = grp * kPGroup < L;
+      const float gm = ok ? a.gmax[(int64_t)rr * a.gmax_stride + (ok ? grp : 0)] : -__builtin_inff();
+      const uint64_t bits = __ballot(gm >= t);
+      if (lane == 0) sm.act[wave][i] = bits;
+    }
+    if (tid < kPRows) sm.cnt[tid] = 0u;
+  }
+
+  const bool want_kmax = PASS == 0 && blockIdx.y == 0;
+  uint32_t kmx = 0u;
+
+  // stage loads: thread t loads chunk (t & 7) of stage positions (t >> 3) + 32i
+  const int lq = tid & 7;
+  uint4 pf0, pf1, pf2, pf3;             // prefetched stage (one variable per load:
+  uint32_t pp0, pp1, pp2, pp3;           // an array here was kept in scratch memory)
+#define PF_LOAD1(S, I)                                                          \
+  {                                                                            \
+    const int64_t p = x0 + (int64_t)(S) * kPStage + (tid >> 3) + 32 * (I);     \
+    const int64_t slot = p < L ? a.map(0, p) : -1;                             \
+    pp##I = slot >= 0 ? 1u : 0u;                                               \
+    pf##I = a.kdata[(slot >= 0 ? slot : 0) * 8 + lq];                          \
+  }
+#define PF_LOAD_STAGE(S) PF_LOAD1(S, 0) PF_LOAD1(S, 1) PF_LOAD1(S, 2) PF_LOAD1(S, 3)
+  PF_LOAD_STAGE(0);
+
+  float gm[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) gm[mt] = -__builtin_inff();
+
+  for (int s = 0; s < n_stage; ++s) {
+    __syncthreads();                       // the previous stage is consumed
+    {
+      const uint4 pv[4] = {pf0, pf1, pf2, pf3};
+      const uint32_t pr[4] = {pp0, pp1, pp2, pp3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pl = (tid >> 3) + 32 * i;
+        sm.keys[pl * 8 + (lq ^ (pl & 7))] = pv[i];
+        sm.present[lq == 0 ? pl : kPStage + tid] = pr[i];     // unconditional store
+        if (want_kmax) {
+          const uint32_t wv[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t m = wv[e] & 0x7FFF7FFFu;
+            kmx = max(kmx, max(m & 0xFFFFu, m >> 16));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (s + 1 < n_stage) { PF_LOAD_STAGE(s + 1); }
+
+#pragma unroll 2
+    for (int nt = 0; nt < kPStage / 16; ++nt) {
+      const int pl = 16 * nt + c;
+      const int grp_wg = (s * kPStage + 16 * nt) / kPGroup;     // group within the workgroup
+      uint32_t tiles = 0xFu;
+      if (PASS == 1) {
+        const uint32_t bits = (uint32_t)(sm.act[wave][grp_wg >> 2] >> (16 * (grp_wg & 3))) & 0xFFFFu;
+        tiles = (bits & 0xFu ? 1u : 0u) | (bits & 0xF0u ? 2u : 0u) | (bits & 0xF00u ? 4u : 0u) |
+                (bits & 0xF000u ? 8u : 0u);
+        tiles = __builtin_amdgcn_readfirstlane(tiles);
+        if (!tiles) continue;
+      }
+      const uint4 b0 = sm.keys[pl * 8 + (g ^ (pl & 7))];
+      const uint4 b1 = sm.keys[pl * 8 + ((4 + g) ^ (pl & 7))];
+      const bool pres = sm.present[pl] != 0u;
+      const int64_t pos = x0 + (int64_t)s * kPStage + pl;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (!(tiles & (1u << mt))) continue;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][0], to_bf16x8(b0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][1], to_bf16x8(b1), acc, 0, 0, 0);
+        const float r0 = fmaxf(acc[0], 0.0f), r1 = fmaxf(acc[1], 0.0f);
+        const float r2 = fmaxf(acc[2], 0.0f), r3 = fmaxf(acc[3], 0.0f);
+        float sc;
+        if (HAS_W)
+          sc = (w[mt][0] * r0 + w[mt][1] * r1) + (w[mt][2] * r2 + w[mt][3] * r3);
+        else
+          sc = (r0 + r1) + (r2 + r3);
+        if (PASS == 0) {
+          gm[mt] = fmaxf(gm[mt], pres ? sc : -__builtin_inff());
+        } else {
+          const bool hit = pres && orow[mt] < a.R && sc >= th[mt];
+          if (__ballot(hit)) {
+            if (hit) {
+              const int rl = 16 * wave + 4 * mt + g;
+              const uint32_t slot = atomicAdd(&sm.cnt[rl], 1u);
+              if (slot < (uint32_t)kPLdsCand) {
+                sm.buf[rl][slot] = (int32_t)pos;
+              } else {
+                const uint32_t gs = atomicAdd(&a.cand_count[orow[mt]], 1u);
+                if (gs < (uint32_t)a.cap) a.cand[(int64_t)orow[mt] * a.cap + gs] = (int32_t)pos;
+              }
+            }
+          }
+        }
+      }
+      if (PASS == 0 && (nt & 3) == 3) {      // end of a group of 64 positions
+        const int64_t grp = (x0 + (int64_t)s * kPStage) / kPGroup + (nt >> 2);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const float v = row16_max(gm[mt]);
+          if (c == 0 && orow[mt] < a.R && grp * kPGroup < L) a.gmax[(int64_t)orow[mt] * a.gmax_stride + grp] = v;
+          gm[mt] = -__builtin_inff();
+        }
+      }
+    }
+  }
+
+  if (want_kmax) {
+    kmx = wave_max_u32(kmx);
+    if (lane == 0) sm.kmax[wave] = kmx;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = sm.kmax[0];
+      for (int i = 1; i < kPWaves; ++i) m = max(m, sm.kmax[i]);
+      a.kmax_part[blockIdx.x] = __uint_as_float(m << 16);
+    }
+  }
+#undef PF_LOAD_STAGE
+#undef PF_LOAD1
+  if (PASS == 1) {
+    // flush the LDS candidates: one global reservation per row
+    __syncthreads();
+    if (tid < kPRows) {
+      const int row = blockIdx.y * kPRows + tid;
+      const uint32_t n = min(sm.cnt[tid], (uint32_t)kPLdsCand);
+      sm.base[tid] = (n && row < a.R) ? atomicAdd(&a.cand_count[row], n) : 0u;
+    }
+    __syncthreads();
+    for (int i = tid; i < kPRows * kPLdsCand; i += kPWaves * 64) {
+      const int rl = i / kPLdsCand, e = i % kPLdsCand;
+      const int row = blockIdx.y * kPRows + rl;
+      const uint32_t n = min(sm.cnt[rl], (uint32_t)kPLdsCand);
+      const uint32_t dst = sm.base[rl] + (uint32_t)e;
+      if (row < a.R && (uint32_t)e < n && dst < (uint32_t)a.cap) a.cand[(int64_t)row * a.cap + dst] = sm.buf[rl][e];
+    }
+  }
+}
+
+// Threshold theta per row (one wave per row): tau = the largest key T with
+// its low 12 bits zero such that at least k group maxima have keys >= T
+// (a lower bound of the k-th largest group maximum), theta = tau - 2D.
+template <int NREG, bool HAS_W>
+__global__ __launch_bounds__(256) void pref_threshold_kernel(PrefArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.fb_count = 0u;
+  if (r >= a.R) return;
+  const int L = min(a.seq_len[0], a.n_max);
+  const int G = (L + kPGroup - 1) / kPGroup;
+  uint32_t key[NREG];
+#pragma unroll
+  for (int i = 0; i < NREG; ++i) {
+    const int gi = lane + 64 * i;
+    key[i] = gi < G ? order_key(a.gmax[(int64_t)r * a.gmax_stride + gi]) : 0u;
+  }
+  uint32_t T = 0u;
+  for (int b = 31; b >= 12; --b) {
+    const uint32_t cand = T | (1u << b);
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) cnt += (uint32_t)__popcll(__ballot(key[i] >= cand));
+    if (cnt >= (uint32_t)a.k) T = cand;
+  }
+  // kmax over the chunks of the sequence
+  const int nchunk = (L + kPChunk - 1) / kPChunk;
+  float km = 0.0f;
+  for (int i = lane; i < nchunk; i += 64) km = fmaxf(km, a.kmax_part[i]);
+  km = __uint_as_float(wave_max_u32(__float_as_uint(km)));
+  // sum_h |w_h| |q_h|_1: lane l holds elements 4l .. 4l+3, head l / 16
+  const uint2 qv = ((const uint2*)(a.q32 + (int64_t)r * 128))[lane];
+  float s1 = (fabsf(bf16_lo(qv.x)) + fabsf(bf16_hi(qv.x))) + (fabsf(bf16_lo(qv.y)) + fabsf(bf16_hi(qv.y)));
+  s1 = row16_sum(s1);
+  if (HAS_W) s1 *= fabsf(a.head_w[(int64_t)r * 4 + (lane >> 4)]);
+  const float aq = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 0)) +
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 16))) +
+                   (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 32)) +
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 48)));
+  if (lane == 0) {
+    float theta = -__builtin_inff();
+    if (T != 0u) {
+      const double tau = (double)key_to_float(T);
+      const double u = 0x1p-24, u2 = 0x1p-20;
+      const double D = (double)aq * (double)km * (17.0 * u + 73.0 * u2) * (1.0 + 0x1p-10) + 0x1p-120;
+      float t = (float)(tau - 2.0 * D);
+      t = t - fabsf(t) * 0x1p-20f;
+      theta = t;
+    }
+    a.theta[r] = theta;
+    a.cand_count[r] = 0u;
+  }
+}
+
+// Exact selection among the candidates of a row (one block per row).
+constexpr int kPSelKeyWords = kPrefCap + kPrefCap / 32;
+constexpr int kPBuckets = kSelThreads;                 // positions >> 9
+static_assert(kPrefMaxN / kPBuckets == 512, "bucket width");
+static_assert(kPrefCap % kSelPad == 0, "candidate capacity is a multiple of the LDS key padding");
+
+struct PrefSelSmem {
+  SelSmemT<kPSelKeyWords> sel;
+  int32_t pos[kPrefCap];
+  uint32_t bcnt[kPBuckets];
+  uint32_t boff[kPBuckets];
+};
+
+template <bool HAS_W>
+__global__ __launch_bounds__(kSelThreads) void pref_select_kernel(PrefArgs a) {
+  __shared__ PrefSelSmem sm;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const uint32_t n = a.cand_count[r];
+  int32_t* out = a.out + (int64_t)r * a.k;
+  if (n > (uint32_t)a.cap) {
+    if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1u)] = r;
+    return;
+  }
+  const int32_t* cl = a.cand + (int64_t)r * a.cap;
+  // ---- candidates into position order: bucket by position / 512, then rank within the bucket
+  sm.bcnt[tid] = 0u;
+  __syncthreads();
+  for (uint32_t e = tid; e < n; e += kSelThreads) atomicAdd(&sm.bcnt[cl[e] >> 9], 1u);
+  __syncthreads();
+  uint32_t total;
+  const uint32_t my_cnt = sm.bcnt[tid];
+  const uint32_t off = block_excl_scan(sm.sel, my_cnt, total);
+  sm.boff[tid] = off;
+  sm.bcnt[tid] = 0u;
+  __syncthreads();
+  for (uint32_t e = tid; e < n; e += kSelThreads) {
+    const int32_t p = cl[e];
+    const uint32_t b = (uint32_t)p >> 9;
+    sm.pos[sm.boff[b] + atomicAdd(&sm.bcnt[b], 1u)] = p;
+  }
+  __syncthreads();
+  constexpr int kPer = kPrefCap / kSelThreads;
+  int32_t rp[kPer];
+  int32_t rd[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t e = tid + i * kSelThreads;
+    rd[i] = -1;
+    if (e < n) {
+      const int32_t p = sm.pos[e];
+      const uint32_t b = (uint32_t)p >> 9;
+      const uint32_t lo = sm.boff[b], hi = lo + sm.bcnt[b];
+      uint32_t rank = 0;
+      for (uint32_t j = lo; j < hi; ++j) rank += sm.pos[j] < p ? 1u : 0u;
+      rp[i] = p;
+      rd[i] = (int32_t)(lo + rank);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (rd[i] >= 0) sm.pos[rd[i]] = rp[i];
+  __syncthreads();
+
+  // ---- canonical scores: 8 lanes per candidate (lane j: channels 8j .. 8j+7)
+  const int j = tid & 7, grp = tid >> 3;
+  float qf[4][8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint4 v = ((const uint4*)(a.q32 + (int64_t)r * 128))[h * 8 + j];
+    qf[h][0] = bf16_lo(v.x); qf[h][1] = bf16_hi(v.x);
+    qf[h][2] = bf16_lo(v.y); qf[h][3] = bf16_hi(v.y);
+    qf[h][4] = bf16_lo(v.z); qf[h][5] = bf16_hi(v.z);
+    qf[h][6] = bf16_lo(v.w); qf[h][7] = bf16_hi(v.w);
+  }
+  float wt[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if (HAS_W) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) wt[h] = a.head_w[(int64_t)r * 4 + h];
+  }
+  const int n_pad = n ? sel_padded((int)n) : kSelPad;
+  for (int e0 = 0; e0 < (int)n; e0 += kSelThreads / 8) {
+    const int e = e0 + grp;
+    const int32_t p = e < (int)n ? sm.pos[e] : -1;
+    const int64_t slot = p >= 0 ? a.map(0, p) : -1;
+    const uint4 kw = a.kdata[(slot >= 0 ? slot : 0) * 8 + j];
+    const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
+                         bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+    float d[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(kf[i], qf[h][i], acc);
+      acc = acc + PF_DPP(acc, kQuadSwap1);     // c_j + c_(j^1)
+      acc = acc + PF_DPP(acc, kQuadSwap2);     // (c0+c1)+(c2+c3) in lanes 0..3
+      acc = acc + PF_DPP(acc, kHalfMirror);    // + ((c4+c5)+(c6+c7))
+      d[h] = acc;
+    }
+    float rr[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) rr[h] = d[h] > 0.0f ? d[h] : 0.0f;
+    float sc;
+    if (HAS_W)
+      sc = (wt[0] * rr[0] + wt[1] * rr[1]) + (wt[2] * rr[2] + wt[3] * rr[3]);
+    else
+      sc = (rr[0] + rr[1]) + (rr[2] + rr[3]);
+    if (j == 0 && e < (int)n) sm.sel.key[skew(e)] = slot >= 0 ? order_key(sc) : 0u;
+  }
+  for (int e = (int)n + tid; e < n_pad; e += kSelThreads) sm.sel.key[skew(e)] = 0u;
+  __syncthreads();
+
+  // ---- exact Top-k in position order
+  const LdsKeysT<SelSmemT<kPSelKeyWords>> ks{&sm.sel, n_pad};
+  const SelResult res = block_select(sm.sel, ks, (uint32_t)a.k, 0u);
+  const uint32_t kept = block_compact(sm.sel, ks, res, (uint32_t)a.k,
+                                      [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
+  for (int i = (int)kept + tid; i < a.k; i += kSelThreads) out[i] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_index(const PrefArgs& a, bool has_w, hipStream_t st) {
+  if (a.R <= 0) return hipSuccess;
+  if (a.n_max > kPrefMaxN || a.cap != kPrefCap || a.k > kPrefCap) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.n_max + kPChunk - 1) / kPChunk), (unsigned)((a.R + kPRows - 1) / kPRows));
+  const dim3 tgrid((unsigned)((a.R + 3) / 4));
+  const int G = (a.n_max + kPGroup - 1) / kPGroup;
+  if (has_w) {
+    hipLaunchKernelGGL((pref_pass_kernel<0, true>), grid, dim3(kPWaves * 64), 0, st, a);
+    if (G <= 2048) hipLaunchKernelGGL((pref_threshold_kernel<32, true>), tgrid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pref_threshold_kernel<64, true>), tgrid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pref_pass_kernel<1, true>), grid, dim3(kPWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((pref_select_kernel<true>), dim3(a.R), dim3(kSelThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((pref_pass_kernel<0, false>), grid, dim3(kPWaves * 64), 0, st, a);
+    if (G <= 2048) hipLaunchKernelGGL((pref_threshold_kernel<32, false>), tgrid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((pref_threshold_kernel<64, false>), tgrid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pref_pass_kernel<1, false>), grid, dim3(kPWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((pref_select_kernel<false>), dim3(a.R), dim3(kSelThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa2

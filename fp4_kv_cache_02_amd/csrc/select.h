@@ -31,14 +31,17 @@ constexpr int kRegCap = kSelThreads * kRegPer; // 2048
 CSA2_DEV int skew(int e) { return e + (e >> 5); }
 constexpr int kSelKeyWords = kSelCap + kSelCap / 32;
 
-struct SelSmem {
-  uint32_t key[kSelKeyWords];
+// KW: LDS words of the key set (skewed), e.g. kSelKeyWords for kSelCap keys.
+template <int KW>
+struct SelSmemT {
+  uint32_t key[KW];
   uint32_t bins[kSelBins];
   uint32_t wa[kSelWaves];
   uint32_t wb[kSelWaves];
   uint32_t wc[kSelWaves];
   uint32_t bc[4];
 };
+using SelSmem = SelSmemT<kSelKeyWords>;
 
 // LDS key sets are read in batches of kSelBatch independent reads without
 // bounds tests (a test per read would make the compiler wait on each read).
@@ -62,8 +65,9 @@ struct RegKeys {
 };
 
 // Keys in LDS: sm.key[skew(e)] for e < n (n a multiple of kSelPad).
-struct LdsKeys {
-  const SelSmem* sm;
+template <class Sm>
+struct LdsKeysT {
+  const Sm* sm;
   int n;
   template <class F>
   CSA2_DEV void each(const F& f) const {
@@ -88,6 +92,7 @@ struct LdsKeys {
     }
   }
 };
+using LdsKeys = LdsKeysT<SelSmem>;
 
 // Wave-wide inclusive scan and reductions through DPP lane shifts (no LDS
 // round trips): shifts by 1, 2, 4, 8 within each row of 16 lanes, then the
@@ -114,7 +119,8 @@ CSA2_DEV uint32_t wave_sum_u32(uint32_t v) {
 }
 
 // Exclusive prefix sum of v in thread order; total returned through `total`.
-CSA2_DEV uint32_t block_excl_scan(SelSmem& sm, uint32_t v, uint32_t& total) {
+template <class Sm>
+CSA2_DEV uint32_t block_excl_scan(Sm& sm, uint32_t v, uint32_t& total) {
   const int tid = threadIdx.x, w = tid / kWave;
   const uint32_t inc = wave_incl_scan_u32(v);
   if (lane_id() == kWave - 1) sm.wa[w] = inc;
@@ -132,8 +138,8 @@ CSA2_DEV uint32_t block_excl_scan(SelSmem& sm, uint32_t v, uint32_t& total) {
 }
 
 // Minimum and maximum present key, and the number of present keys.
-template <class Keys>
-CSA2_DEV void block_range(SelSmem& sm, const Keys& ks, uint32_t& kmin, uint32_t& kmax, uint32_t& count) {
+template <class Keys, class Sm>
+CSA2_DEV void block_range(Sm& sm, const Keys& ks, uint32_t& kmin, uint32_t& kmax, uint32_t& count) {
   uint32_t mn = 0xFFFFFFFFu, mx = 0u, c = 0u;
   ks.each([&](uint32_t v) {
     mn = v ? min(mn, v) : mn;
@@ -175,8 +181,8 @@ struct SelResult {
 // The k-th largest present key (exact = true), or, when `cap` > 0, an earlier
 // bin edge T such that k <= #{keys >= T} <= cap (exact = false; keep every
 // key >= T).  With at most k present keys: T = 0, n_gt = count (keep all).
-template <class Keys>
-CSA2_DEV SelResult block_select(SelSmem& sm, const Keys& ks, uint32_t kth, uint32_t cap, uint64_t* tr = nullptr) {
+template <class Keys, class Sm>
+CSA2_DEV SelResult block_select(Sm& sm, const Keys& ks, uint32_t kth, uint32_t cap, uint64_t* tr = nullptr) {
   const int tid = threadIdx.x;
   uint32_t lo, hi, count;
   block_range(sm, ks, lo, hi, count);
@@ -257,8 +263,8 @@ CSA2_DEV SelResult block_select(SelSmem& sm, const Keys& ks, uint32_t kth, uint3
 // wanted: keys > T, plus (exact) the first k - n_gt keys == T in element
 // order, or (not exact) every key >= T.  emit(out_pos, element) is called for
 // each kept element; returns the number kept.
-template <class Keys, class Emit>
-CSA2_DEV uint32_t block_compact(SelSmem& sm, const Keys& ks, const SelResult& s, uint32_t kth, const Emit& emit) {
+template <class Keys, class Emit, class Sm>
+CSA2_DEV uint32_t block_compact(Sm& sm, const Keys& ks, const SelResult& s, uint32_t kth, const Emit& emit) {
   const uint32_t need_eq = s.exact ? (kth > s.n_gt ? kth - s.n_gt : 0u) : 0u;
   const bool keep_all = (s.T == 0u);
   const uint32_t T = s.T;

@@ -259,7 +259,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
   __shared__ SelSmem sm;
   __shared__ int32_t par[2][kSelCap / 8];
   __shared__ int32_t cmap[kSelCap / 8];     // the row's candidate blocks (output index map)
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
+  int r = blockIdx.x;
+  if (a.row_list) {
+    if ((uint32_t)r >= *a.row_list_count) return;
+    r = a.row_list[r];
+  }
   if (a.cand_blocks)
     for (int i = tid; i < a.cand_stride; i += kSelThreads) cmap[i] = a.cand_blocks[(int64_t)r * a.cand_stride + i];
   const int64_t n0 = row_count(a, r);
