@@ -52,12 +52,15 @@ constexpr int kStepKeys = 128;                  // keys per step (32 per wave)
 constexpr int kQRow = 65;                       // uint4 per head row of Q in LDS (64 + 1 pad)
 constexpr int kPRow = kStepKeys + 8;            // halves per head row of P in LDS
 
+constexpr int kCodeRow = 68;                   // dwords per staged key row (256 B of codes + 16 B pad)
+
 struct AttnSmem {
-  uint4 qb[16 * kQRow];        // query, bf16
-  uint4 qh[16 * kQRow];        // query, fp16
+  uint4 q[16 * kQRow];         // query of the step kind: fp16 (main steps) or bf16 (window step)
   uint16_t p_hi[16 * kPRow];
   uint16_t p_lo[16 * kPRow];
   int32_t slot[kStepKeys];     // slot of each main key of the step (-1: absent)
+  uint32_t code[kStepKeys * kCodeRow];   // FP4 codes of the step's main keys (zeros when absent)
+  uint32_t scale[kStepKeys * 8];         // their E4M3 scales
   float red_m[kAttnWaves][16];
   float red_l[kAttnWaves][16];
 };
@@ -107,6 +110,7 @@ CSA2_DEV uint32_t f32_to_bf16_rne(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+CSA2_DEV uint4 mask4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
 CSA2_DEV float pick4(const float (&v)[4], int i) {
   return (i == 0) ? v[0] : (i == 1) ? v[1] : (i == 2) ? v[2] : v[3];
 }
@@ -120,24 +124,17 @@ struct RowState {
 
 // ---- phase 1: logits of this wave's 32 keys (lane (c, g): head c, keys sigma(g, e)) ----
 // sigma(g, e) = 4g + e (e < 4), 16 + 4g + e - 4 (e >= 4)
-CSA2_DEV void qk_main(const AttnArgs& a, const AttnSmem& sm, int slot, int c, int g, float (&s)[8]) {
-  const uint4* qrow = sm.qh + c * kQRow + 16 * g;
+CSA2_DEV void qk_main(const AttnSmem& sm, int w, int c, int g, float (&s)[8]) {
+  const uint4* qrow = sm.q + c * kQRow + 16 * g;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int32_t su = __shfl(slot, 16 * u + c, 64);
+    const int key = 32 * w + 16 * u + c;
+    const uint4* src = (const uint4*)&sm.code[key * kCodeRow + 16 * g];
     uint4 raw[4];
-    uint2 sc;
-    if (su >= 0) {
-      const uint4* src = (const uint4*)(a.kv + (int64_t)su * 256 + g * 64);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = src[i];
-      sc = *(const uint2*)(a.kv_scale + (int64_t)su * 32 + g * 8);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = make_uint4(0, 0, 0, 0);
-      sc = make_uint2(0, 0);
-    }
+    for (int i = 0; i < 4; ++i) raw[i] = src[i];
+    const uint2 sc = *(const uint2*)&sm.scale[key * 8 + 2 * g];
     const uint32_t rw[16] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w,
                              raw[2].x, raw[2].y, raw[2].z, raw[2].w, raw[3].x, raw[3].y, raw[3].z, raw[3].w};
 #pragma unroll
@@ -153,17 +150,21 @@ CSA2_DEV void qk_main(const AttnArgs& a, const AttnSmem& sm, int slot, int c, in
 
 CSA2_DEV void qk_win(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int kk0, int c, int g,
                      float (&s)[8]) {
-  const uint4* qrow = sm.qb + c * kQRow + 16 * g;
-#pragma unroll
+  const uint4* qrow = sm.q + c * kQRow + 16 * g;
+#pragma unroll 1
   for (int u = 0; u < 2; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int kk = kk0 + 16 * u + c;
     const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
+    // unconditional loads (entry 0 stands in for an absent one), zeroed after
     const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
+    uint4 kr[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) kr[t] = src[t];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint4 kr = ok ? src[t] : make_uint4(0, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr), as_bf8(qrow[t]), acc, 0, 0, 0);
+      const uint4 kz = mask4(kr[t], ok ? 0xFFFFFFFFu : 0u);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kz), as_bf8(qrow[t]), acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
@@ -171,7 +172,7 @@ CSA2_DEV void qk_win(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, in
 }
 
 // ---- phase 3: O[16 heads x dims 128w .. 128w+127] += P V over the step's 128 keys ----
-CSA2_DEV void pv_main(const AttnArgs& a, const AttnSmem& sm, RowState& st, int w, int c, int g) {
+CSA2_DEV void pv_main(const AttnSmem& sm, RowState& st, int w, int c, int g) {
 #pragma unroll 1
   for (int ks = 0; ks < 4; ++ks) {
     const int key0 = 32 * ks + 8 * g;
@@ -179,14 +180,10 @@ CSA2_DEV void pv_main(const AttnArgs& a, const AttnSmem& sm, RowState& st, int w
     half2_t sv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int32_t sl = sm.slot[key0 + i];
-      uint32_t code = 0, sb = 0;
-      if (sl >= 0) {
-        code = *(const uint32_t*)(a.kv + (int64_t)sl * 256 + 64 * w + 4 * c);
-        sb = a.kv_scale[(int64_t)sl * 32 + 8 * w + (c >> 1)];
-      }
-      dw[i] = code;
-      sv[i] = scale_h2(sb);
+      const int key = key0 + i;
+      dw[i] = sm.code[key * kCodeRow + 16 * w + c];
+      const uint32_t sw = sm.scale[key * 8 + 2 * w + (c >> 3)];
+      sv[i] = scale_h2((sw >> (8 * ((c >> 1) & 3))) & 0xFFu);
     }
     const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
     const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
@@ -215,7 +212,8 @@ CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int 
     for (int i = 0; i < 8; ++i) {
       const int kk = key0 + i;
       const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
-      vr[i] = ok ? Ly.swa_v[((int64_t)b * Ly.S + wst + kk) * 64 + 16 * w + c] : make_uint4(0, 0, 0, 0);
+      const uint4 v = Ly.swa_v[((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + 16 * w + c];
+      vr[i] = mask4(v, ok ? 0xFFFFFFFFu : 0u);
     }
     const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
     const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
@@ -234,7 +232,7 @@ CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int 
   }
 }
 
-__global__ __launch_bounds__(kAttnWaves * 64) void fp4_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fp4_attn_kernel(AttnArgs a) {
   __shared__ AttnSmem sm;
   // flat grid: block id = (li * R + r) * n_blocks + blk
   const int blk = blockIdx.x % a.n_blocks;
@@ -252,19 +250,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void fp4_attn_kernel(AttnArgs a) {
   const int wl = min(Ly.swa_len[r], CSA2_MAX_WINDOW);
   CSA2_MARK(a, 0);
 
-  // query of the row into LDS, bf16 and fp16
-  {
-    const uint4* q = Ly.q + (int64_t)r * 16 * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i;          // uint4 index: head e / 64, piece e % 64
-      const uint4 v = q[e];
-      const int h = e >> 6, p = e & 63;
-      sm.qb[h * kQRow + p] = v;
-      sm.qh[h * kQRow + p] = bf16x8_to_f16x8(v);
-    }
-  }
-
   RowState st;
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.o[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -274,27 +259,56 @@ __global__ __launch_bounds__(kAttnWaves * 64) void fp4_attn_kernel(AttnArgs a) {
     st.l[i] = 0.f;
   }
 
+  const uint4* qsrc = Ly.q + (int64_t)r * 16 * 64;
   for (int step = st0; step < st1; ++step) {
     const bool is_main = step < n_main;
+    // query of the row into LDS: fp16 for main steps, bf16 for the window
+    // step (the previous step ended with a barrier)
+    if (step == st0 || !is_main) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + 256 * i;          // uint4 index: head e / 64, piece e % 64
+        const uint4 v = qsrc[e];
+        sm.q[(e >> 6) * kQRow + (e & 63)] = is_main ? bf16x8_to_f16x8(v) : v;
+      }
+    }
     // ---- keys of this wave: 32w .. 32w+31 of the step ----
-    const int kk = step * kStepKeys + 32 * w + (lane & 31);    // main: index into idx
-    int32_t slot = -1;
     bool valid;
     if (is_main) {
-      const int pos = kk < a.k ? idx_row[kk] : -1;
-      slot = (pos >= 0 && pos < L) ? (int32_t)a.map(b, pos) : -1;
-      valid = slot >= 0;
-      if (lane < 32) sm.slot[32 * w + lane] = slot;
+      if (tid < kStepKeys) {
+        const int kk = step * kStepKeys + tid;
+        const int pos = kk < a.k ? idx_row[kk] : -1;
+        sm.slot[tid] = (pos >= 0 && pos < L) ? (int32_t)a.map(b, pos) : -1;
+      }
+      __syncthreads();
+      // stage the step's FP4 rows: thread t loads half (t & 1) of key t >> 1
+      // (unconditional loads from slot 0 for absent keys, zeroed after)
+      {
+        const int key = tid >> 1, half = tid & 1;
+        const int32_t sl = sm.slot[key];
+        const int64_t ss = sl >= 0 ? sl : 0;
+        const uint4* src = (const uint4*)(a.kv + ss * 256 + 128 * half);
+        uint4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = src[i];
+        const uint4 sc = *(const uint4*)(a.kv_scale + ss * 32 + 16 * half);
+        const uint32_t m = sl >= 0 ? 0xFFFFFFFFu : 0u;    // (a select of whole uint4s goes through scratch)
+        uint4* dst = (uint4*)&sm.code[key * kCodeRow + 32 * half];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = mask4(v[i], m);
+        *(uint4*)&sm.scale[key * 8 + 4 * half] = mask4(sc, m);
+      }
+      valid = sm.slot[32 * w + (lane & 31)] >= 0;
     } else {
       const int e = 32 * w + (lane & 31);
       valid = e < wl && wst >= 0 && (int64_t)wst + e < Ly.S;
     }
     const uint64_t vmask = __ballot(valid);
-    __syncthreads();    // query (first step) and slots visible
+    __syncthreads();    // query, codes and scales visible
     CSA2_MARK(a, 1);
     float s[8];
     if (is_main)
-      qk_main(a, sm, slot, c, g, s);
+      qk_main(sm, w, c, g, s);
     else
       qk_win(Ly, sm, b, wst, wl, 32 * w, c, g, s);
     CSA2_MARK(a, 2);
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void fp4_attn_kernel(AttnArgs a) {
     }
     CSA2_MARK(a, 3);
     if (is_main)
-      pv_main(a, sm, st, w, c, g);
+      pv_main(sm, st, w, c, g);
     else
       pv_win(Ly, sm, st, b, wst, wl, w, c, g);
     CSA2_MARK(a, 4);
@@ -424,23 +438,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const AttnLayer& Ly = a.layer[li];
   const int tid = threadIdx.x, th = tid >> 4, tc = tid & 15;
   const int64_t prow = (int64_t)lr * a.n_blocks;
+  CSA2_MARK(a, 16);
+  // every load is unconditional (blocks past n_blocks re-read the last one
+  // and get weight 0), so all of them are in flight at once
   float mj[kMaxAttnBlocks], lj[kMaxAttnBlocks];
-  float M = -__builtin_inff();
+  float4 v[kMaxAttnBlocks][8];
 #pragma unroll
   for (int j = 0; j < kMaxAttnBlocks; ++j) {
-    if (j < a.n_blocks) {
-      mj[j] = a.part_ml[(prow + j) * 32 + th * 2 + 0];
-      lj[j] = a.part_ml[(prow + j) * 32 + th * 2 + 1];
-    } else {
-      mj[j] = -__builtin_inff();
-      lj[j] = 0.f;
-    }
-    M = fmaxf(M, mj[j]);
+    const int64_t pj = prow + min(j, a.n_blocks - 1);
+    mj[j] = a.part_ml[pj * 32 + th * 2 + 0];
+    lj[j] = a.part_ml[pj * 32 + th * 2 + 1];
+    const float* po = a.part_o + pj * (16 * 512) + th * 512 + tc * 32;
+#pragma unroll
+    for (int q4 = 0; q4 < 8; ++q4) v[j][q4] = *(const float4*)(po + 4 * q4);
   }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < kMaxAttnBlocks; ++j) M = fmaxf(M, j < a.n_blocks ? mj[j] : -__builtin_inff());
+  CSA2_MARK(a, 17);
   float Lsum = 0.f, wj[kMaxAttnBlocks];
 #pragma unroll
   for (int j = 0; j < kMaxAttnBlocks; ++j) {
-    wj[j] = (mj[j] == -__builtin_inff()) ? 0.f : __expf(mj[j] - M);
+    wj[j] = (j >= a.n_blocks || mj[j] == -__builtin_inff()) ? 0.f : __expf(mj[j] - M);
     Lsum += wj[j] * lj[j];
   }
   float4 acc[8];
@@ -448,16 +467,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   for (int q4 = 0; q4 < 8; ++q4) acc[q4] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < kMaxAttnBlocks; ++j) {
-    if (j < a.n_blocks) {
-      const float* po = a.part_o + (prow + j) * (16 * 512) + th * 512 + tc * 32;
 #pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4) {
-        const float4 v = *(const float4*)(po + 4 * q4);
-        acc[q4].x += wj[j] * v.x;
-        acc[q4].y += wj[j] * v.y;
-        acc[q4].z += wj[j] * v.z;
-        acc[q4].w += wj[j] * v.w;
-      }
+    for (int q4 = 0; q4 < 8; ++q4) {
+      acc[q4].x += wj[j] * v[j][q4].x;
+      acc[q4].y += wj[j] * v[j][q4].y;
+      acc[q4].z += wj[j] * v[j][q4].z;
+      acc[q4].w += wj[j] * v[j][q4].w;
     }
   }
   const float inv = (Lsum > 0.f) ? 1.0f / Lsum : 0.f;
@@ -466,6 +481,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   for (int q4 = 0; q4 < 8; ++q4)
     *(float4*)(out_row + 4 * q4) = make_float4(acc[q4].x * inv, acc[q4].y * inv, acc[q4].z * inv, acc[q4].w * inv);
   if (Ly.lse && tc == 0) Ly.lse[(int64_t)r * 16 + th] = (Lsum > 0.f) ? M + __logf(Lsum) : -__builtin_inff();
+  CSA2_MARK(a, 18);
 }
 
 int attn_steps(int k) { return (k + kStepKeys - 1) / kStepKeys + 1; }

@@ -83,13 +83,16 @@ CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Phase timestamps for kernel tuning: only a build with -DCSA2_TRACE records
-// them (thread 0 of the block with all block indices 0 writes the 100 MHz
+// them (thread 0 of block CSA2_TRACE_BLOCK, default 0, writes the 100 MHz
 // wall clock into slot i of the trace buffer set by csa2_trace_set).
 #ifdef CSA2_TRACE
+#ifndef CSA2_TRACE_BLOCK
+#define CSA2_TRACE_BLOCK 0
+#endif
 #define CSA2_TRACE_ARG uint64_t* trace;
 #define CSA2_MARK(a, i)                                                                       \
   do {                                                                                         \
-    if ((a).trace && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) { \
+    if ((a).trace && threadIdx.x == 0 && blockIdx.x == CSA2_TRACE_BLOCK && blockIdx.y == 0 && blockIdx.z == 0) { \
       (a).trace[(i)] = wall_clock64();                                                         \
       (a).trace[32 + (i)] = __builtin_amdgcn_s_memtime();                                      \
     }                                                                                          \
@@ -97,7 +100,7 @@ CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
 // inner marks: a trace pointer passed down explicitly
 #define CSA2_MARKP(tr, i)                                                                        \
   do {                                                                                           \
-    if ((tr) && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {     \
+    if ((tr) && threadIdx.x == 0 && blockIdx.x == CSA2_TRACE_BLOCK && blockIdx.y == 0 && blockIdx.z == 0) { \
       (tr)[(i)] = wall_clock64();                                                                \
       (tr)[32 + (i)] = __builtin_amdgcn_s_memtime();                                             \
     }                                                                                            \

@@ -89,7 +89,7 @@ CSA2_DEV uint4 key_chunk(const uint4* __restrict__ kd, const StepGeo& s, int i, 
   return kd[slot * 8 + j];
 }
 
-template <bool CAND, bool HAS_W, bool MAXIMA>
+template <bool CAND, bool HAS_W, bool MAXIMA, bool PERSIST>
 __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 3, j = lane & 7;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
       }
     }
     const uint32_t next = item + W;
-    const bool has_next = next < n_items;
+    const bool has_next = PERSIST && next < n_items;
     StepGeo nxt = cur;
     if (has_next) nxt = step_geo<CAND>(a, next, g);
 
@@ -219,12 +219,21 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
 hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxima, hipStream_t st) {
   const int64_t items = (int64_t)a.R * a.steps_per_row;
   if (items == 0) return hipSuccess;
-  if (items > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  if (items > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  // One step per wave: every wave issues its eight loads at once and the
+  // hardware refills freed wave slots (measured faster than persistent waves
+  // that prefetch their next step).  A row list (device-side count) runs on
+  // a persistent grid of ~4 resident blocks per CU instead.
+  const bool persist = a.row_list != nullptr;
   int64_t blocks = (items + kScanWaves - 1) / kScanWaves;
-  const int64_t cap = 256 * 6;           // ~6 resident blocks of 4 waves per CU
-  if (blocks > cap) blocks = cap;
-#define CSA2_IDX_LAUNCH(C, Wt, M) \
-  hipLaunchKernelGGL((index_scan_kernel<C, Wt, M>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a)
+  if (persist && blocks > 256 * 4) blocks = 256 * 4;
+#define CSA2_IDX_LAUNCH(C, Wt, M)                                                                       \
+  do {                                                                                                 \
+    if (persist)                                                                                       \
+      hipLaunchKernelGGL((index_scan_kernel<C, Wt, M, true>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a); \
+    else                                                                                               \
+      hipLaunchKernelGGL((index_scan_kernel<C, Wt, M, false>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a); \
+  } while (0)
   if (cand) {
     if (has_w) CSA2_IDX_LAUNCH(true, true, false); else CSA2_IDX_LAUNCH(true, false, false);
   } else if (maxima) {
