@@ -31,10 +31,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=1, help="workload id (1: 128K decode group)")
+    p.add_argument("--config", type=int, default=1,
+                   help="workload id (1: 128K decode group; 2: 1M decode group; 3: prefill chunk; 4: mixed serving)")
     p.add_argument("--replicas", type=int, default=3,
                    help="input replicas cycled per step so the 256 MB last-level cache cannot serve them")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-1m", action="store_true", help="skip the 1M-context group (reported beside the default)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -96,7 +98,7 @@ def cpu_baseline(w, min_seconds):
     from fp4_kv_cache_02_amd import synth
     from oracle import csa2_oracle as O
 
-    rows = list(range(w.R))
+    rows = list(range(w.R if not w.prefill_rows else 4))   # prefill: a sample of 4 chunk rows
     n_slots, pt, _ = synth.slots_layout(w)
     K = np.zeros((n_slots, 64), np.uint16)
     q_full = synth.gen_q_idx(w, 0) if w.planted > 0 else None
@@ -127,7 +129,8 @@ def cpu_baseline(w, min_seconds):
         for li, m in enumerate(w.schedule):
             qi, q, k, v, st, ln = layer_in[li]
             blocks_only = m == "F" and w.hier and w.full_blocks_only
-            O.layer_step(synth.MODES[m], cache, state, list(range(w.R)), qi, q, k, v, st, ln,
+            row_seq = [0] * w.R if w.prefill_rows else list(range(w.R))
+            O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln,
                          1.0 / math.sqrt(512), hier=w.hier, blocks_only=blocks_only, rows=rows)
             attended += 0 if blocks_only else len(rows)
         reps += 1
@@ -137,37 +140,35 @@ def cpu_baseline(w, min_seconds):
     if ctx is not None:
         ctx.restore_original_limits()
     return {"value": attended / dt, "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
-            "sample": f"the whole workload ({w.R} rows x {len(w.schedule)} layers) run {reps} times, "
+            "sample": f"{'the whole workload' if len(rows) == w.R else f'{len(rows)} of the {w.R} rows of the workload'} "
+                      f"({len(rows)} rows x {len(w.schedule)} layers) run {reps} times, "
                       f"{attended} row-layers in {dt:.1f} s on 1 host thread (numpy elementwise float32 "
                       f"scores, float64 attention); input generation not timed"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU design "
-                                   "(sequence- or context-parallel) is not built", "n_gpus": args.gpus}))
-        sys.exit(2)
-    import numpy as np
+def data_desc(w):
+    if w.raw_fp4:
+        kv = "main KV drawn as raw FP4 nibbles and E4M3 scale codes 0x20-0x37"
+    elif w.kv_pool:
+        kv = f"N(0,1) main KV quantised on the GPU from a pool of {w.kv_pool} vectors"
+    else:
+        kv = "N(0,1) main KV quantised on the GPU"
+    extra = f", {w.planted:.0%} planted indexer keys" if w.planted else ""
+    return f"synthetic (seeded; {kv}; bf16 N(0,1) queries, indexer keys and windows{extra})"
+
+
+def measure(w, steps, warmup, n_replicas):
+    """Times `steps` whole steps of workload w (every group once) and, apart,
+    back-to-back launches of its dominant kernel (the Full layer's scan, with
+    the arguments, grid and outputs of the step).  Returns a dict."""
     import torch
+    from fp4_kv_cache_02_amd import csa2, group
 
-    if args.copy_probe:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 3}))
-        return
-
-    from fp4_kv_cache_02_amd import csa2, group, synth
-
-    w = synth.workload(args.config)
     t_setup = time.perf_counter()
     base = group.build_inputs(w)
     reps = [base]
     # extra replicas of the per-position caches (the per-layer inputs are small)
-    for _ in range(max(0, args.replicas - 1)):
+    for _ in range(max(0, n_replicas - 1)):
         reps.append(group.GroupInputs(kv_fp4=base.kv_fp4.clone(), kv_scale=base.kv_scale.clone(),
                                       k_idx=base.k_idx.clone(), seq_len=base.seq_len, page_table=base.page_table,
                                       seq_stride=base.seq_stride, row_seq=base.row_seq, layers=base.layers))
@@ -176,29 +177,27 @@ def main():
     t_setup = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
+    for i in range(warmup):
         runners[i % len(runners)].step()
     torch.cuda.synchronize()
-
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         runners[i % len(runners)].step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / steps
 
     algo, scan_bytes, attn_layers = algorithmic_bytes(w)
-    value = w.R * attn_layers / (ms * 1e-3)
-
-    # dominant kernel: the Full layer's indexer scan, launched exactly as in the
-    # step (same entry point, arguments, grid and outputs), K launches cycling
-    # the replicas between two events on the stream they are launched on
+    res = {"ms": ms, "value": w.R * attn_layers / (ms * 1e-3), "attn_layers": attn_layers, "algo": algo,
+           "replicas": len(runners), "setup_s": t_setup}
+    if w.prefill_rows:
+        return res              # prefill: the step as a whole is priced against the MFMA peak
     li_full = w.schedule.index("F")
-    n_scan = max(10, args.steps)
+    n_scan = max(10, steps)
     scores = torch.empty((w.R, w.n_max), dtype=torch.float32, device="cuda")
     bmax = torch.empty((w.R, (w.n_max + 7) // 8), dtype=torch.float32, device="cuda")
+
     def scan(i):
         r = runners[i % len(runners)]
         csa2.csa2_index_score(r.inp.layers[li_full].q_idx, r.kidx, r.inp.seq_len, scores, row_seq=r.inp.row_seq,
@@ -214,33 +213,79 @@ def main():
     torch.cuda.synchronize()
     kern_ms = a.elapsed_time(b) / n_scan
     scan_algo = sum(128 * L + 512 for L in w.seq_lens)   # indexer keys + query, per launch
-    achieved = scan_algo / (kern_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(os.path.join(ROOT, "fp4_kv_cache_02_amd", "csrc", "index_score.hip"))
+    res.update({"kern_ms": kern_ms, "scan_algo": scan_algo})
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU design "
+                                   "(sequence- or context-parallel) is not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 3}))
+        return
+
+    from fp4_kv_cache_02_amd import synth
+
+    w = synth.workload(args.config)
+    m = measure(w, args.steps, args.warmup, args.replicas if not w.prefill_rows else 1)
+    if w.prefill_rows:
+        # indexer 512 flop per (row, entry); attention 20.97 MFLOP per row-layer
+        flops = w.R * w.n_max * 512 + m["attn_layers"] * w.R * 2 * 2 * 16 * 512 * (512 + 128)
+        tflops = flops / (m["ms"] * 1e-3) / 1e12
+        roof = {"kernel": "whole prefill group step (MFMA indexer passes, selection, attention)", "bound": "mfma",
+                "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "flops_per_step": flops}
+    else:
+        achieved = m["scan_algo"] / (m["kern_ms"] * 1e-3) / 1e9
+        traffic = traffic_from_profiles(os.path.join(ROOT, "fp4_kv_cache_02_amd", "csrc", "index_score.hip"))
+        if w.name != "cfg1_F3R_b8_L131072":
+            traffic = None          # the committed counter summary covers the 128K decode scan only
+        roof = {"kernel": "index_scan_kernel (Full-layer indexer scan)", "bound": "hbm",
+                "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                "algorithmic_bytes_per_launch": m["scan_algo"], "avg_launch_ms": m["kern_ms"]}
 
     out = {
         "metric": "CSA2 decode tokens/s/layer + % of HBM roofline at 128K and 1M ctx",
-        "value": value,
+        "value": m["value"],
         "unit": "tokens/s/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": m["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp4(e2m1)+e4m3 main KV, bf16 indexer/query/window, f32 accumulate",
-        "data": "synthetic (seeded; N(0,1) main KV quantised on the GPU, 1% planted indexer keys)",
+        "data": data_desc(w),
         "config": {"workload": w.name, "batch": w.B, "context": w.n_max, "layers": w.schedule,
-                   "topk": 512, "window": 128, "replicas": len(runners)},
-        "step_algorithmic_bytes": algo,
-        "step_gbps": algo / (ms * 1e-3) / 1e9,
-        "step_frac_of_hbm_peak": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "roofline": {"kernel": "index_scan_kernel (Full-layer indexer scan)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": scan_algo, "avg_launch_ms": kern_ms},
-        "setup_s": t_setup,
+                   "topk": 512, "window": 128, "replicas": m["replicas"]},
+        "step_algorithmic_bytes": m["algo"],
+        "step_gbps": m["algo"] / (m["ms"] * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": m["algo"] / (m["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": roof,
+        "setup_s": m["setup_s"],
     }
+    if args.config == 1 and not args.no_1m:
+        # the metric's second context: the 1M decode group (hierarchical Full
+        # layer building 2048 candidate blocks, then Reindex + 3 Reuse)
+        w2 = synth.workload(2)
+        m2 = measure(w2, args.steps, args.warmup, args.replicas)
+        a2 = m2["scan_algo"] / (m2["kern_ms"] * 1e-3) / 1e9
+        out["context_1m"] = {"workload": w2.name, "value": m2["value"], "unit": "tokens/s/layer",
+                             "ms_per_step": m2["ms"], "step_gbps": m2["algo"] / (m2["ms"] * 1e-3) / 1e9,
+                             "scan_avg_launch_ms": m2["kern_ms"], "scan_achieved_gbps": a2,
+                             "scan_frac": a2 / HBM_PEAK_GBPS, "replicas": m2["replicas"]}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
