@@ -101,11 +101,12 @@ def kv_slots_gpu_quantized(w: synth.Workload, n_slots: int, page_table, device="
     return fp4, sc
 
 
-def build_inputs(w: synth.Workload, kv_fp4=None, kv_scale=None, device="cuda") -> GroupInputs:
+def build_inputs(w: synth.Workload, kv_fp4=None, kv_scale=None, device="cuda", k_idx=None) -> GroupInputs:
     """Device inputs of a workload.  kv_fp4/kv_scale (numpy or tensors) may be
-    given; otherwise they are quantised on the GPU."""
+    given; otherwise they are quantised on the GPU.  k_idx: the indexer keys at
+    their slots when already generated (k_idx_slots_from_synth)."""
     n_slots, page_table, _ = synth.slots_layout(w)
-    kidx = k_idx_slots_from_synth(w, n_slots, page_table)
+    kidx = k_idx_slots_from_synth(w, n_slots, page_table) if k_idx is None else k_idx
     if kv_fp4 is None:
         kv_fp4, kv_scale = kv_slots_gpu_quantized(w, n_slots, page_table, device)
     elif isinstance(kv_fp4, np.ndarray):

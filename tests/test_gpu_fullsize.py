@@ -1,0 +1,102 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (the same inputs, the GPU-quantised main KV, the same group calls), on
+sampled rows the oracle computes one by one: Top-512 indices and candidate
+blocks bit-exact, outputs within 2e-3, and the GPU-quantised main-KV bytes
+equal to the oracle's quantisation at every gathered position."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_02_amd import synth
+from oracle import csa2_oracle as O
+from tests.gpu_util import ATTN_TOL, host, lse_ok, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_caches(w, K):
+    """The oracle's own main KV (quantised by the oracle from the seeded source
+    values) and the indexer keys at their slots."""
+    n_slots, pt, _ = synth.slots_layout(w)
+    if w.raw_fp4:
+        P, S = synth.gen_fp4_raw(w, n_slots)
+    else:
+        P = np.zeros((n_slots, 256), np.uint8)
+        S = np.zeros((n_slots, 32), np.uint8)
+        if w.kv_pool:
+            pp, ps = O.quantize_fp4(synth.gen_kv_pool(w))
+        for b in range(w.B):
+            L = w.seq_lens[b]
+            sl = synth.slot_index(w, pt, b, np.arange(L))
+            if w.kv_pool:
+                m = synth.gen_kv_pool_map(w, b)
+                P[sl], S[sl] = pp[m], ps[m]
+            else:
+                P[sl], S[sl] = O.quantize_fp4(synth.gen_kv_values(w, b, 0, L))
+    return O.Cache(P, S, K, w.seq_lens, pt, 64, 0 if w.paged else w.n_max), P, S, pt
+
+
+def run_fullsize(w, rows):
+    from fp4_kv_cache_02_amd import group
+    n_slots, pt, _ = synth.slots_layout(w)
+    say(w.name, "building inputs, rows checked", rows)
+    K = group.k_idx_slots_from_synth(w, n_slots, pt)
+    inp = group.build_inputs(w, k_idx=K)
+    run = group.GroupRunner(w, inp)
+    cache, P, S, _ = oracle_caches(w, K)
+    gP, gS = host(inp.kv_fp4), host(inp.kv_scale)
+    row_seq = np.zeros(w.R, np.int64) if w.prefill_rows else np.arange(w.R)
+    state = O.GroupState(w.R)
+    for gi, (li0, n) in enumerate(run.groups):
+        say(w.name, "group", gi, w.schedule[li0:li0 + n])
+        run.step_group(gi)
+        torch.cuda.synchronize()
+        for li in range(li0, li0 + n):
+            m = w.schedule[li]
+            k, v, _, st, ln = synth.gen_swa(w, li)
+            qi = synth.gen_q_idx(w, li) if m in "FI" else None
+            q = synth.gen_q(w, li)
+            blocks_only = m == "F" and w.hier and w.full_blocks_only
+            res = O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln, group.SM_SCALE,
+                               hier=w.hier, blocks_only=blocks_only, rows=rows)
+            if m == "F" and w.hier:
+                gc = host(run.cand)
+                for r in rows:
+                    assert np.array_equal(gc[r], state.cand[r]), (w.name, li, r)
+            if blocks_only:
+                continue
+            gt = host(run.topk_idx)
+            go, gl = host(run.out[li]), host(run.lse[li])
+            for r in rows:
+                assert np.array_equal(gt[r], state.topk[r]), (w.name, li, r)
+                b = int(row_seq[r])
+                pos = state.topk[r][state.topk[r] >= 0]
+                sl = O.slot_of(b, pos, pt, 64, 0 if w.paged else w.n_max)
+                assert np.array_equal(gP[sl], P[sl]) and np.array_equal(gS[sl], S[sl]), (w.name, li, r)
+                e = rel_err(go[r], res[r][0])
+                assert np.all(e <= ATTN_TOL), (w.name, li, r, e.max())
+                assert lse_ok(gl[r], res[r][1]), (w.name, li, r)
+
+
+def test_fullsize_cfg1_decode_128k():
+    w = synth.workload(1)
+    run_fullsize(w, list(range(w.R)))
+
+
+def test_fullsize_cfg2_decode_1m():
+    w = synth.workload(2)
+    run_fullsize(w, [0])
+
+
+def test_fullsize_cfg3_prefill():
+    w = synth.workload(3)
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 127, 2048, w.R - 1] + list(rng.choice(w.R, size=5, replace=False))))
+    run_fullsize(w, rows)
+
+
+def test_fullsize_cfg4_mixed_serving():
+    w = synth.workload(4)
+    lens = np.array(w.seq_lens)
+    rows = sorted(set([int(lens.argmax()), int(lens.argmin()), 5, 17]))
+    run_fullsize(w, rows)
