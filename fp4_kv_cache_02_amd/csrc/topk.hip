@@ -98,7 +98,11 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
     }
   }
   CSA2_MARK(a, 9);
-  const SelResult s = block_select(sm, top, K, 0u, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 10 : nullptr);
+  // Above level 0 any threshold at or below the k-th largest value serves
+  // (the descent keeps every child >= it), so the search may stop at the
+  // first bin edge with at most 1.5 k values above it (usually one pass).
+  const uint32_t cap = (T == 0) ? 0u : K + K / 2;
+  const SelResult s = block_select(sm, top, K, cap, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 10 : nullptr);
   CSA2_MARK(a, 1);
   if (T == 0) {
     const uint32_t m = block_compact(sm, top, s, K, [&](uint32_t pos, int e) {
@@ -212,22 +216,26 @@ CSA2_DEV void topk_general(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, in
     // keys to a multiple of kSelPad; every read is in bounds (an absent
     // candidate reads element 0 of the row, which exists when n_elem > 0)
     const int n_pad = sel_padded(n_elem);
-    for (int e0 = tid; e0 < n_pad; e0 += kSelPad) {
-      int64_t src[kSelBatch];
-      bool ok[kSelBatch];
+    // two batches of loads in flight per round trip (n_pad is a multiple of kSelPad)
+    for (int e00 = tid; e00 < n_pad; e00 += 2 * kSelPad) {
+      int64_t src[2 * kSelBatch];
+      bool ok[2 * kSelBatch];
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) {
-        const int e = e0 + j * kSelThreads;
+      for (int j = 0; j < 2 * kSelBatch; ++j) {
+        const int e = e00 + j * kSelThreads;
         const int ec = min(e, max(n_elem - 1, 0));
         const int64_t i = all ? (int64_t)ec : (int64_t)par[cur][ec >> 3] * 8 + (ec & 7);
         ok[j] = e < n_elem && i < n;
         src[j] = ok[j] ? i : 0;
       }
-      float v[kSelBatch];
+      float v[2 * kSelBatch];
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) v[j] = base[src[j]];
+      for (int j = 0; j < 2 * kSelBatch; ++j) v[j] = base[src[j]];
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) sm.key[skew(e0 + j * kSelThreads)] = ok[j] ? order_key(v[j]) : 0u;
+      for (int j = 0; j < 2 * kSelBatch; ++j) {
+        const int e = e00 + j * kSelThreads;
+        if (e < n_pad) sm.key[skew(e)] = ok[j] ? order_key(v[j]) : 0u;
+      }
     }
     __syncthreads();
     const LdsKeys ks{&sm, n_pad};
