@@ -235,9 +235,24 @@ CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int 
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fp4_attn_kernel(AttnArgs a) {
   __shared__ AttnSmem sm;
   // flat grid: block id = (li * R + r) * n_blocks + blk
-  const int blk = blockIdx.x % a.n_blocks;
-  const int lr = blockIdx.x / a.n_blocks;
-  const int li = lr / a.R, r = lr - li * a.R;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so
+  // within each run of 8 rows, row 8q + x takes every id = x (mod 8): all
+  // layers and steps of a row share one XCD's L2 (the gathered rows, the
+  // indices and, for neighbouring prefill rows, the window)
+  const int per = a.n_layers * a.n_blocks;                // blocks of one row
+  const int full = (a.R / 8) * 8 * per;                   // ids in complete runs of 8 rows
+  int r, sub;
+  if ((int)blockIdx.x < full) {
+    const int q = blockIdx.x / (8 * per), rem = blockIdx.x - q * 8 * per;
+    r = 8 * q + (rem & 7);
+    sub = rem >> 3;
+  } else {
+    const int rem = blockIdx.x - full;
+    r = (a.R / 8) * 8 + rem / per;
+    sub = rem - (rem / per) * per;
+  }
+  const int li = sub / a.n_blocks, blk = sub - li * a.n_blocks;
+  const int lr = li * a.R + r;
   const AttnLayer& Ly = a.layer[li];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c = lane & 15, g = lane >> 4;
   const int b = a.row_seq ? a.row_seq[r] : r;
