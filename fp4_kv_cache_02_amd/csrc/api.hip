@@ -96,22 +96,36 @@ int topk_levels_needed(int64_t n) {
 }
 
 struct TopkWs {
-  float* lv1;
-  float* lv2;
+  float* lv1 = nullptr;
+  float* lv2 = nullptr;
+  uint32_t* seg_kth = nullptr;    // large-k path (segment thresholds)
+  int32_t* fail_list = nullptr;
+  uint32_t* fail_count = nullptr;
 };
 
+// Large k over long rows: segment thresholds, then a gather above them.
+bool topk_large_shape(int64_t n_max, int k) { return k >= 1024 && n_max > kSelCapHost && n_max <= kTauMaxN; }
+
+void carve_large(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
+  if (!topk_large_shape(n_max, k)) return;
+  t.seg_kth = bp.take<uint32_t>((size_t)R * cdiv(n_max, kSegLen));
+  t.fail_list = bp.take<int32_t>((size_t)R);
+  t.fail_count = bp.take<uint32_t>(1);
+}
+
 // Workspace for the levels of maxima a generic Top-k must build itself.
-TopkWs carve_topk(Bump& bp, int R, int64_t n_max) {
-  TopkWs t{nullptr, nullptr};
+TopkWs carve_topk(Bump& bp, int R, int64_t n_max, int k) {
+  TopkWs t;
   const int need = topk_levels_needed(n_max);
   if (need >= 1) t.lv1 = bp.take<float>((size_t)R * cdiv(n_max, 8));
   if (need >= 2) t.lv2 = bp.take<float>((size_t)R * cdiv(n_max, 64));
+  carve_large(bp, t, R, n_max, k);
   return t;
 }
 
-size_t topk_region(int R, int64_t n_max) {
+size_t topk_region(int R, int64_t n_max, int k) {
   Bump bp{nullptr, 0};
-  carve_topk(bp, R, n_max);
+  carve_topk(bp, R, n_max, k);
   return bp.off;
 }
 
@@ -135,6 +149,10 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
   a.out_stride = k;
   a.row_list = nullptr;
   a.row_list_count = nullptr;
+  a.seg_kth = nullptr;
+  a.nseg = 0;
+  a.fail_list = nullptr;
+  a.fail_count = nullptr;
   return a;
 }
 
@@ -161,6 +179,13 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
     a.lv[l] = dst;
   }
   CSA2_SET_TRACE(a, 1);
+  if (tw.seg_kth && a.lv[1] && !a.cand_blocks && !a.row_list && topk_large_shape(a.n_max, a.k)) {
+    a.seg_kth = tw.seg_kth;
+    a.nseg = (int32_t)cdiv(a.n_max, kSegLen);
+    a.fail_list = tw.fail_list;
+    a.fail_count = tw.fail_count;
+    return hip_status(launch_topk_large(a, st));
+  }
   return hip_status(launch_topk(a, st));
 }
 
@@ -277,6 +302,10 @@ size_t index_region(csa2_mode mode, int R, int n_max, int hier) {
     bp.take<float>((size_t)R * cdiv(n_max, 8));
     bp.take<float>((size_t)R * cdiv(n_max, 64));
     if (prefill_shape(mode, R, n_max, hier)) carve_prefill(bp, R, n_max);
+    if (mode == CSA2_FULL && hier) {
+      TopkWs t;
+      carve_large(bp, t, R, cdiv(n_max, 8), CSA2_KEEP_BLOCKS);
+    }
   } else if (mode == CSA2_REINDEX) {
     bp.take<float>((size_t)R * CSA2_KEEP_BLOCKS * 8);
   }
@@ -348,7 +377,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       t.lv[2] = m64;
       t.row_list = pw.fb_list;
       t.row_list_count = pw.fb_count;
-      return run_topk(t, TopkWs{nullptr, nullptr}, st);
+      return run_topk(t, TopkWs{}, st);
     }
     s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max, scores,
                        bmax, m64, st);
@@ -357,15 +386,17 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       TopkArgs t = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
       t.lv[1] = bmax;
       t.lv[2] = m64;
-      s = run_topk(t, TopkWs{nullptr, nullptr}, st);
+      s = run_topk(t, TopkWs{}, st);
       if (s) return s;
     }
     if (mode == CSA2_FULL && sh->hier) {
       const int nb = (int)cdiv(n_max, 8);
+      TopkWs tw;
+      carve_large(bp, tw, R, nb, CSA2_KEEP_BLOCKS);
       TopkArgs t = topk_args(bmax, nb, a->row_seq, sh->seq_len, 8, R, nb, CSA2_KEEP_BLOCKS, sh->cand_blocks);
       t.lv[1] = m64;     // maxima of 8 block maxima
       t.lv_stride[1] = cdiv(n_max, 64);
-      s = run_topk(t, TopkWs{nullptr, nullptr}, st);
+      s = run_topk(t, tw, st);
       if (s) return s;
     }
     return CSA2_OK;
@@ -379,7 +410,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
   TopkArgs t = topk_args(scores, nc, nullptr, nullptr, 1, R, nc, CSA2_TOPK, sh->topk_idx);
   t.cand_blocks = sh->cand_blocks;
   t.cand_stride = CSA2_KEEP_BLOCKS;
-  return run_topk(t, TopkWs{nullptr, nullptr}, st);
+  return run_topk(t, TopkWs{}, st);
 }
 
 csa2_status check_shared(const csa2_shared* sh, int R) {
@@ -426,7 +457,7 @@ csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
 
 size_t csa2_topk_workspace_bytes(int32_t R, int32_t n_max, int32_t k) {
   if (R < 0 || n_max < 0 || k < 1) return 0;
-  return kCtrlBytes + topk_region(R, n_max);
+  return kCtrlBytes + topk_region(R, n_max, k);
 }
 
 size_t csa2_attn_workspace_bytes(int32_t R) {
@@ -464,7 +495,7 @@ csa2_status csa2_topk(const float* scores, int64_t row_stride, const int32_t* ro
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_topk_workspace_bytes(R, n_max, k)) return CSA2_ERR_WORKSPACE;
   Bump bp{(char*)ws, kCtrlBytes};
-  const TopkWs tw = carve_topk(bp, R, n_max);
+  const TopkWs tw = carve_topk(bp, R, n_max, k);
   TopkArgs t = topk_args(scores, row_stride, row_seq, n_valid, 1, R, n_max, k, idx);
   t.cand_blocks = cand_blocks;
   t.cand_stride = n_max / 8;
@@ -481,7 +512,7 @@ csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq,
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_topk_workspace_bytes(R, nb, keep)) return CSA2_ERR_WORKSPACE;
   Bump bp{(char*)ws, kCtrlBytes};
-  const TopkWs tw = carve_topk(bp, R, nb);
+  const TopkWs tw = carve_topk(bp, R, nb, keep);
   return run_topk(topk_args(block_max, nb, row_seq, seq_len, 8, R, nb, keep, cand_blocks), tw, stream);
 }
 

@@ -44,8 +44,17 @@ struct TopkArgs {
   int32_t out_stride;
   const int32_t* row_list;    // optional: select only rows row_list[0 .. *row_list_count)
   const uint32_t* row_list_count;
+  // large-k path (segment thresholds): per (row, segment) k-th largest keys,
+  // and the rows it hands to the general path
+  uint32_t* seg_kth;          // [R][nseg] or null
+  int32_t nseg;
+  int32_t* fail_list;         // [R]
+  uint32_t* fail_count;       // [1]
   CSA2_TRACE_ARG
 };
+
+constexpr int kSegLen = 8192;             // level-0 values per segment of the large-k path
+constexpr int kTauMaxN = 131072;          // level-0 values per row it handles (8 x 16384)
 
 // Prefill-chunk indexer on MFMA: every query row sees the positions of one
 // sequence (sequence 0).
@@ -119,6 +128,7 @@ struct AttnArgs {
 
 hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxima, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st);
 hipError_t launch_maxima(const MaximaArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,

@@ -290,6 +290,180 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
   CSA2_MARK(a, 8);
 }
 
+
+// ---- large k over a long row (the 2048 candidate blocks of a hierarchical
+// indexer at up to 1M positions) ----
+//
+// seg_kth_kernel, grid (segments, rows): segment s of kSegLen level-0 values
+// (n_s of the row's n0) takes a key t_s with at least m_s = ceil(k n_s / n0)
+// of its values >= t_s (a bin edge near its m_s-th largest; 0 when it holds at
+// most m_s present values; all-ones for an empty segment).  Their minimum tau has at least m_s values >= tau in every
+// segment, sum m_s >= k of them in the row, so the row's k-th largest value
+// is >= tau and the row's top k lie among the values >= tau -- typically a
+// little more than k values, and only those are gathered.
+// topk_tau_kernel, one block per row: level-1 groups >= tau, their level-0
+// children >= tau (in index order), the exact top k of those.  A row whose
+// survivors exceed the block's capacity is listed for the general path.
+
+constexpr int kTauL1Cap = 8192;           // level-1 groups >= tau
+constexpr int kTauCap = 8192;             // level-0 values >= tau
+constexpr int kTauJ = 32;                 // level-0 elements per thread per round
+constexpr int kTauRound = kTauJ * kSelThreads;
+constexpr int kTauKeyWords = kTauCap + kTauCap / 32;
+static_assert(kSegLen == 2 * kSelPad, "a segment is two LDS key batches");
+static_assert(kTauMaxN / 8 <= 32 * kSelThreads, "level 1 is 32 values per thread");
+
+__global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
+  __shared__ SelSmemT<kSegLen + kSegLen / 32> sm;
+  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  if (s == 0 && r == 0 && tid == 0) *a.fail_count = 0u;
+  const int64_t n0 = row_count(a, r);
+  const int64_t lo = (int64_t)s * kSegLen;
+  const int n = (int)max((int64_t)0, min(n0 - lo, (int64_t)kSegLen));
+  if (n == 0) {
+    if (tid == 0) a.seg_kth[(int64_t)r * a.nseg + s] = 0xFFFFFFFFu;
+    return;
+  }
+  const uint32_t m_s = (uint32_t)(((int64_t)a.k * n + n0 - 1) / n0);
+  const float* base = a.lv[0] + (int64_t)r * a.lv_stride[0] + lo;
+  float v[kSegLen / kSelThreads];
+#pragma unroll
+  for (int j = 0; j < kSegLen / kSelThreads; ++j) v[j] = base[min(tid + j * kSelThreads, n - 1)];
+#pragma unroll
+  for (int j = 0; j < kSegLen / kSelThreads; ++j) {
+    const int e = tid + j * kSelThreads;
+    sm.key[skew(e)] = e < n ? order_key(v[j]) : 0u;
+  }
+  __syncthreads();
+  const LdsKeysT<SelSmemT<kSegLen + kSegLen / 32>> ks{&sm, kSegLen};
+  // any key with at least m_s values at or above it serves: stop at the first
+  // bin edge with at most 2 m_s above it
+  const SelResult res = block_select(sm, ks, m_s, 2u * m_s);
+  if (tid == 0) a.seg_kth[(int64_t)r * a.nseg + s] = res.T;
+}
+
+struct TauSmem {
+  SelSmemT<kTauKeyWords> sel;     // level-0 survivors' keys
+  int32_t l1[kTauL1Cap];          // level-1 survivors
+  int32_t idx0[kTauCap];          // level-0 survivors' indices
+  uint32_t cnt[kTauJ * kSelWaves];
+  uint32_t off[kTauJ * kSelWaves];
+};
+static_assert(kTauJ * kSelWaves <= kSelThreads, "one ballot count per thread in the scan");
+
+__global__ __launch_bounds__(kSelThreads) void topk_tau_kernel(TopkArgs a) {
+  __shared__ TauSmem sm;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const uint32_t K = (uint32_t)a.k;
+  int32_t* out = a.out + (int64_t)r * a.out_stride;
+  const int64_t n0 = row_count(a, r);
+  if (n0 == 0) {
+    for (int i = tid; i < a.k; i += kSelThreads) out[i] = -1;
+    return;
+  }
+  CSA2_MARK(a, 20);
+  // nseg <= 64: one value per lane, minimum over the wave (every wave alike)
+  const int lane = tid & 63;
+  uint32_t tau = lane < a.nseg ? a.seg_kth[(int64_t)r * a.nseg + lane] : 0xFFFFFFFFu;
+  tau = max(wave_min_u32(tau), 1u);
+
+  // ---- level 1: thread t owns groups 32t .. 32t+31 ----
+  const int64_t n1 = (n0 + 7) / 8;
+  const float* b1 = a.lv[1] + (int64_t)r * a.lv_stride[1];
+  float v1[32];
+  if (((uintptr_t)b1 & 15u) == 0 && 32 * tid + 32 <= n1) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 x = *(const float4*)(b1 + 32 * tid + 4 * q);
+      v1[4 * q] = x.x; v1[4 * q + 1] = x.y; v1[4 * q + 2] = x.z; v1[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v1[j] = b1[min((int64_t)(32 * tid + j), n1 - 1)];
+  }
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    keep |= (32 * tid + j < n1 && order_key(v1[j]) >= tau) ? (1u << j) : 0u;
+  CSA2_MARK(a, 21);
+  uint32_t n_l1;
+  uint32_t pos = block_excl_scan(sm.sel, (uint32_t)__popc(keep), n_l1);
+  bool fail = n_l1 > (uint32_t)kTauL1Cap;
+  if (!fail) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if ((keep >> j) & 1u) sm.l1[pos++] = 32 * tid + j;
+  }
+  __syncthreads();
+
+  // ---- level 0: the children of the level-1 survivors, element e = 8 i + c
+  // (child c of survivor i).  A round covers kTauRound elements; thread t
+  // takes e = t + 512 j, so the 8 lanes of a survivor read its 32 contiguous
+  // bytes together and every load of the round is in flight at once.  Order-
+  // preserving compaction: per (j, wave) ballot counts, one block scan over
+  // them in (j, wave) order = element order, then each lane's rank in its
+  // ballot. ----
+  const float* b0 = a.lv[0] + (int64_t)r * a.lv_stride[0];
+  const int lane_w = tid & 63, wv = tid >> 6;
+  const uint64_t lt_mask = (1ull << lane_w) - 1ull;
+  uint32_t n_sv = 0u;
+  for (uint32_t base = 0; !fail && base < 8u * n_l1; base += kTauRound) {
+    float v[kTauJ];
+    int64_t ix[kTauJ];
+#pragma unroll
+    for (int j = 0; j < kTauJ; ++j) {
+      const uint32_t e = base + tid + kSelThreads * j;
+      const bool ok = e < 8u * n_l1;
+      const int64_t i = ok ? (int64_t)sm.l1[e >> 3] * 8 + (e & 7) : -1;
+      ix[j] = (i >= 0 && i < n0) ? i : -1;
+      v[j] = b0[ix[j] >= 0 ? ix[j] : 0];
+    }
+    uint64_t m[kTauJ];
+#pragma unroll
+    for (int j = 0; j < kTauJ; ++j) {
+      m[j] = __ballot(ix[j] >= 0 && order_key(v[j]) >= tau);
+      if (lane_w == 0) sm.cnt[j * kSelWaves + wv] = (uint32_t)__popcll(m[j]);
+    }
+    __syncthreads();
+    uint32_t tot;
+    const uint32_t off = block_excl_scan(sm.sel, tid < kTauJ * kSelWaves ? sm.cnt[tid] : 0u, tot);
+    if (tid < kTauJ * kSelWaves) sm.off[tid] = off;
+    __syncthreads();
+    if (n_sv + tot > (uint32_t)kTauCap) {
+      fail = true;
+      break;
+    }
+#pragma unroll
+    for (int j = 0; j < kTauJ; ++j)
+      if ((m[j] >> lane_w) & 1ull) {
+        const uint32_t p = n_sv + sm.off[j * kSelWaves + wv] + (uint32_t)__popcll(m[j] & lt_mask);
+        sm.sel.key[skew((int)p)] = order_key(v[j]);
+        sm.idx0[p] = (int32_t)ix[j];
+      }
+    n_sv += tot;
+    __syncthreads();
+    CSA2_MARK(a, 22 + min(base / kTauRound, 3u));
+  }
+  if (fail) {
+    if (tid == 0) a.fail_list[atomicAdd(a.fail_count, 1u)] = r;
+    return;
+  }
+  const int n_pad = sel_padded((int)n_sv);
+  for (int e = (int)n_sv + tid; e < n_pad; e += kSelThreads) sm.sel.key[skew(e)] = 0u;
+  __syncthreads();
+  const LdsKeysT<SelSmemT<kTauKeyWords>> ks{&sm.sel, n_pad};
+  const SelResult res = block_select(sm.sel, ks, K, 0u, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 64 : nullptr);
+  CSA2_MARK(a, 26);
+  const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) { out[o] = sm.idx0[e]; });
+  for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
+  CSA2_MARK(a, 27);
+  if (CSA2_TRACE_PTR(a) && tid == 0 && blockIdx.x == 0) {
+    CSA2_TRACE_PTR(a)[28] = n_l1;
+    CSA2_TRACE_PTR(a)[29] = n_sv;
+    CSA2_TRACE_PTR(a)[30] = tau;
+  }
+}
+
 // out[r][g] = maximum (in the Top-k order) of in[r][8g .. 8g+7] below the
 // row's count, -inf when none is present.  The row's count at this level is
 // ceil(n0 / div) with n0 the level-0 count of the row.
@@ -317,6 +491,20 @@ __global__ __launch_bounds__(256) void maxima_kernel(MaximaArgs a) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// Large k over rows of at most kTauMaxN values with level 1 stored: segment
+// thresholds, the threshold gather, then the general path for listed rows.
+hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st) {
+  if (a.R == 0) return hipSuccess;
+  hipLaunchKernelGGL(seg_kth_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(topk_tau_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
+  TopkArgs f = a;
+  f.row_list = a.fail_list;
+  f.row_list_count = a.fail_count;
+  f.seg_kth = nullptr;
+  hipLaunchKernelGGL(topk_kernel, dim3(a.R), dim3(kSelThreads), 0, st, f);
   return hipGetLastError();
 }
 

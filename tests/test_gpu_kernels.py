@@ -144,7 +144,7 @@ def _topk_case(rng, kind, n):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("k", [1, 7, 512, 2048])
+@pytest.mark.parametrize("k", [1, 7, 512, 1024, 2048])
 def test_topk_bitexact(C, k):
     rng = np.random.default_rng(400 + k)
     kinds = ["normal", "ties", "zeros", "equal", "clustered", "neginf"]
