@@ -53,7 +53,6 @@ constexpr int kPChunk = 2048;               // positions per workgroup
 constexpr int kPStage = 128;                // positions per LDS stage
 constexpr int kPGroup = 64;                 // positions per gmax group
 constexpr int kPGroupsWG = kPChunk / kPGroup;
-constexpr int kPLdsCand = 32;               // candidates per row buffered in LDS (pass 1)
 
 // DPP lane patterns inside a row of 16 lanes
 #define PF_DPP(v, ctrl) \
@@ -82,9 +81,9 @@ CSA2_DEV float row16_sum(float v) {
 struct PassSmem {
   uint4 keys[kPStage * 8];            // chunk c of stage position p at p*8 + (c ^ (p & 7))
   uint32_t present[kPStage + kPWaves * 64];   // [kPStage, ...): sink of the non-writing lanes
-  uint32_t cnt[kPRows];               // pass 1: candidates found per row
-  uint32_t base[kPRows];
-  int32_t buf[kPRows][kPLdsCand];
+  uint32_t bm[kPRows][kPChunk / 32];  // pass 1: candidate bitmap (row, position in the chunk)
+  uint32_t qcnt[kPWaves * 64];        // pass 1 flush: candidates per (row, quarter of the chunk)
+  uint32_t rowbase[kPRows];
   uint32_t kmax[kPWaves];
   uint64_t act[kPWaves][kPGroupsWG / 4];
 };
@@ -147,7 +146,7 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
       const uint64_t bits = __ballot(gm >= t);
       if (lane == 0) sm.act[wave][i] = bits;
     }
-    if (tid < kPRows) sm.cnt[tid] = 0u;
+    for (int i = tid; i < kPRows * kPChunk / 32; i += kPWaves * 64) (&sm.bm[0][0])[i] = 0u;
   }
 
   const bool want_kmax = PASS == 0 && blockIdx.y == 0;
@@ -198,46 +197,50 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
     for (int nt = 0; nt < kPStage / 16; ++nt) {
       const int pl = 16 * nt + c;
       const int grp_wg = (s * kPStage + 16 * nt) / kPGroup;     // group within the workgroup
-      uint32_t tiles = 0xFu;
       if (PASS == 1) {
+        // skip the 16 positions when none of the wave's 16 rows can hold a
+        // candidate in this group (all four tiles are computed otherwise: the
+        // eight MFMAs issue back to back)
         const uint32_t bits = (uint32_t)(sm.act[wave][grp_wg >> 2] >> (16 * (grp_wg & 3))) & 0xFFFFu;
-        tiles = (bits & 0xFu ? 1u : 0u) | (bits & 0xF0u ? 2u : 0u) | (bits & 0xF00u ? 4u : 0u) |
-                (bits & 0xF000u ? 8u : 0u);
-        tiles = __builtin_amdgcn_readfirstlane(tiles);
-        if (!tiles) continue;
+        if (!__builtin_amdgcn_readfirstlane(bits)) continue;
       }
       const uint4 b0 = sm.keys[pl * 8 + (g ^ (pl & 7))];
       const uint4 b1 = sm.keys[pl * 8 + ((4 + g) ^ (pl & 7))];
       const bool pres = sm.present[pl] != 0u;
       const int64_t pos = x0 + (int64_t)s * kPStage + pl;
+      f32x4_t acc[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        if (!(tiles & (1u << mt))) continue;
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][0], to_bf16x8(b0), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][1], to_bf16x8(b1), acc, 0, 0, 0);
-        const float r0 = fmaxf(acc[0], 0.0f), r1 = fmaxf(acc[1], 0.0f);
-        const float r2 = fmaxf(acc[2], 0.0f), r3 = fmaxf(acc[3], 0.0f);
+        acc[mt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][0], to_bf16x8(b0), acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][1], to_bf16x8(b1), acc[mt], 0, 0, 0);
+      }
+      bool hit[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float r0 = fmaxf(acc[mt][0], 0.0f), r1 = fmaxf(acc[mt][1], 0.0f);
+        const float r2 = fmaxf(acc[mt][2], 0.0f), r3 = fmaxf(acc[mt][3], 0.0f);
         float sc;
         if (HAS_W)
           sc = (w[mt][0] * r0 + w[mt][1] * r1) + (w[mt][2] * r2 + w[mt][3] * r3);
         else
           sc = (r0 + r1) + (r2 + r3);
-        if (PASS == 0) {
-          gm[mt] = fmaxf(gm[mt], pres ? sc : -__builtin_inff());
-        } else {
-          const bool hit = pres && orow[mt] < a.R && sc >= th[mt];
-          if (__ballot(hit)) {
-            if (hit) {
-              const int rl = 16 * wave + 4 * mt + g;
-              const uint32_t slot = atomicAdd(&sm.cnt[rl], 1u);
-              if (slot < (uint32_t)kPLdsCand) {
-                sm.buf[rl][slot] = (int32_t)pos;
-              } else {
-                const uint32_t gs = atomicAdd(&a.cand_count[orow[mt]], 1u);
-                if (gs < (uint32_t)a.cap) a.cand[(int64_t)orow[mt] * a.cap + gs] = (int32_t)pos;
-              }
-            }
+        if (PASS == 0) gm[mt] = fmaxf(gm[mt], pres ? sc : -__builtin_inff());
+        hit[mt] = PASS == 1 && pres && orow[mt] < a.R && sc >= th[mt];
+      }
+      if (PASS == 1) {
+        // hits as bits: lane (c, g) of tile mt is position 16 nt + c of row
+        // 16 wave + 4 mt + g; one LDS OR (no return value, no wait) per row
+        uint64_t mm[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) mm[mt] = __ballot(hit[mt]);
+        if ((mm[0] | mm[1] | mm[2] | mm[3]) != 0ull && c == 0) {
+          const int word = (s * kPStage + 16 * nt) >> 5;
+          const uint32_t sh = 16u * (uint32_t)(nt & 1);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const uint32_t bits = (uint32_t)(mm[mt] >> (16 * g)) & 0xFFFFu;
+            if (bits) atomicOr(&sm.bm[16 * wave + 4 * mt + g][word], bits << sh);
           }
         }
       }
@@ -266,20 +269,34 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 #undef PF_LOAD_STAGE
 #undef PF_LOAD1
   if (PASS == 1) {
-    // flush the LDS candidates: one global reservation per row
+    // flush the bitmap: thread t takes row t / 4, words 16 (t % 4) .. +15;
+    // one global reservation per row, positions written in increasing order
     __syncthreads();
-    if (tid < kPRows) {
-      const int row = blockIdx.y * kPRows + tid;
-      const uint32_t n = min(sm.cnt[tid], (uint32_t)kPLdsCand);
-      sm.base[tid] = (n && row < a.R) ? atomicAdd(&a.cand_count[row], n) : 0u;
+    const int rl = tid >> 2, q = tid & 3;
+    const int row = blockIdx.y * kPRows + rl;
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cnt += (uint32_t)__popc(sm.bm[rl][16 * q + i]);
+    sm.qcnt[tid] = cnt;
+    __syncthreads();
+    uint32_t pre = 0u, tot = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = sm.qcnt[4 * rl + i];
+      pre += i < q ? v : 0u;
+      tot += v;
     }
+    if (q == 0) sm.rowbase[rl] = (tot && row < a.R) ? atomicAdd(&a.cand_count[row], tot) : 0u;
     __syncthreads();
-    for (int i = tid; i < kPRows * kPLdsCand; i += kPWaves * 64) {
-      const int rl = i / kPLdsCand, e = i % kPLdsCand;
-      const int row = blockIdx.y * kPRows + rl;
-      const uint32_t n = min(sm.cnt[rl], (uint32_t)kPLdsCand);
-      const uint32_t dst = sm.base[rl] + (uint32_t)e;
-      if (row < a.R && (uint32_t)e < n && dst < (uint32_t)a.cap) a.cand[(int64_t)row * a.cap + dst] = sm.buf[rl][e];
+    uint32_t dst = sm.rowbase[rl] + pre;
+    for (int i = 0; i < 16 && cnt; ++i) {
+      uint32_t wbits = sm.bm[rl][16 * q + i];
+      while (wbits) {
+        const int bit = __ffs(wbits) - 1;
+        wbits &= wbits - 1u;
+        if (dst < (uint32_t)a.cap) a.cand[(int64_t)row * a.cap + dst] = (int32_t)(x0 + 32 * (16 * q + i) + bit);
+        ++dst;
+      }
     }
   }
 }
@@ -450,11 +467,20 @@ __global__ __launch_bounds__(kSelThreads) void pref_select_kernel(PrefArgs a) {
   for (int e = (int)n + tid; e < n_pad; e += kSelThreads) sm.sel.key[skew(e)] = 0u;
   __syncthreads();
 
-  // ---- exact Top-k in position order
-  const LdsKeysT<SelSmemT<kPSelKeyWords>> ks{&sm.sel, n_pad};
-  const SelResult res = block_select(sm.sel, ks, (uint32_t)a.k, 0u);
-  const uint32_t kept = block_compact(sm.sel, ks, res, (uint32_t)a.k,
-                                      [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
+  // ---- exact Top-k in position order (keys in registers when they fit)
+  uint32_t kept;
+  if (n <= (uint32_t)kRegCap) {
+    RegKeys rk;
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) rk.v[j] = sm.sel.key[skew(kRegPer * tid + j)];
+    __syncthreads();
+    const SelResult res = block_select(sm.sel, rk, (uint32_t)a.k, 0u);
+    kept = block_compact(sm.sel, rk, res, (uint32_t)a.k, [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
+  } else {
+    const LdsKeysT<SelSmemT<kPSelKeyWords>> ks{&sm.sel, n_pad};
+    const SelResult res = block_select(sm.sel, ks, (uint32_t)a.k, 0u);
+    kept = block_compact(sm.sel, ks, res, (uint32_t)a.k, [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
+  }
   for (int i = (int)kept + tid; i < a.k; i += kSelThreads) out[i] = -1;
 }
 
