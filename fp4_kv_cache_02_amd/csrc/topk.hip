@@ -125,9 +125,9 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
   for (int l = T - 1; l >= 0; --l) {
     const float* base = a.lv[l] + (int64_t)r * a.lv_stride[l];
     const int64_t n = nl[l];
-    // children of this thread's parents kRegPer*t .. +kRegPer-1: two 16-byte
-    // loads per parent when the row is 16-byte aligned and the group is whole
-    const bool al16 = ((uintptr_t)base & 15u) == 0;
+    // children of this thread's parents kRegPer*t .. +kRegPer-1; every load
+    // is unconditional (clamped index) so all of them are in flight at once
+    // (a load under a branch is waited for before the next branch)
     int64_t idx[kRegPer * 8];
     float v[kRegPer * 8];
 #pragma unroll
@@ -136,15 +136,9 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
       const int64_t g = (pi < n_par) ? (int64_t)par[cur][pi] : -1;
 #pragma unroll
       for (int c = 0; c < 8; ++c) idx[8 * p + c] = (g >= 0 && g * 8 + c < n) ? g * 8 + c : -1;
-      if (g >= 0 && al16 && g * 8 + 8 <= n) {
-        const float4 x = *(const float4*)(base + g * 8), y = *(const float4*)(base + g * 8 + 4);
-        v[8 * p + 0] = x.x; v[8 * p + 1] = x.y; v[8 * p + 2] = x.z; v[8 * p + 3] = x.w;
-        v[8 * p + 4] = y.x; v[8 * p + 5] = y.y; v[8 * p + 6] = y.z; v[8 * p + 7] = y.w;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[8 * p + c] = base[idx[8 * p + c] >= 0 ? idx[8 * p + c] : 0];
-      }
     }
+#pragma unroll
+    for (int j = 0; j < kRegPer * 8; ++j) v[j] = base[idx[j] >= 0 ? idx[j] : 0];
     uint32_t cnt = 0;
     uint32_t keepm = 0;           // bit j: child j kept
 #pragma unroll
