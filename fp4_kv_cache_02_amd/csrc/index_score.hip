@@ -83,10 +83,14 @@ CSA2_DEV StepGeo step_geo(const IdxArgs& a, uint32_t item, int g) {
 }
 
 // The 16-byte chunk j of the key of position i of the group (slot 0 stands
-// in for absent positions: every load is unconditional and in bounds).
+// in for absent positions: every load is unconditional and in bounds).  The
+// keys are streamed once per scan: non-temporal loads (measured ~10 % faster
+// than ordinary ones at 8 x 128K positions).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 CSA2_DEV uint4 key_chunk(const uint4* __restrict__ kd, const StepGeo& s, int i, int j) {
   const int64_t slot = (i < s.nv) ? s.s0 + i : 0;
-  return kd[slot * 8 + j];
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)&kd[slot * 8 + j]);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 template <bool CAND, bool HAS_W, bool MAXIMA, bool PERSIST>
