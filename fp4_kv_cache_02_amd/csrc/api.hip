@@ -428,8 +428,9 @@ csa2_status check_shared(const csa2_shared* sh, int R) {
 extern "C" {
 
 #ifdef CSA2_TRACE
-// Tuning builds only: device buffers that receive phase timestamps of the
-// scan (0), Top-k (1) and attention (2) kernels; NULL stops recording.
+// Tuning builds only: device buffers (2048 uint64 each) that receive phase
+// timestamps and per-block spans of the scan (0), Top-k (1) and attention (2)
+// kernels; NULL stops recording.
 void csa2_trace_set(int which, uint64_t* dev_buf) {
   if (which >= 0 && which < 3) g_trace[which] = dev_buf;
 }

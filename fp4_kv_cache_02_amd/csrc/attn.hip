@@ -264,6 +264,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int wst = Ly.swa_start[r];
   const int wl = min(Ly.swa_len[r], CSA2_MAX_WINDOW);
   CSA2_MARK(a, 0);
+  CSA2_SPAN(a, 256, 0);
 
   RowState st;
 #pragma unroll
@@ -280,11 +281,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     // query of the row into LDS: fp16 for main steps, bf16 for the window
     // step (the previous step ended with a barrier)
     if (step == st0 || !is_main) {
+      // all four loads first, then per-word selects (a select of whole uint4s
+      // becomes a branch per load, each waiting for its load)
+      uint4 qv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];   // uint4 e: head e / 64, piece e % 64
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = tid + 256 * i;          // uint4 index: head e / 64, piece e % 64
-        const uint4 v = qsrc[e];
-        sm.q[(e >> 6) * kQRow + (e & 63)] = is_main ? bf16x8_to_f16x8(v) : v;
+        const int e = tid + 256 * i;
+        const uint4 h = bf16x8_to_f16x8(qv[i]);
+        sm.q[(e >> 6) * kQRow + (e & 63)] = make_uint4(is_main ? h.x : qv[i].x, is_main ? h.y : qv[i].y,
+                                                       is_main ? h.z : qv[i].z, is_main ? h.w : qv[i].w);
       }
     }
     // ---- keys of this wave: 32w .. 32w+31 of the step ----
@@ -427,6 +434,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       if (Ly.lse && w == 0 && c == 0)
         Ly.lse[(int64_t)r * 16 + h] = (st.l[i] > 0.f) ? st.m[i] + __logf(st.l[i]) : -__builtin_inff();
     }
+    CSA2_SPAN(a, 256, 1);
     return;
   }
   const int64_t pidx = (int64_t)lr * a.n_blocks + blk;
@@ -442,30 +450,34 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
   }
   CSA2_MARK(a, 5);
+  CSA2_SPAN(a, 256, 1);
 }
 
-// One block per (layer, row): out = sum_j w_j O_j / sum_j w_j l_j with
-// w_j = exp(m_j - max_j m_j), the partials of the row's blocks merged as one
-// softmax; lse = max + log(sum).
+// One block per (layer, row, quarter of the heads): out = sum_j w_j O_j /
+// sum_j w_j l_j with w_j = exp(m_j - max_j m_j), the partials of the row's
+// blocks merged as one softmax; lse = max + log(sum).  Block id = quarter *
+// (layers x rows) + layer * R + row.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int lr = blockIdx.x;                 // li * R + r
+  const int nlr = a.n_layers * a.R;
+  const int hq = blockIdx.x / nlr, lr = blockIdx.x - hq * nlr;   // lr = li * R + r
   const int li = lr / a.R, r = lr - li * a.R;
   const AttnLayer& Ly = a.layer[li];
-  const int tid = threadIdx.x, th = tid >> 4, tc = tid & 15;
+  const int tid = threadIdx.x, th = 4 * hq + (tid >> 6), tc = tid & 63;   // head th, dims 8tc .. 8tc+7
   const int64_t prow = (int64_t)lr * a.n_blocks;
   CSA2_MARK(a, 16);
+  CSA2_SPAN(a, 1280, 0);
   // every load is unconditional (blocks past n_blocks re-read the last one
   // and get weight 0), so all of them are in flight at once
   float mj[kMaxAttnBlocks], lj[kMaxAttnBlocks];
-  float4 v[kMaxAttnBlocks][8];
+  float4 v[kMaxAttnBlocks][2];
 #pragma unroll
   for (int j = 0; j < kMaxAttnBlocks; ++j) {
     const int64_t pj = prow + min(j, a.n_blocks - 1);
     mj[j] = a.part_ml[pj * 32 + th * 2 + 0];
     lj[j] = a.part_ml[pj * 32 + th * 2 + 1];
-    const float* po = a.part_o + pj * (16 * 512) + th * 512 + tc * 32;
-#pragma unroll
-    for (int q4 = 0; q4 < 8; ++q4) v[j][q4] = *(const float4*)(po + 4 * q4);
+    const float* po = a.part_o + pj * (16 * 512) + th * 512 + tc * 8;
+    v[j][0] = *(const float4*)po;
+    v[j][1] = *(const float4*)(po + 4);
   }
   float M = -__builtin_inff();
 #pragma unroll
@@ -477,13 +489,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     wj[j] = (j >= a.n_blocks || mj[j] == -__builtin_inff()) ? 0.f : __expf(mj[j] - M);
     Lsum += wj[j] * lj[j];
   }
-  float4 acc[8];
+  float4 acc[2];
 #pragma unroll
-  for (int q4 = 0; q4 < 8; ++q4) acc[q4] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q4 = 0; q4 < 2; ++q4) acc[q4] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < kMaxAttnBlocks; ++j) {
 #pragma unroll
-    for (int q4 = 0; q4 < 8; ++q4) {
+    for (int q4 = 0; q4 < 2; ++q4) {
       acc[q4].x += wj[j] * v[j][q4].x;
       acc[q4].y += wj[j] * v[j][q4].y;
       acc[q4].z += wj[j] * v[j][q4].z;
@@ -491,12 +503,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     }
   }
   const float inv = (Lsum > 0.f) ? 1.0f / Lsum : 0.f;
-  float* out_row = Ly.out + ((int64_t)r * 16 + th) * 512 + tc * 32;
+  float* out_row = Ly.out + ((int64_t)r * 16 + th) * 512 + tc * 8;
 #pragma unroll
-  for (int q4 = 0; q4 < 8; ++q4)
+  for (int q4 = 0; q4 < 2; ++q4)
     *(float4*)(out_row + 4 * q4) = make_float4(acc[q4].x * inv, acc[q4].y * inv, acc[q4].z * inv, acc[q4].w * inv);
   if (Ly.lse && tc == 0) Ly.lse[(int64_t)r * 16 + th] = (Lsum > 0.f) ? M + __logf(Lsum) : -__builtin_inff();
   CSA2_MARK(a, 18);
+  CSA2_SPAN(a, 1280, 1);
 }
 
 int attn_steps(int k) { return (k + kStepKeys - 1) / kStepKeys + 1; }
@@ -515,7 +528,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(fp4_attn_kernel, dim3(a.n_blocks * a.R * a.n_layers), dim3(kAttnWaves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_blocks == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_layers * a.R), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(4 * a.n_layers * a.R), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

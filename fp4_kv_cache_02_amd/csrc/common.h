@@ -106,7 +106,17 @@ CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
     }                                                                                            \
   } while (0)
 #define CSA2_TRACE_PTR(a) (a).trace
+// per-block start (i = 0) and end (i = 1) times of a 1-D grid at slots
+// base + 2 * block + i of a 2048-slot trace buffer
+#define CSA2_SPAN(a, base, i)                                                                     \
+  do {                                                                                            \
+    if ((a).trace && threadIdx.x == 0 && blockIdx.y == 0 && (base) + 2 * blockIdx.x + 1 < 2048)   \
+      (a).trace[(base) + 2 * blockIdx.x + (i)] = wall_clock64();                                  \
+  } while (0)
 #else
+#define CSA2_SPAN(a, base, i) \
+  do {                        \
+  } while (0)
 #define CSA2_TRACE_ARG
 #define CSA2_MARK(a, i) \
   do {                  \

@@ -36,6 +36,21 @@ CSA2_DEV int64_t row_count(const TopkArgs& a, int r) {
 }
 
 
+// Level l's values of row r, and the number of values of level l over n0
+// level-0 values (selects, not an indexed array: a runtime index into an
+// array of the kernel's arguments or of locals is served from scratch memory).
+CSA2_DEV const float* lv_row(const TopkArgs& a, int l, int r) {
+  // the three row bases first, then the choice: a choice between two loads
+  // would be folded into one load at a runtime offset
+  const float* b0 = a.lv[0] ? a.lv[0] + (int64_t)r * a.lv_stride[0] : nullptr;
+  const float* b1 = a.lv[1] ? a.lv[1] + (int64_t)r * a.lv_stride[1] : nullptr;
+  const float* b2 = a.lv[2] ? a.lv[2] + (int64_t)r * a.lv_stride[2] : nullptr;
+  return (l == 0) ? b0 : (l == 1) ? b1 : b2;
+}
+CSA2_DEV int64_t lv_count(int64_t n0, int l) {
+  return (l == 0) ? n0 : (l == 1) ? (n0 + 7) / 8 : (l == 2) ? (n0 + 63) / 64 : (n0 + 511) / 512;
+}
+
 // Threshold path.  tau = the k-th largest value of the top level T (the
 // lowest level with at most kRegCap values, taken as maxima of 8 of level T-1
 // when level T is not stored).  By the fact above applied level by level,
@@ -49,34 +64,32 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
                              const int32_t* cmap, int32_t* out) {
   const int tid = threadIdx.x;
   const uint32_t K = (uint32_t)a.k;
-  int64_t nl[4];
-  nl[0] = n0;
-  for (int l = 1; l < 4; ++l) nl[l] = (nl[l - 1] + 7) / 8;
   int T = 0;
-  while (T < 3 && nl[T] > kRegCap) ++T;
-  if (nl[T] > kRegCap) return false;
-  const bool direct = (T == 0) || (T <= 2 && a.lv[T] != nullptr);
-  if (!direct && (T - 1 > 2 || a.lv[T - 1] == nullptr)) return false;
+  while (T < 3 && lv_count(n0, T) > kRegCap) ++T;
+  const int64_t nT = lv_count(n0, T);
+  if (nT > kRegCap) return false;
+  const bool direct = (T == 0) || (T <= 2 && lv_row(a, T, r) != nullptr);
+  if (!direct && (T - 1 > 2 || lv_row(a, T - 1, r) == nullptr)) return false;
   for (int l = 0; l < T; ++l)
-    if (l > 2 || a.lv[l] == nullptr) return false;
+    if (l > 2 || lv_row(a, l, r) == nullptr) return false;
 
   // ---- top level: 4 values per thread ----
   RegKeys top;
   if (direct) {
-    const float* base = a.lv[T] + (int64_t)r * a.lv_stride[T];
+    const float* base = lv_row(a, T, r);
     float v[kRegPer];
-    if (((uintptr_t)base & 15u) == 0 && kRegPer * tid + kRegPer <= nl[T]) {
+    if (((uintptr_t)base & 15u) == 0 && kRegPer * tid + kRegPer <= nT) {
       const float4 x = *(const float4*)(base + kRegPer * tid);
       v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     } else {
 #pragma unroll
-      for (int j = 0; j < kRegPer; ++j) v[j] = base[min((int64_t)(kRegPer * tid + j), nl[T] - 1)];
+      for (int j = 0; j < kRegPer; ++j) v[j] = base[min((int64_t)(kRegPer * tid + j), nT - 1)];
     }
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) top.v[j] = (kRegPer * tid + j < nl[T]) ? order_key(v[j]) : 0u;
+    for (int j = 0; j < kRegPer; ++j) top.v[j] = (kRegPer * tid + j < nT) ? order_key(v[j]) : 0u;
   } else {
-    const float* base = a.lv[T - 1] + (int64_t)r * a.lv_stride[T - 1];
-    const int64_t nb = nl[T - 1];
+    const float* base = lv_row(a, T - 1, r);
+    const int64_t nb = lv_count(n0, T - 1);
     float v[kRegPer * 8];
     if (((uintptr_t)base & 15u) == 0 && 8 * kRegPer * tid + 8 * kRegPer <= nb) {
 #pragma unroll
@@ -123,8 +136,8 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
 
   // ---- descend: children of the kept groups with value >= tau ----
   for (int l = T - 1; l >= 0; --l) {
-    const float* base = a.lv[l] + (int64_t)r * a.lv_stride[l];
-    const int64_t n = nl[l];
+    const float* base = lv_row(a, l, r);
+    const int64_t n = lv_count(n0, l);
     // children of this thread's parents kRegPer*t .. +kRegPer-1; every load
     // is unconditional (clamped index) so all of them are in flight at once
     // (a load under a branch is waited for before the next branch)
@@ -196,15 +209,14 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
 CSA2_DEV void topk_general(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, int32_t (*par)[kSelCap / 8],
                            const int32_t* cmap, int32_t* out) {
   const int tid = threadIdx.x;
-  const int64_t nl[3] = {n0, (n0 + 7) / 8, (n0 + 63) / 64};
   int level = 0;
-  if (n0 > kSelCap) level = (nl[1] > kSelCap) ? 2 : 1;
+  if (n0 > kSelCap) level = (lv_count(n0, 1) > kSelCap) ? 2 : 1;
   bool all = true;     // candidates = every index of the level
   int n_par = 0;       // otherwise: children of par[cur][0 .. n_par)
   int cur = 0;
   for (;;) {
-    const float* base = a.lv[level] + (int64_t)r * a.lv_stride[level];
-    const int64_t n = nl[level];
+    const float* base = lv_row(a, level, r);
+    const int64_t n = lv_count(n0, level);
     const int n_elem = all ? (int)n : 8 * n_par;
     // candidates of this level into LDS in index order, padded with absent
     // keys to a multiple of kSelPad; every read is in bounds (an absent
@@ -262,6 +274,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
   __shared__ int32_t par[2][kSelCap / 8];
   __shared__ int32_t cmap[kSelCap / 8];     // the row's candidate blocks (output index map)
   const int tid = threadIdx.x;
+  CSA2_SPAN(a, 256, 0);
   int r = blockIdx.x;
   if (a.row_list) {
     if ((uint32_t)r >= *a.row_list_count) return;
@@ -282,6 +295,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
     topk_general(a, r, n0, sm, par, cmap, out);
   }
   CSA2_MARK(a, 8);
+  CSA2_SPAN(a, 256, 1);
 }
 
 
