@@ -137,6 +137,9 @@ def _topk_case(rng, kind, n):
         s = rng.standard_normal(n).astype(np.float32)
         s[:min(n, 3000)] += 100
         return s
+    if kind == "copies":      # ~8 copies of each value: ties inside the bin that holds the k-th value
+        pool = rng.standard_normal(max(1, n // 8)).astype(np.float32)
+        return pool[rng.integers(0, len(pool), size=n)]
     if kind == "neginf":
         s = rng.standard_normal(n).astype(np.float32)
         s[rng.random(n) < 0.5] = -np.inf
@@ -147,7 +150,7 @@ def _topk_case(rng, kind, n):
 @pytest.mark.parametrize("k", [1, 7, 512, 1024, 2048])
 def test_topk_bitexact(C, k):
     rng = np.random.default_rng(400 + k)
-    kinds = ["normal", "ties", "zeros", "equal", "clustered", "neginf"]
+    kinds = ["normal", "ties", "zeros", "equal", "clustered", "neginf", "copies"]
     ns = [0, 5, k, 4096, 4097, 9000, 70000, 131072]
     rows = [(kd, n) for kd in kinds for n in ns]
     R = len(rows)
