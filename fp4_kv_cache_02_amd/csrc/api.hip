@@ -98,7 +98,10 @@ int topk_levels_needed(int64_t n) {
 struct TopkWs {
   float* lv1 = nullptr;
   float* lv2 = nullptr;
-  uint32_t* seg_kth = nullptr;    // large-k path (segment thresholds)
+  uint32_t* seg_kth = nullptr;    // large-k path (segment thresholds, gathered values)
+  uint32_t* seg_cnt = nullptr;
+  uint32_t* seg_key = nullptr;
+  int32_t* seg_pos = nullptr;
   int32_t* fail_list = nullptr;
   uint32_t* fail_count = nullptr;
 };
@@ -108,7 +111,11 @@ bool topk_large_shape(int64_t n_max, int k) { return k >= 1024 && n_max > kSelCa
 
 void carve_large(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
   if (!topk_large_shape(n_max, k)) return;
-  t.seg_kth = bp.take<uint32_t>((size_t)R * cdiv(n_max, kSegLen));
+  const size_t nseg = (size_t)cdiv(n_max, kSegLen);
+  t.seg_kth = bp.take<uint32_t>((size_t)R * nseg);
+  t.seg_cnt = bp.take<uint32_t>((size_t)R * nseg);
+  t.seg_key = bp.take<uint32_t>((size_t)R * nseg * kSegLen);
+  t.seg_pos = bp.take<int32_t>((size_t)R * nseg * kSegLen);
   t.fail_list = bp.take<int32_t>((size_t)R);
   t.fail_count = bp.take<uint32_t>(1);
 }
@@ -151,6 +158,9 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
   a.row_list_count = nullptr;
   a.seg_kth = nullptr;
   a.nseg = 0;
+  a.seg_cnt = nullptr;
+  a.seg_key = nullptr;
+  a.seg_pos = nullptr;
   a.fail_list = nullptr;
   a.fail_count = nullptr;
   return a;
@@ -182,6 +192,9 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
   if (tw.seg_kth && a.lv[1] && !a.cand_blocks && !a.row_list && topk_large_shape(a.n_max, a.k)) {
     a.seg_kth = tw.seg_kth;
     a.nseg = (int32_t)cdiv(a.n_max, kSegLen);
+    a.seg_cnt = tw.seg_cnt;
+    a.seg_key = tw.seg_key;
+    a.seg_pos = tw.seg_pos;
     a.fail_list = tw.fail_list;
     a.fail_count = tw.fail_count;
     return hip_status(launch_topk_large(a, st));

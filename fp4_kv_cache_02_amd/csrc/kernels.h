@@ -48,6 +48,9 @@ struct TopkArgs {
   // and the rows it hands to the general path
   uint32_t* seg_kth;          // [R][nseg] or null
   int32_t nseg;
+  uint32_t* seg_cnt;          // [R][nseg]: values >= tau gathered per segment
+  uint32_t* seg_key;          // [R][nseg][kSegLen]: their keys, in index order
+  int32_t* seg_pos;           // [R][nseg][kSegLen]: their indices
   int32_t* fail_list;         // [R]
   uint32_t* fail_count;       // [1]
   CSA2_TRACE_ARG

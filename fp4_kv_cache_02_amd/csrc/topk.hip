@@ -305,21 +305,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
 // seg_kth_kernel, grid (segments, rows): segment s of kSegLen level-0 values
 // (n_s of the row's n0) takes a key t_s with at least m_s = ceil(k n_s / n0)
 // of its values >= t_s (a bin edge near its m_s-th largest; 0 when it holds at
-// most m_s present values; all-ones for an empty segment).  Their minimum tau has at least m_s values >= tau in every
-// segment, sum m_s >= k of them in the row, so the row's k-th largest value
-// is >= tau and the row's top k lie among the values >= tau -- typically a
-// little more than k values, and only those are gathered.
-// topk_tau_kernel, one block per row: level-1 groups >= tau, their level-0
-// children >= tau (in index order), the exact top k of those.  A row whose
-// survivors exceed the block's capacity is listed for the general path.
+// most m_s present values; all-ones for an empty segment).  Their minimum tau
+// has at least m_s values >= tau in every segment, sum m_s >= k of them in the
+// row, so the row's k-th largest value is >= tau and the row's top k lie among
+// the values >= tau -- typically a little more than k values.
+// seg_gather_kernel, grid (segments, rows): the values >= tau of each segment,
+// in index order, into the segment's own list (every segment on its own CU:
+// one CU fetching the whole row is bound by the misses it keeps in flight).
+// seg_final_kernel, one block per row: the lists concatenated in segment
+// order (= index order) and the exact top k of them.  A row with more than
+// kTauCap gathered values is listed for the general path.
 
-constexpr int kTauL1Cap = 8192;           // level-1 groups >= tau
-constexpr int kTauCap = 8192;             // level-0 values >= tau
-constexpr int kTauJ = 32;                 // level-0 elements per thread per round
-constexpr int kTauRound = kTauJ * kSelThreads;
+constexpr int kTauCap = 8192;             // gathered values a row's final selection holds
 constexpr int kTauKeyWords = kTauCap + kTauCap / 32;
+constexpr int kSegPer = kSegLen / kSelThreads;   // values per thread of a segment
 static_assert(kSegLen == 2 * kSelPad, "a segment is two LDS key batches");
-static_assert(kTauMaxN / 8 <= 32 * kSelThreads, "level 1 is 32 values per thread");
+static_assert(kTauMaxN / kSegLen <= kWave, "one segment per lane of a wave");
 
 __global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
   __shared__ SelSmemT<kSegLen + kSegLen / 32> sm;
@@ -334,11 +335,11 @@ __global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
   }
   const uint32_t m_s = (uint32_t)(((int64_t)a.k * n + n0 - 1) / n0);
   const float* base = a.lv[0] + (int64_t)r * a.lv_stride[0] + lo;
-  float v[kSegLen / kSelThreads];
+  float v[kSegPer];
 #pragma unroll
-  for (int j = 0; j < kSegLen / kSelThreads; ++j) v[j] = base[min(tid + j * kSelThreads, n - 1)];
+  for (int j = 0; j < kSegPer; ++j) v[j] = base[min(tid + j * kSelThreads, n - 1)];
 #pragma unroll
-  for (int j = 0; j < kSegLen / kSelThreads; ++j) {
+  for (int j = 0; j < kSegPer; ++j) {
     const int e = tid + j * kSelThreads;
     sm.key[skew(e)] = e < n ? order_key(v[j]) : 0u;
   }
@@ -350,18 +351,77 @@ __global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
   if (tid == 0) a.seg_kth[(int64_t)r * a.nseg + s] = res.T;
 }
 
-struct TauSmem {
-  SelSmemT<kTauKeyWords> sel;     // level-0 survivors' keys
-  int32_t l1[kTauL1Cap];          // level-1 survivors
-  int32_t idx0[kTauCap];          // level-0 survivors' indices
-  uint32_t cnt[kTauJ * kSelWaves];
-  uint32_t off[kTauJ * kSelWaves];
-};
-static_assert(kTauJ * kSelWaves <= kSelThreads, "one ballot count per thread in the scan");
+// tau of row r: the minimum of its segment keys (every lane of every wave)
+CSA2_DEV uint32_t row_tau(const TopkArgs& a, int r) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t t = lane < a.nseg ? a.seg_kth[(int64_t)r * a.nseg + lane] : 0xFFFFFFFFu;
+  return max(wave_min_u32(t), 1u);
+}
 
-__global__ __launch_bounds__(kSelThreads) void topk_tau_kernel(TopkArgs a) {
-  __shared__ TauSmem sm;
+struct GatherSmem {
+  uint32_t wa[kSelWaves];
+  uint32_t cnt[kSegPer * kSelWaves];   // values kept per (round, wave)
+};
+
+__global__ __launch_bounds__(kSelThreads) void seg_gather_kernel(TopkArgs a) {
+  __shared__ GatherSmem sm;
+  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t n0 = row_count(a, r);
+  const int64_t lo = (int64_t)s * kSegLen;
+  const int n = (int)max((int64_t)0, min(n0 - lo, (int64_t)kSegLen));
+  const int64_t rs = (int64_t)r * a.nseg + s;
+  if (n == 0) {
+    if (tid == 0) a.seg_cnt[rs] = 0u;
+    return;
+  }
+  const uint32_t tau = row_tau(a, r);
+  // element e = 512 j + 64 w + l: round j, wave w, lane l (coalesced loads;
+  // index order = (round, wave, lane) order)
+  const float* base = a.lv[0] + (int64_t)r * a.lv_stride[0] + lo;
+  float v[kSegPer];
+#pragma unroll
+  for (int j = 0; j < kSegPer; ++j) v[j] = base[min(tid + j * kSelThreads, n - 1)];
+  uint32_t keepm = 0u;
+#pragma unroll
+  for (int j = 0; j < kSegPer; ++j) {
+    const bool kp = tid + j * kSelThreads < n && order_key(v[j]) >= tau;
+    keepm |= kp ? (1u << j) : 0u;
+    const uint64_t b = __ballot(kp);
+    if (lane == 0) sm.cnt[j * kSelWaves + wv] = (uint32_t)__popcll(b);
+  }
+  __syncthreads();
+  // offsets of the (round, wave) runs: an exclusive scan in that order
+  uint32_t tot;
+  const uint32_t off = block_excl_scan(sm, tid < kSegPer * kSelWaves ? sm.cnt[tid] : 0u, tot);
+  __syncthreads();
+  if (tid < kSegPer * kSelWaves) sm.cnt[tid] = off;
+  __syncthreads();
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  uint32_t* kd = a.seg_key + rs * kSegLen;
+  int32_t* pd = a.seg_pos + rs * kSegLen;
+#pragma unroll
+  for (int j = 0; j < kSegPer; ++j) {
+    const bool kp = (keepm >> j) & 1u;
+    const uint64_t b = __ballot(kp);
+    if (kp) {
+      const uint32_t p = sm.cnt[j * kSelWaves + wv] + (uint32_t)__popcll(b & lt_mask);
+      kd[p] = order_key(v[j]);
+      pd[p] = (int32_t)(lo + tid + j * kSelThreads);
+    }
+  }
+  if (tid == 0) a.seg_cnt[rs] = tot;
+}
+
+struct FinalSmem {
+  SelSmemT<kTauKeyWords> sel;     // the gathered keys
+  int32_t pos[kTauCap];           // their indices
+};
+
+__global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
+  __shared__ FinalSmem sm;
   const int r = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63;
   const uint32_t K = (uint32_t)a.k;
   int32_t* out = a.out + (int64_t)r * a.out_stride;
   const int64_t n0 = row_count(a, r);
@@ -369,107 +429,49 @@ __global__ __launch_bounds__(kSelThreads) void topk_tau_kernel(TopkArgs a) {
     for (int i = tid; i < a.k; i += kSelThreads) out[i] = -1;
     return;
   }
-  CSA2_MARK(a, 20);
-  // nseg <= 64: one value per lane, minimum over the wave (every wave alike)
-  const int lane = tid & 63;
-  uint32_t tau = lane < a.nseg ? a.seg_kth[(int64_t)r * a.nseg + lane] : 0xFFFFFFFFu;
-  tau = max(wave_min_u32(tau), 1u);
-
-  // ---- level 1: thread t owns groups 32t .. 32t+31 ----
-  const int64_t n1 = (n0 + 7) / 8;
-  const float* b1 = a.lv[1] + (int64_t)r * a.lv_stride[1];
-  float v1[32];
-  if (((uintptr_t)b1 & 15u) == 0 && 32 * tid + 32 <= n1) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 x = *(const float4*)(b1 + 32 * tid + 4 * q);
-      v1[4 * q] = x.x; v1[4 * q + 1] = x.y; v1[4 * q + 2] = x.z; v1[4 * q + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) v1[j] = b1[min((int64_t)(32 * tid + j), n1 - 1)];
-  }
-  uint32_t keep = 0u;
-#pragma unroll
-  for (int j = 0; j < 32; ++j)
-    keep |= (32 * tid + j < n1 && order_key(v1[j]) >= tau) ? (1u << j) : 0u;
-  CSA2_MARK(a, 21);
-  uint32_t n_l1;
-  uint32_t pos = block_excl_scan(sm.sel, (uint32_t)__popc(keep), n_l1);
-  bool fail = n_l1 > (uint32_t)kTauL1Cap;
-  if (!fail) {
-#pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if ((keep >> j) & 1u) sm.l1[pos++] = 32 * tid + j;
-  }
-  __syncthreads();
-
-  // ---- level 0: the children of the level-1 survivors, element e = 8 i + c
-  // (child c of survivor i).  A round covers kTauRound elements; thread t
-  // takes e = t + 512 j, so the 8 lanes of a survivor read its 32 contiguous
-  // bytes together and every load of the round is in flight at once.  Order-
-  // preserving compaction: per (j, wave) ballot counts, one block scan over
-  // them in (j, wave) order = element order, then each lane's rank in its
-  // ballot. ----
-  const float* b0 = a.lv[0] + (int64_t)r * a.lv_stride[0];
-  const int lane_w = tid & 63, wv = tid >> 6;
-  const uint64_t lt_mask = (1ull << lane_w) - 1ull;
-  uint32_t n_sv = 0u;
-  for (uint32_t base = 0; !fail && base < 8u * n_l1; base += kTauRound) {
-    float v[kTauJ];
-    int64_t ix[kTauJ];
-#pragma unroll
-    for (int j = 0; j < kTauJ; ++j) {
-      const uint32_t e = base + tid + kSelThreads * j;
-      const bool ok = e < 8u * n_l1;
-      const int64_t i = ok ? (int64_t)sm.l1[e >> 3] * 8 + (e & 7) : -1;
-      ix[j] = (i >= 0 && i < n0) ? i : -1;
-      v[j] = b0[ix[j] >= 0 ? ix[j] : 0];
-    }
-    uint64_t m[kTauJ];
-#pragma unroll
-    for (int j = 0; j < kTauJ; ++j) {
-      m[j] = __ballot(ix[j] >= 0 && order_key(v[j]) >= tau);
-      if (lane_w == 0) sm.cnt[j * kSelWaves + wv] = (uint32_t)__popcll(m[j]);
-    }
-    __syncthreads();
-    uint32_t tot;
-    const uint32_t off = block_excl_scan(sm.sel, tid < kTauJ * kSelWaves ? sm.cnt[tid] : 0u, tot);
-    if (tid < kTauJ * kSelWaves) sm.off[tid] = off;
-    __syncthreads();
-    if (n_sv + tot > (uint32_t)kTauCap) {
-      fail = true;
-      break;
-    }
-#pragma unroll
-    for (int j = 0; j < kTauJ; ++j)
-      if ((m[j] >> lane_w) & 1ull) {
-        const uint32_t p = n_sv + sm.off[j * kSelWaves + wv] + (uint32_t)__popcll(m[j] & lt_mask);
-        sm.sel.key[skew((int)p)] = order_key(v[j]);
-        sm.idx0[p] = (int32_t)ix[j];
-      }
-    n_sv += tot;
-    __syncthreads();
-    CSA2_MARK(a, 22 + min(base / kTauRound, 3u));
-  }
-  if (fail) {
+  // segment counts and their offsets (one segment per lane; every wave alike)
+  const int nseg = (int)((n0 + kSegLen - 1) / kSegLen);
+  const uint32_t c = lane < nseg ? a.seg_cnt[(int64_t)r * a.nseg + lane] : 0u;
+  const uint32_t inc = wave_incl_scan_u32(c);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  if (total > (uint32_t)kTauCap) {
     if (tid == 0) a.fail_list[atomicAdd(a.fail_count, 1u)] = r;
     return;
   }
-  const int n_pad = sel_padded((int)n_sv);
-  for (int e = (int)n_sv + tid; e < n_pad; e += kSelThreads) sm.sel.key[skew(e)] = 0u;
+  // element e of the concatenation lies in segment s = #{segments whose
+  // inclusive end is <= e}; thread t takes e = t + 512 j (all loads at once)
+  constexpr int kJ = kTauCap / kSelThreads;
+  const int64_t rb = (int64_t)r * a.nseg * kSegLen;
+  uint32_t key[kJ];
+  int32_t ps[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const uint32_t e = tid + j * kSelThreads;
+    uint32_t sidx = 0u, start = 0u;
+    for (int q = 0; q < nseg; ++q) {
+      const uint32_t end_q = (uint32_t)__builtin_amdgcn_readlane((int)inc, q);
+      const bool past = end_q <= e;
+      sidx += past ? 1u : 0u;
+      start = past ? end_q : start;
+    }
+    const int64_t g = (e < total) ? rb + (int64_t)sidx * kSegLen + (e - start) : rb;
+    key[j] = a.seg_key[g];
+    ps[j] = a.seg_pos[g];
+  }
+  const int n_pad = sel_padded((int)total);
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int e = tid + j * kSelThreads;
+    if (e < n_pad) {
+      sm.sel.key[skew(e)] = e < (int)total ? key[j] : 0u;
+      sm.pos[e] = ps[j];
+    }
+  }
   __syncthreads();
   const LdsKeysT<SelSmemT<kTauKeyWords>> ks{&sm.sel, n_pad};
-  const SelResult res = block_select(sm.sel, ks, K, 0u, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 64 : nullptr);
-  CSA2_MARK(a, 26);
-  const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) { out[o] = sm.idx0[e]; });
+  const SelResult res = block_select(sm.sel, ks, K, 0u);
+  const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
   for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
-  CSA2_MARK(a, 27);
-  if (CSA2_TRACE_PTR(a) && tid == 0 && blockIdx.x == 0) {
-    CSA2_TRACE_PTR(a)[28] = n_l1;
-    CSA2_TRACE_PTR(a)[29] = n_sv;
-    CSA2_TRACE_PTR(a)[30] = tau;
-  }
 }
 
 // out[r][g] = maximum (in the Top-k order) of in[r][8g .. 8g+7] below the
@@ -502,12 +504,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Large k over rows of at most kTauMaxN values with level 1 stored: segment
-// thresholds, the threshold gather, then the general path for listed rows.
+// Large k over rows of at most kTauMaxN values: segment thresholds, the
+// per-segment gather above their minimum, the final selection, then the
+// general path for listed rows.
 hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   hipLaunchKernelGGL(seg_kth_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
-  hipLaunchKernelGGL(topk_tau_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(seg_gather_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(seg_final_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
   TopkArgs f = a;
   f.row_list = a.fail_list;
   f.row_list_count = a.fail_count;
