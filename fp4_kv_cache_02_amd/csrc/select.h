@@ -40,6 +40,7 @@ struct SelSmemT {
   uint32_t wb[kSelWaves];
   uint32_t wc[kSelWaves];
   uint32_t bc[4];
+  uint32_t fin[kWave];       // keys of the final bin, ranked by one wave
 };
 using SelSmem = SelSmemT<kSelKeyWords>;
 
@@ -181,6 +182,8 @@ struct SelResult {
 // The k-th largest present key (exact = true), or, when `cap` > 0, an earlier
 // bin edge T such that k <= #{keys >= T} <= cap (exact = false; keep every
 // key >= T).  With at most k present keys: T = 0, n_gt = count (keep all).
+// Once the bin holding the k-th largest key has at most 64 keys, one wave
+// ranks them instead of running further passes over every key.
 template <class Keys, class Sm>
 CSA2_DEV SelResult block_select(Sm& sm, const Keys& ks, uint32_t kth, uint32_t cap, uint64_t* tr = nullptr) {
   const int tid = threadIdx.x;
@@ -204,6 +207,7 @@ CSA2_DEV SelResult block_select(Sm& sm, const Keys& ks, uint32_t kth, uint32_t c
     while (shift < 32 && (width >> shift) >= (uint32_t)kSelBins) ++shift;
 #pragma unroll
     for (int i = 0; i < kSelBinsPerThread; ++i) sm.bins[tid + i * kSelThreads] = 0u;
+    if (tid == 0) sm.bc[3] = 0u;     // fill count of sm.fin
     __syncthreads();
     ks.each([&](uint32_t v) {
       if (v >= lo && v <= hi && v != 0u) atomicAdd(&sm.bins[(v - lo) >> shift], 1u);
@@ -251,6 +255,37 @@ CSA2_DEV SelResult block_select(Sm& sm, const Keys& ks, uint32_t kth, uint32_t c
       res.n_gt = acc;
       res.n_eq = h;
       res.exact = true;
+      return res;
+    }
+    if (h <= (uint32_t)kWave) {
+      // the bin's h keys into sm.fin (any order): acc keys lie above the bin
+      // and the k-th largest is the need-th largest of the bin
+      ks.each([&](uint32_t v) {
+        if (v >= blo && v <= bhi && v != 0u) sm.fin[atomicAdd(&sm.bc[3], 1u)] = v;
+      });
+      __syncthreads();
+      if (tid < kWave) {
+        const uint32_t need = kth - acc;
+        const uint32_t mine = (tid < (int)h) ? sm.fin[tid] : 0u;
+        uint32_t gt = 0u, ge = 0u;
+        for (int j = 0; j < (int)h; ++j) {
+          const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+          gt += (o > mine) ? 1u : 0u;
+          ge += (o >= mine) ? 1u : 0u;
+        }
+        // the lanes holding the need-th largest value (all equal) publish it
+        if (tid < (int)h && gt < need && ge >= need) {
+          sm.bc[0] = mine;
+          sm.bc[1] = acc + gt;
+          sm.bc[2] = ge - gt;
+        }
+      }
+      __syncthreads();
+      res.T = sm.bc[0];
+      res.n_gt = sm.bc[1];
+      res.n_eq = sm.bc[2];
+      res.exact = true;
+      __syncthreads();
       return res;
     }
     above = acc;
