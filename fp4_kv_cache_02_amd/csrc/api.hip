@@ -102,8 +102,6 @@ struct TopkWs {
   uint32_t* seg_cnt = nullptr;
   uint32_t* seg_key = nullptr;
   int32_t* seg_pos = nullptr;
-  int32_t* fail_list = nullptr;
-  uint32_t* fail_count = nullptr;
 };
 
 // Large k over long rows: segment thresholds, then a gather above them.
@@ -116,8 +114,6 @@ void carve_large(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
   t.seg_cnt = bp.take<uint32_t>((size_t)R * nseg);
   t.seg_key = bp.take<uint32_t>((size_t)R * nseg * kSegLen);
   t.seg_pos = bp.take<int32_t>((size_t)R * nseg * kSegLen);
-  t.fail_list = bp.take<int32_t>((size_t)R);
-  t.fail_count = bp.take<uint32_t>(1);
 }
 
 // Workspace for the levels of maxima a generic Top-k must build itself.
@@ -161,8 +157,6 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
   a.seg_cnt = nullptr;
   a.seg_key = nullptr;
   a.seg_pos = nullptr;
-  a.fail_list = nullptr;
-  a.fail_count = nullptr;
   return a;
 }
 
@@ -195,8 +189,6 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
     a.seg_cnt = tw.seg_cnt;
     a.seg_key = tw.seg_key;
     a.seg_pos = tw.seg_pos;
-    a.fail_list = tw.fail_list;
-    a.fail_count = tw.fail_count;
     return hip_status(launch_topk_large(a, st));
   }
   return hip_status(launch_topk(a, st));

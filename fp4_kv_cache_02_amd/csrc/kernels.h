@@ -44,15 +44,12 @@ struct TopkArgs {
   int32_t out_stride;
   const int32_t* row_list;    // optional: select only rows row_list[0 .. *row_list_count)
   const uint32_t* row_list_count;
-  // large-k path (segment thresholds): per (row, segment) k-th largest keys,
-  // and the rows it hands to the general path
+  // large-k path: per (row, segment) thresholds and gathered values
   uint32_t* seg_kth;          // [R][nseg] or null
   int32_t nseg;
   uint32_t* seg_cnt;          // [R][nseg]: values >= tau gathered per segment
   uint32_t* seg_key;          // [R][nseg][kSegLen]: their keys, in index order
   int32_t* seg_pos;           // [R][nseg][kSegLen]: their indices
-  int32_t* fail_list;         // [R]
-  uint32_t* fail_count;       // [1]
   CSA2_TRACE_ARG
 };
 

@@ -313,8 +313,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
 // in index order, into the segment's own list (every segment on its own CU:
 // one CU fetching the whole row is bound by the misses it keeps in flight).
 // seg_final_kernel, one block per row: the lists concatenated in segment
-// order (= index order) and the exact top k of them.  A row with more than
-// kTauCap gathered values is listed for the general path.
+// order (= index order) and the exact top k of them; a row with more than
+// kTauCap gathered values takes the general path in the same block.
 
 constexpr int kTauCap = 8192;             // gathered values a row's final selection holds
 constexpr int kTauKeyWords = kTauCap + kTauCap / 32;
@@ -325,7 +325,6 @@ static_assert(kTauMaxN / kSegLen <= kWave, "one segment per lane of a wave");
 __global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
   __shared__ SelSmemT<kSegLen + kSegLen / 32> sm;
   const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-  if (s == 0 && r == 0 && tid == 0) *a.fail_count = 0u;
   const int64_t n0 = row_count(a, r);
   const int64_t lo = (int64_t)s * kSegLen;
   const int n = (int)max((int64_t)0, min(n0 - lo, (int64_t)kSegLen));
@@ -417,9 +416,19 @@ struct FinalSmem {
   SelSmemT<kTauKeyWords> sel;     // the gathered keys
   int32_t pos[kTauCap];           // their indices
 };
+struct GeneralSmem {              // the general path, for a row with more
+  SelSmem sel;
+  int32_t par[2][kSelCap / 8];
+  int32_t cmap[1];                // (no candidate map on this path)
+};
+union FinalOrGeneral {
+  FinalSmem f;
+  GeneralSmem g;
+};
 
 __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
-  __shared__ FinalSmem sm;
+  __shared__ FinalOrGeneral u;
+  FinalSmem& sm = u.f;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63;
   const uint32_t K = (uint32_t)a.k;
@@ -435,7 +444,12 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
   const uint32_t inc = wave_incl_scan_u32(c);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
   if (total > (uint32_t)kTauCap) {
-    if (tid == 0) a.fail_list[atomicAdd(a.fail_count, 1u)] = r;
+    // too many values at or above tau (ties, or scores that favour one
+    // segment): this block takes the row through the general path
+    if (!topk_threshold(a, r, n0, u.g.sel, u.g.par, u.g.cmap, out)) {
+      __syncthreads();
+      topk_general(a, r, n0, u.g.sel, u.g.par, u.g.cmap, out);
+    }
     return;
   }
   // element e of the concatenation lies in segment s = #{segments whose
@@ -505,18 +519,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 }
 
 // Large k over rows of at most kTauMaxN values: segment thresholds, the
-// per-segment gather above their minimum, the final selection, then the
-// general path for listed rows.
+// per-segment gather above their minimum, the final selection.
 hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   hipLaunchKernelGGL(seg_kth_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(seg_gather_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(seg_final_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
-  TopkArgs f = a;
-  f.row_list = a.fail_list;
-  f.row_list_count = a.fail_count;
-  f.seg_kth = nullptr;
-  hipLaunchKernelGGL(topk_kernel, dim3(a.R), dim3(kSelThreads), 0, st, f);
   return hipGetLastError();
 }
 
