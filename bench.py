@@ -32,11 +32,14 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=1,
-                   help="workload id (1: 128K decode group; 2: 1M decode group; 3: prefill chunk; 4: mixed serving)")
+                   help="workload id (1: 128K decode group; 2: 1M decode group; 3: prefill chunk; 4: mixed serving; "
+                        "5: the 38 CSA2 layers of one decode step, encoder at ratio 2 + decoder, batch 8 at 128K)")
     p.add_argument("--replicas", type=int, default=3,
                    help="input replicas cycled per step so the 256 MB last-level cache cannot serve them")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-1m", action="store_true", help="skip the 1M-context group (reported beside the default)")
+    p.add_argument("--no-model", action="store_true",
+                   help="skip the 38-layer decode step (reported beside the default)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -217,6 +220,49 @@ def measure(w, steps, warmup, n_replicas):
     return res
 
 
+def measure_model(ws, steps, warmup, n_replicas):
+    """Times `steps` decode steps of the 38 CSA2 layers: every layer of the
+    encoder workload, then every layer of the decoder workload, each over its
+    own caches (cycled over replicas like measure())."""
+    import torch
+    from fp4_kv_cache_02_amd import group
+
+    t_setup = time.perf_counter()
+    runners = []            # runners[replica] = [encoder runner, decoder runner]
+    bases = [group.build_inputs(w) for w in ws]
+    for i in range(max(1, n_replicas)):
+        row = []
+        for w, base in zip(ws, bases):
+            inp = base if i == 0 else group.GroupInputs(
+                kv_fp4=base.kv_fp4.clone(), kv_scale=base.kv_scale.clone(), k_idx=base.k_idx.clone(),
+                seq_len=base.seq_len, page_table=base.page_table, seq_stride=base.seq_stride,
+                row_seq=base.row_seq, layers=base.layers)
+            row.append(group.GroupRunner(w, inp))
+        runners.append(row)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    def step(i):
+        for r in runners[i % len(runners)]:
+            r.step()
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    algo = sum(algorithmic_bytes(w)[0] for w in ws)
+    layers = sum(algorithmic_bytes(w)[2] for w in ws)
+    rows = ws[0].R
+    return {"ms": ms, "value": rows * layers / (ms * 1e-3), "attn_layers": layers, "algo": algo,
+            "replicas": len(runners), "setup_s": t_setup}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -235,6 +281,24 @@ def main():
         return
 
     from fp4_kv_cache_02_amd import synth
+
+    if args.config == 5:
+        ws = synth.model_step()
+        m5 = measure_model(ws, args.steps, args.warmup, args.replicas)
+        out = {
+            "metric": "CSA2 decode tokens/s/layer over the 38 CSA2 layers of one decode step",
+            "value": m5["value"], "unit": "tokens/s/layer", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": m5["ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "fp4(e2m1)+e4m3 main KV, bf16 indexer/query/window, f32 accumulate",
+            "data": data_desc(ws[1]),
+            "config": {"workload": "+".join(w.name for w in ws), "batch": ws[0].B, "layers": m5["attn_layers"],
+                       "topk": 512, "window": 128, "replicas": m5["replicas"]},
+            "step_algorithmic_bytes": m5["algo"], "step_gbps": m5["algo"] / (m5["ms"] * 1e-3) / 1e9,
+            "setup_s": m5["setup_s"],
+        }
+        print(json.dumps(out), flush=True)
+        return
 
     w = synth.workload(args.config)
     m = measure(w, args.steps, args.warmup, args.replicas if not w.prefill_rows else 1)
@@ -286,6 +350,14 @@ def main():
                              "ms_per_step": m2["ms"], "step_gbps": m2["algo"] / (m2["ms"] * 1e-3) / 1e9,
                              "scan_avg_launch_ms": m2["kern_ms"], "scan_achieved_gbps": a2,
                              "scan_frac": a2 / HBM_PEAK_GBPS, "replicas": m2["replicas"]}
+    if args.config == 1 and not args.no_model:
+        # the whole decode step's CSA2 layers: encoder (18, ratio 2) + decoder (20)
+        ws = synth.model_step()
+        m5 = measure_model(ws, args.steps, args.warmup, args.replicas)
+        out["model_38_layers"] = {"workload": "+".join(w.name for w in ws), "layers": m5["attn_layers"],
+                                  "value": m5["value"], "unit": "tokens/s/layer", "ms_per_step": m5["ms"],
+                                  "step_gbps": m5["algo"] / (m5["ms"] * 1e-3) / 1e9,
+                                  "replicas": m5["replicas"]}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -126,6 +126,24 @@ def workload(cfg: int, reduced: bool = False) -> Workload:
     raise ValueError(cfg)
 
 
+def model_step(reduced: bool = False) -> List[Workload]:
+    """The 38 CSA2 layers of one decode step as two workloads over their own
+    caches: the encoder's 18 layers at compression ratio 2 (three groups of
+    Full + 5 Reuse over L/2 compressed entries) and the decoder's 20 (Full +
+    3 Reuse, the Full layer also building the hierarchical candidate set, then
+    four groups of Reindex + 3 Reuse over L positions) -- the layer pattern of
+    the 7minutos.es page, section "Atención escasa comprimida 2 (CSA2)", and
+    the conexaotc.com.br page, paragraph on CSA2.  Decode batch 8 at L = 131072."""
+    if reduced:
+        return [Workload("model38_reduced_enc18_b2_E5000", 1005, [5000, 2048], "FRRRRR" * 3, planted=0.01),
+                Workload("model38_reduced_dec20_b2_L20000", 1006, [20000, 9000], "FRRR" + "IRRR" * 4,
+                         hier=True, planted=0.01)]
+    return [Workload("model38_enc18_F5Rx3_b8_E65536", 1005, [65536] * 8, "FRRRRR" * 3, planted=0.01,
+                     kv_pool=65536),
+            Workload("model38_dec20_F3R_4xI3R_b8_L131072", 1006, [131072] * 8, "FRRR" + "IRRR" * 4,
+                     hier=True, planted=0.01, kv_pool=65536)]
+
+
 # --------------------------------------------------------------------------
 # generators (numpy, host)
 # --------------------------------------------------------------------------
