@@ -184,6 +184,33 @@ def _fma32(c: np.ndarray, a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return (c.astype(np.float64) + a * b).astype(np.float32)
 
 
+def _head_dots(q_bits, k_vals) -> np.ndarray:
+    """The four heads' dot products d_h, float32 [N, 4], in the fixed order:
+    eight partial sums c_j over channels 8j .. 8j+7, each accumulated from +0
+    in channel order with one fused multiply-add per channel, then
+    ((c0+c1)+(c2+c3)) + ((c4+c5)+(c6+c7)).  k_vals: [N, 64] float64 holding
+    values exactly representable in bf16."""
+    q = bf16_to_f64(q_bits).reshape(4, 8, 8)           # [head, chunk, lane]
+    N = k_vals.shape[0]
+    k = np.asarray(k_vals, dtype=np.float64).reshape(N, 1, 8, 8)   # [pos, -, chunk, lane]
+    c = np.zeros((N, 4, 8), dtype=np.float32)
+    for i in range(8):
+        c = _fma32(c, q[None, :, :, i], k[:, :, :, i])
+    return ((c[..., 0] + c[..., 1]) + (c[..., 2] + c[..., 3])) + \
+        ((c[..., 4] + c[..., 5]) + (c[..., 6] + c[..., 7]))
+
+
+def _head_sum(d, w) -> np.ndarray:
+    """(w0*r0 + w1*r1) + (w2*r2 + w3*r3), r_h = ReLU(d_h), every product and
+    sum rounded to float32."""
+    r = np.where(d > 0, d, np.float32(0.0)).astype(np.float32)
+    if w is None:
+        w = np.ones(4, dtype=np.float32)
+    w = np.asarray(w, dtype=np.float32)
+    p = (r * w[None, :]).astype(np.float32)
+    return ((p[:, 0] + p[:, 1]) + (p[:, 2] + p[:, 3])).astype(np.float32)
+
+
 def index_scores(q_bits, k_bits, w=None) -> np.ndarray:
     """Indexer scores of N keys for one query: float32 [N].
 
@@ -198,27 +225,42 @@ def index_scores(q_bits, k_bits, w=None) -> np.ndarray:
     ((c0+c1)+(c2+c3)) + ((c4+c5)+(c6+c7)).  Every operation rounds to float32;
     each w_h*r_h product is rounded on its own.
     """
-    q = bf16_to_f64(q_bits).reshape(4, 8, 8)           # [head, chunk, lane]
-    k = bf16_to_f64(k_bits)
-    N = k.shape[0]
-    k = k.reshape(N, 1, 8, 8)                           # [pos, -, chunk, lane]
-    c = np.zeros((N, 4, 8), dtype=np.float32)
-    for i in range(8):
-        c = _fma32(c, q[None, :, :, i], k[:, :, :, i])
-    d = ((c[..., 0] + c[..., 1]) + (c[..., 2] + c[..., 3])) + \
-        ((c[..., 4] + c[..., 5]) + (c[..., 6] + c[..., 7]))            # [N, 4] f32
-    r = np.where(d > 0, d, np.float32(0.0)).astype(np.float32)
-    if w is None:
-        w = np.ones(4, dtype=np.float32)
-    w = np.asarray(w, dtype=np.float32)
-    p = (r * w[None, :]).astype(np.float32)
-    return ((p[:, 0] + p[:, 1]) + (p[:, 2] + p[:, 3])).astype(np.float32)
+    return _head_sum(_head_dots(q_bits, bf16_to_f64(k_bits)), w)
+
+
+def index_scores_fp8(q_bits, k_codes, k_scale, w=None) -> np.ndarray:
+    """Indexer scores against FP8 indexer keys: float32 [N].
+
+    The variant in which an indexer entry is 64 E4M3 codes and one 4-byte
+    scale, 68 B per position -- the entry size under which the pages' global
+    KV cache of 890 B per token adds up with the 288-B FP4 main-KV entry
+    (890 = 2.5 x (288 + 68); the figure: conexaotc.com.br page, opening
+    paragraph; 7minutos.es page, opening section).  The pages give no
+    formula; the reading taken here: the entry's value is the decoded
+    E4M3 vector times its scale, and the scale multiplies each head's dot
+    product, d'_h = float32(s * d_h), with d_h evaluated over the exact E4M3
+    values in the order of index_scores; then ReLU and the head sum as there.
+
+    k_codes: [N, 64] OCP E4M3FN bytes (no NaN codes); k_scale: [N] float32,
+    finite and >= 0.
+    """
+    d = _head_dots(q_bits, e4m3_value(k_codes))
+    sc = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
+    d = (d.astype(np.float64) * sc[:, None]).astype(np.float32)     # exact product, one rounding
+    return _head_sum(d, w)
 
 
 def index_scores_chunked(q_bits, k_bits, w=None, chunk: int = 1 << 16) -> np.ndarray:
     out = np.empty(k_bits.shape[0], dtype=np.float32)
     for s in range(0, k_bits.shape[0], chunk):
         out[s:s + chunk] = index_scores(q_bits, k_bits[s:s + chunk], w)
+    return out
+
+
+def index_scores_fp8_chunked(q_bits, k_codes, k_scale, w=None, chunk: int = 1 << 16) -> np.ndarray:
+    out = np.empty(k_codes.shape[0], dtype=np.float32)
+    for s in range(0, k_codes.shape[0], chunk):
+        out[s:s + chunk] = index_scores_fp8(q_bits, k_codes[s:s + chunk], k_scale[s:s + chunk], w)
     return out
 
 

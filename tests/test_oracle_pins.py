@@ -191,6 +191,82 @@ def test_score_close_to_exact_value():
     assert np.all(np.abs(got - exact) <= bound)
 
 
+def _fp8_codes(rng, shape):
+    """Random OCP E4M3FN codes without the two NaN codes."""
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] ^= 1
+    return c
+
+
+def test_fp8_score_unit_scale_equals_bf16_path():
+    """With scale 1 the FP8 variant is the bf16 score of the decoded keys
+    (every E4M3 value is exact in bf16): ties the variant to the pinned path."""
+    rng = np.random.default_rng(21)
+    qb = bf16(rng.standard_normal((4, 64)))
+    c = _fp8_codes(rng, (3000, 64))
+    kb = bf16(O.e4m3_value(c))
+    assert np.array_equal(O.bf16_to_f64(kb), O.e4m3_value(c))
+    w = np.array([1.0, 0.5, 2.0, 0.25], np.float32)
+    got = O.index_scores_fp8(qb, c, np.ones(3000, np.float32), w)
+    ref = O.index_scores(qb, kb, w)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_fp8_score_integer_closed_form():
+    """Small integer keys and queries with integer or power-of-two scales: every
+    step is exact, so the score is sum_h w_h * max(0, s * q_h . k)."""
+    rng = np.random.default_rng(22)
+    q = rng.integers(-3, 4, size=(4, 64))
+    kv = rng.integers(-4, 5, size=(300, 64))
+    c = O.e4m3_encode(np.abs(kv).astype(np.float64)) | np.where(kv < 0, 0x80, 0).astype(np.uint8)
+    assert np.array_equal(O.e4m3_value(c), kv.astype(np.float64))
+    sc = rng.choice([0.0, 0.25, 0.5, 1.0, 3.0, 8.0], size=300).astype(np.float32)
+    w = rng.integers(0, 3, size=4)
+    got = O.index_scores_fp8(bf16(q), c, sc, w.astype(np.float32))
+    for n in range(300):
+        exact = sum(int(w[h]) * max(0.0, float(sc[n]) * sum(int(q[h, i]) * int(kv[n, i]) for i in range(64)))
+                    for h in range(4))
+        assert float(got[n]) == exact, n
+
+
+def test_fp8_score_close_to_exact_value():
+    """Random codes and scales: within the summation bound of the exact value
+    (one more rounding for the scale)."""
+    rng = np.random.default_rng(23)
+    qb = bf16(rng.standard_normal((4, 64)))
+    c = _fp8_codes(rng, (2000, 64))
+    c &= 0xBF                        # exponents <= 7: values within [-2, 2)
+    sc = np.exp(rng.uniform(-3, 3, size=2000)).astype(np.float32)
+    q, k = O.bf16_to_f64(qb), O.e4m3_value(c)
+    d = k @ q.T
+    exact = np.maximum(d * sc[:, None].astype(np.float64), 0.0).sum(axis=1)
+    bound = (np.abs(k) @ np.abs(q).T * sc[:, None]).sum(axis=1) * 72 * 2.0 ** -24 + 1e-30
+    got = O.index_scores_fp8(qb, c, sc).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= bound)
+    # a negative dot product stays at zero after the scale
+    one = np.zeros((1, 64), np.uint8)
+    one[0, 0] = 0xB8                 # -1.0
+    qe = np.zeros((4, 64), np.float32)
+    qe[0, 0] = 1.0
+    assert float(O.index_scores_fp8(bf16(qe), one, np.array([5.0], np.float32))[0]) == 0.0
+    one[0, 0] = 0x38                 # +1.0
+    assert float(O.index_scores_fp8(bf16(qe), one, np.array([5.0], np.float32))[0]) == 5.0
+
+
+def test_fp8_scale_placement():
+    """The scale multiplies each head's dot product before the head sum: with
+    d0 = 1, d1 = 2^-24 and s = 3, float32(3) + float32(3 * 2^-24) rounds to
+    3 + 2^-22 (0.75 of an ulp of 3 rounds up), whereas scaling the finished
+    sum would give 3 * float32(1 + 2^-24) = 3 (the tie rounds to even)."""
+    qe = np.zeros((4, 64), np.float32)
+    qe[0, 0] = 1.0
+    qe[1, 0] = 2.0 ** -24
+    k = np.zeros((1, 64), np.uint8)
+    k[0, 0] = 0x38                   # +1.0
+    got = float(O.index_scores_fp8(bf16(qe), k, np.array([3.0], np.float32))[0])
+    assert got == 3.0 + 2.0 ** -22
+
+
 # ---------------------------------------------------------------------- O5 --
 
 def _brute_topk(vals, k):
