@@ -120,9 +120,11 @@ def csa2_version() -> str:
 
 def make_cache(data, scale=None, page_table=None, seq_stride: int = 0, n_slots: Optional[int] = None,
                page_size: int = PAGE) -> csa2_cache:
-    """Describe a per-position cache.  data: [n_slots, 256] uint8 (main KV) or
-    [n_slots, 64] bf16/int16 (indexer keys); scale: [n_slots, 32] uint8;
-    page_table: [B, max_pages] int32 or None (then slot = b*seq_stride + p)."""
+    """Describe a per-position cache.  data: [n_slots, 256] uint8 (main KV),
+    [n_slots, 64] bf16/int16 (indexer keys) or [n_slots, 64] uint8 E4M3 codes
+    (FP8 indexer keys); scale: [n_slots, 32] uint8 (main KV), None (bf16
+    indexer keys) or [n_slots] float32 (FP8 indexer keys); page_table:
+    [B, max_pages] int32 or None (then slot = b*seq_stride + p)."""
     c = csa2_cache()
     c.data = _p(data)
     c.scale = _p(scale)

@@ -56,6 +56,17 @@ bool cache_ok(const csa2_cache* c, bool need_scale) {
 
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
+// The indexer-key cache: bf16 keys (scale NULL, 16-byte aligned rows) or FP8
+// keys (64 E4M3 codes per slot, 8-byte aligned rows, and a float32 scale per
+// slot, 4-byte aligned).
+csa2_status idx_cache_status(const csa2_cache* c) {
+  if (!cache_ok(c, false)) return CSA2_ERR_NULL;
+  if (c->n_slots < 1 || c->n_slots > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
+  if (c->scale && (((uintptr_t)c->scale & 3u) || ((uintptr_t)c->data & 7u))) return CSA2_ERR_SHAPE;
+  if (!c->scale && ((uintptr_t)c->data & 15u)) return CSA2_ERR_SHAPE;
+  return CSA2_OK;
+}
+
 // ---------------------------------------------------------------- scoring --
 
 csa2_status do_index_score(const uint16_t* q_idx, const float* head_w, const csa2_cache* k_idx,
@@ -66,6 +77,7 @@ csa2_status do_index_score(const uint16_t* q_idx, const float* head_w, const csa
   a.q32 = (const uint32_t*)q_idx;
   a.head_w = head_w;
   a.kdata = (const uint4*)k_idx->data;
+  a.kscale = (const float*)k_idx->scale;
   a.map = make_slot_map(*k_idx);
   a.row_seq = row_seq;
   a.seq_len = seq_len;
@@ -329,7 +341,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
     float* bmax = bp.take<float>((size_t)R * cdiv(n_max, 8));
     float* m64 = bp.take<float>((size_t)R * cdiv(n_max, 64));
     // (one sequence: every row's row_seq entry is 0)
-    if (sh->B == 1 && a->row_seq && !blocks_only && prefill_shape(mode, R, n_max, sh->hier)) {
+    if (sh->B == 1 && a->row_seq && !blocks_only && !sh->k_idx.scale && prefill_shape(mode, R, n_max, sh->hier)) {
       // prefill chunk: matrix-core indexer with exact selection; the rows it
       // lists (too many candidates) take the exact scan and Top-k below
       const PrefWs pw = carve_prefill(bp, R, n_max);
@@ -358,6 +370,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       ia.q32 = p.q32;
       ia.head_w = a->head_w;
       ia.kdata = p.kdata;
+      ia.kscale = nullptr;            // (the matrix-core path runs on bf16 keys only)
       ia.map = p.map;
       ia.row_seq = a->row_seq;
       ia.seq_len = sh->seq_len;
@@ -476,9 +489,8 @@ csa2_status csa2_index_score(const uint16_t* q_idx, const float* head_w, const c
                              int32_t n_cand, int32_t R, int32_t n_max, float* scores, float* block_max,
                              hipStream_t stream) {
   if (!q_idx || !k_idx || !seq_len || !scores) return CSA2_ERR_NULL;
-  if (!cache_ok(k_idx, false)) return CSA2_ERR_NULL;
+  if (const csa2_status cs = idx_cache_status(k_idx)) return cs;
   if (R < 1 || R > CSA2_MAX_ROWS || n_max < 0) return CSA2_ERR_SHAPE;
-  if (k_idx->n_slots < 1 || k_idx->n_slots > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
   if (cand_blocks) {
     if (n_cand < 1 || n_cand > CSA2_KEEP_BLOCKS) return CSA2_ERR_SHAPE;
     if (block_max) return CSA2_ERR_UNSUPPORTED;
@@ -579,8 +591,7 @@ csa2_status csa2_group_step(csa2_mode first_mode, int32_t n_layers, const csa2_l
   if ((int64_t)R * n_layers > CSA2_MAX_ROWS) return CSA2_ERR_SHAPE;
   if (first_mode != CSA2_REUSE) {
     if (!layers[0].q_idx) return CSA2_ERR_NULL;
-    if (!cache_ok(&sh->k_idx, false)) return CSA2_ERR_NULL;
-    if (sh->k_idx.n_slots < 1 || sh->k_idx.n_slots > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
+    if (const csa2_status cs = idx_cache_status(&sh->k_idx)) return cs;
     if (sh->hier && !sh->cand_blocks) return CSA2_ERR_NULL;
   }
   if (!ws) return CSA2_ERR_WORKSPACE;

@@ -82,18 +82,37 @@ CSA2_DEV StepGeo step_geo(const IdxArgs& a, uint32_t item, int g) {
   return s;
 }
 
-// The 16-byte chunk j of the key of position i of the group (slot 0 stands
-// in for absent positions: every load is unconditional and in bounds).  The
-// keys are streamed once per scan: non-temporal loads (measured ~10 % faster
-// than ordinary ones at 8 x 128K positions).
+// Chunk j (channels 8j .. 8j+7) of the key of position i of the group (slot
+// 0 stands in for absent positions: every load is unconditional and in
+// bounds): 16 bytes of bf16, or 8 bytes of E4M3 codes for FP8 keys (in .x,
+// .y).  The keys are streamed once per scan: non-temporal loads (measured
+// ~10 % faster than ordinary ones at 8 x 128K positions).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <bool FP8>
 CSA2_DEV uint4 key_chunk(const uint4* __restrict__ kd, const StepGeo& s, int i, int j) {
   const int64_t slot = (i < s.nv) ? s.s0 + i : 0;
+  if (FP8) {
+    const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)kd + slot * 8 + j);
+    return make_uint4(v[0], v[1], 0u, 0u);
+  }
   const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)&kd[slot * 8 + j]);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-template <bool CAND, bool HAS_W, bool MAXIMA, bool PERSIST>
+// The eight channel values of a chunk as exact floats.
+template <bool FP8>
+CSA2_DEV void chunk_values(uint4 kw, float (&kf)[8]) {
+  if (FP8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[e] = e4m3_to_float(((e < 4 ? kw.x : kw.y) >> (8 * (e & 3))) & 0xFFu);
+  } else {
+    kf[0] = bf16_lo(kw.x); kf[1] = bf16_hi(kw.x); kf[2] = bf16_lo(kw.y); kf[3] = bf16_hi(kw.y);
+    kf[4] = bf16_lo(kw.z); kf[5] = bf16_hi(kw.z); kf[6] = bf16_lo(kw.w); kf[7] = bf16_hi(kw.w);
+  }
+}
+
+template <bool CAND, bool HAS_W, bool MAXIMA, bool PERSIST, bool FP8>
 __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 3, j = lane & 7;
@@ -112,7 +131,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
   uint4 regs[8];
   StepGeo cur = step_geo<CAND>(a, item, g);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) regs[i] = key_chunk(kd, cur, i, j);
+  for (int i = 0; i < 8; ++i) regs[i] = key_chunk<FP8>(kd, cur, i, j);
+  // FP8 keys: the scale of the position this lane finishes (slot 0 when absent)
+  float ksc = 1.0f;
+  if (FP8) ksc = a.kscale[pj < cur.nv ? cur.s0 + pj : 0];
 
   int qrow = -1;
   float qf[4][8];
@@ -139,15 +161,17 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
     const bool has_next = PERSIST && next < n_items;
     StepGeo nxt = cur;
     if (has_next) nxt = step_geo<CAND>(a, next, g);
+    float ksc_next = ksc;
+    if (FP8 && has_next) ksc_next = a.kscale[pj < nxt.nv ? nxt.s0 + pj : 0];
 
     // chunk partials c_j of the eight positions, four heads
     float P[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint4 kw = regs[i];
-      if (has_next) regs[i] = key_chunk(kd, nxt, i, j);
-      const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
-                           bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+      if (has_next) regs[i] = key_chunk<FP8>(kd, nxt, i, j);
+      float kf[8];
+      chunk_values<FP8>(kw, kf);
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         float acc = 0.0f;
@@ -179,6 +203,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
       const float keep = upper ? Rr[1][h] : Rr[0][h];
       const float send = upper ? Rr[0][h] : Rr[1][h];
       d[h] = keep + CSA2_DPP(send, 0x141);              // partner 7 - j
+    }
+    // FP8 keys: the entry's scale multiplies each head's dot product (one rounding)
+    if (FP8) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) d[h] = d[h] * ksc;
     }
     float rr[4];
 #pragma unroll
@@ -217,6 +246,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
     if (!has_next) break;
     item = next;
     cur = nxt;
+    ksc = ksc_next;
   }
 }
 
@@ -231,12 +261,18 @@ hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxi
   const bool persist = a.row_list != nullptr;
   int64_t blocks = (items + kScanWaves - 1) / kScanWaves;
   if (persist && blocks > 256 * 4) blocks = 256 * 4;
-#define CSA2_IDX_LAUNCH(C, Wt, M)                                                                       \
-  do {                                                                                                 \
-    if (persist)                                                                                       \
-      hipLaunchKernelGGL((index_scan_kernel<C, Wt, M, true>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a); \
-    else                                                                                               \
-      hipLaunchKernelGGL((index_scan_kernel<C, Wt, M, false>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a); \
+  const bool fp8 = a.kscale != nullptr;
+#define CSA2_IDX_LAUNCH4(C, Wt, M, F)                                                                      \
+  do {                                                                                                     \
+    if (persist)                                                                                           \
+      hipLaunchKernelGGL((index_scan_kernel<C, Wt, M, true, F>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a); \
+    else                                                                                                   \
+      hipLaunchKernelGGL((index_scan_kernel<C, Wt, M, false, F>), dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, st, a); \
+  } while (0)
+#define CSA2_IDX_LAUNCH(C, Wt, M)              \
+  do {                                         \
+    if (fp8) CSA2_IDX_LAUNCH4(C, Wt, M, true); \
+    else CSA2_IDX_LAUNCH4(C, Wt, M, false);    \
   } while (0)
   if (cand) {
     if (has_w) CSA2_IDX_LAUNCH(true, true, false); else CSA2_IDX_LAUNCH(true, false, false);
@@ -246,6 +282,7 @@ hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxi
     if (has_w) CSA2_IDX_LAUNCH(false, true, false); else CSA2_IDX_LAUNCH(false, false, false);
   }
 #undef CSA2_IDX_LAUNCH
+#undef CSA2_IDX_LAUNCH4
   return hipGetLastError();
 }
 

@@ -5,27 +5,32 @@
 
 namespace csa2 {
 
+// (every optional pointer defaults to null: a new field left unset by a caller
+// must select no variant)
 struct IdxArgs {
-  const uint32_t* q32;        // [R][4][32] bf16 pairs
-  const float* head_w;        // [R][4] or null
-  const uint4* kdata;         // [n_slots][8] 16-byte chunks of the indexer key
-  SlotMap map;
-  const int32_t* row_seq;
-  const int32_t* seq_len;
-  const int32_t* cand;        // [R][n_cand] or null
-  int32_t n_cand;
-  int32_t R;
-  int32_t n_max;
-  int32_t steps_per_row;      // 64-position steps: ceil(n_max/64) (scan) or ceil(n_cand/8) (Reindex)
-  int64_t score_stride;
-  int64_t bmax_stride;
-  int64_t max64_stride;
-  float* scores;
-  float* block_max;           // [R][ceil(n_max/8)] maxima of 8 positions (scan, optional)
-  float* max64;               // [R][ceil(n_max/64)] maxima of 64 positions (scan, optional)
-  const int32_t* row_list;    // optional: score only rows row_list[0 .. *row_list_count)
-  const uint32_t* row_list_count;
-  CSA2_TRACE_ARG
+  const uint32_t* q32 = nullptr;        // [R][4][32] bf16 pairs
+  const float* head_w = nullptr;        // [R][4] or null
+  const uint4* kdata = nullptr;         // bf16 keys: [n_slots][8] 16-byte chunks; FP8 keys: [n_slots][4] (64 codes)
+  const float* kscale = nullptr;        // FP8 keys: [n_slots] scales; null for bf16 keys
+  SlotMap map = {};
+  const int32_t* row_seq = nullptr;
+  const int32_t* seq_len = nullptr;
+  const int32_t* cand = nullptr;        // [R][n_cand] or null
+  int32_t n_cand = 0;
+  int32_t R = 0;
+  int32_t n_max = 0;
+  int32_t steps_per_row = 0;            // 64-position steps: ceil(n_max/64) (scan) or ceil(n_cand/8) (Reindex)
+  int64_t score_stride = 0;
+  int64_t bmax_stride = 0;
+  int64_t max64_stride = 0;
+  float* scores = nullptr;
+  float* block_max = nullptr;           // [R][ceil(n_max/8)] maxima of 8 positions (scan, optional)
+  float* max64 = nullptr;               // [R][ceil(n_max/64)] maxima of 64 positions (scan, optional)
+  const int32_t* row_list = nullptr;    // optional: score only rows row_list[0 .. *row_list_count)
+  const uint32_t* row_list_count = nullptr;
+#ifdef CSA2_TRACE
+  uint64_t* trace = nullptr;
+#endif
 };
 
 // Top-k over level 0 of a tree of maxima (level l+1 = maxima of 8 of level l).

@@ -79,7 +79,15 @@ typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
  *                        bit 3 sign, bits 2..1 exponent, bit 0 mantissa);
  *                scale = [n_slots][32] uint8, E4M3 (OCP E4M3FN) scale of
  *                        channels 16j .. 16j+15 in byte j.
- *   indexer K:   data  = [n_slots][64] bf16; scale = NULL.
+ *   indexer K:   data  = [n_slots][64] bf16 (16-byte aligned); scale = NULL;
+ *                or, FP8 indexer keys, data = [n_slots][64] uint8 OCP E4M3FN
+ *                codes (no NaN codes; 8-byte aligned) and scale = [n_slots]
+ *                float32 (4-byte aligned, finite, >= 0), passed through
+ *                this uint8 pointer: 68 B per position, the entry under which
+ *                the pages' 890 B per token of global KV cache adds up with
+ *                the 288-B FP4 main-KV entry (890 = 2.5 x (288 + 68)).
+ *                The FP8 form is read by csa2_index_score and by the
+ *                Full/Reindex layers of csa2_layer_step / csa2_group_step.
  * Slot of position p of sequence b:
  *   page_table == NULL : b * seq_stride + p
  *   page_table != NULL : page_table[b * max_pages + p / page_size] * page_size
@@ -106,6 +114,9 @@ typedef struct {
  * multiply-adds in channel order starting from +0, combined as
  * ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)); then ReLU; then
  * (w0*r0 + w1*r1) + (w2*r2 + w3*r3) with each product rounded on its own.
+ * FP8 indexer keys: the chains run over the exact E4M3 values and each head's
+ * dot product is multiplied by the position's scale (one float32 rounding)
+ * before the ReLU.
  *
  * cand_blocks == NULL (scan):  scores[r][p] for p < L (entries p >= L are not
  *   written; a position below L whose slot is absent scores -inf); if

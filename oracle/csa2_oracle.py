@@ -331,11 +331,16 @@ def reindex_topk(q_bits, k_bits_seq, cand_blocks, L: int, k: int = 512, w=None,
     """Reindex layer: re-score the candidate positions with the layer's own
     indexer query against the shared indexer keys, then Top-k over them with
     ties to the lower position.  Without candidates every position is scored."""
+    return reindex_topk_from(lambda pos: index_scores_chunked(q_bits, k_bits_seq[pos], w), cand_blocks, L, k,
+                             block)
+
+
+def reindex_topk_from(score_fn, cand_blocks, L: int, k: int = 512, block: int = 8) -> np.ndarray:
+    """reindex_topk with the scores of given positions from score_fn(pos)."""
     if cand_blocks is None:
-        return topk(index_scores_chunked(q_bits, k_bits_seq[:L], w), k)
+        return topk(score_fn(np.arange(L)), k)
     pos = candidate_positions(cand_blocks, L, block)
-    s = index_scores(q_bits, k_bits_seq[pos], w)
-    sel = topk(s, k)
+    sel = topk(score_fn(pos), k)
     out = np.full(k, -1, dtype=np.int32)
     n = int(np.sum(sel >= 0))
     out[:n] = pos[sel[:n]]
@@ -411,18 +416,27 @@ FULL, REINDEX, REUSE = 0, 1, 2
 
 
 class Cache:
-    """Per-slot caches shared by a layer group: FP4 main KV and bf16 indexer K,
-    with the slot mapping of every sequence."""
+    """Per-slot caches shared by a layer group: FP4 main KV and the indexer K
+    (bf16, or FP8: E4M3 codes with a float32 scale per slot when k_idx_scale
+    is given), with the slot mapping of every sequence."""
 
     def __init__(self, kv_packed, kv_scale, k_idx_bits, seq_lens, page_table=None,
-                 page_size: int = 64, seq_stride: int = 0):
+                 page_size: int = 64, seq_stride: int = 0, k_idx_scale=None):
         self.kv_packed = kv_packed
         self.kv_scale = kv_scale
         self.k_idx = k_idx_bits
+        self.k_idx_scale = k_idx_scale
         self.seq_lens = list(seq_lens)
         self.page_table = page_table
         self.page_size = page_size
         self.seq_stride = seq_stride
+
+    def scores(self, q_bits, b: int, pos, w=None) -> np.ndarray:
+        """Indexer scores of positions `pos` of sequence b (O4)."""
+        s = self.slots(b, np.asarray(pos, dtype=np.int64))
+        if self.k_idx_scale is None:
+            return index_scores_chunked(q_bits, self.k_idx[s], w)
+        return index_scores_fp8_chunked(q_bits, self.k_idx[s], self.k_idx_scale[s], w)
 
     def slots(self, b: int, pos) -> np.ndarray:
         return slot_of(b, pos, self.page_table, self.page_size, self.seq_stride)
@@ -470,15 +484,15 @@ def layer_step(mode: int, cache: Cache, state: GroupState, row_seq, q_idx_bits, 
         L = cache.seq_lens[b]
         w = None if head_w is None else head_w[r]
         if mode == FULL:
-            s = index_scores_chunked(q_idx_bits[r], cache.k_idx_seq(b), w)
+            s = cache.scores(q_idx_bits[r], b, np.arange(L), w)
             if hier:
                 state.cand[r] = hier_candidates(s, L, keep)
             if blocks_only:
                 continue
             state.topk[r] = topk(s, k)
         elif mode == REINDEX:
-            kseq = cache.k_idx_seq(b)
-            state.topk[r] = reindex_topk(q_idx_bits[r], kseq, state.cand[r], L, k, w)
+            state.topk[r] = reindex_topk_from(lambda pos: cache.scores(q_idx_bits[r], b, pos, w),
+                                              state.cand[r], L, k)
         elif mode != REUSE:
             raise ValueError(mode)
         sel = state.topk[r]

@@ -484,3 +484,36 @@ def test_byte_accounting_identity():
     entry = p.nbytes + s.nbytes
     assert entry == 288
     assert 2.5 * (entry + 68) == 890
+
+
+def test_fp8_cache_unit_scale_equals_bf16_cache_layers():
+    """A layer group over FP8 indexer keys at unit scale selects exactly what
+    the same group selects over the decoded keys in bf16 (Full with the
+    candidate build, then Reindex over the candidates)."""
+    rng, lens, _, stride, nslots = _small_group(False)
+    B = len(lens)
+    codes = _fp8_codes(rng, (nslots, 64))
+    codes &= 0xBF
+    K = bf16(O.e4m3_value(codes))
+    P = rng.integers(0, 256, (nslots, 256)).astype(np.uint8)
+    S = rng.integers(0x30, 0x40, (nslots, 32)).astype(np.uint8)
+    c_bf = O.Cache(P, S, K, lens, None, 64, stride)
+    c_f8 = O.Cache(P, S, codes, lens, None, 64, stride, k_idx_scale=np.ones(nslots, np.float32))
+    qi = bf16(rng.standard_normal((B, 4, 64)))
+    qr = bf16(rng.standard_normal((B, 4, 64)))
+    q = bf16(rng.standard_normal((B, 16, 512)))
+    sk = bf16(rng.standard_normal((B, 128, 512)))
+    sv = bf16(rng.standard_normal((B, 128, 512)))
+    st, ln = np.zeros(B, np.int32), np.array([128, 100, 64], np.int32)
+    rs = np.arange(B)
+    states = []
+    for cache in (c_bf, c_f8):
+        state = O.GroupState(B)
+        O.layer_step(O.FULL, cache, state, rs, qi, q, sk, sv, st, ln, 0.05, hier=True, k=32, keep=40)
+        full = [t.copy() for t in state.topk]
+        O.layer_step(O.REINDEX, cache, state, rs, qr, q, sk, sv, st, ln, 0.05, k=32)
+        states.append((full, state))
+    (f1, s1), (f2, s2) = states
+    for r in range(B):
+        assert np.array_equal(f1[r], f2[r]) and np.array_equal(s1.cand[r], s2.cand[r])
+        assert np.array_equal(s1.topk[r], s2.topk[r])
