@@ -40,26 +40,29 @@ def parse():
     p.add_argument("--no-1m", action="store_true", help="skip the 1M-context group (reported beside the default)")
     p.add_argument("--no-model", action="store_true",
                    help="skip the 38-layer decode step (reported beside the default)")
+    p.add_argument("--no-fp8", action="store_true",
+                   help="skip the 128K group on FP8 indexer keys (reported beside the default)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (for counter scaling)")
     return p.parse_args()
 
 
-def algorithmic_bytes(w):
-    """Per step: indexer keys 128 B/position + q_idx 512 B + Top-512 out 2048 B
-    per Full row; per attention row-layer 460 800 B (512 FP4 entries of 288 B,
-    window K+V 2*128*1024 B, query 16 KiB, output 32 KiB fp32, indices 2 KiB)."""
+def algorithmic_bytes(w, key_bytes=128):
+    """Per step: indexer keys key_bytes/position (128 bf16, 68 FP8) + q_idx
+    512 B + Top-512 out 2048 B per Full row; per attention row-layer 460 800 B
+    (512 FP4 entries of 288 B, window K+V 2*128*1024 B, query 16 KiB, output
+    32 KiB fp32, indices 2 KiB)."""
     per_attn = 512 * 288 + 2 * 128 * 1024 + 16 * 512 * 2 + 16 * 512 * 4 + 512 * 4
     scan = 0
     attn_layers = 0
     for m in w.schedule:
         if m == "F":
-            scan += sum(128 * L + 512 + 2048 for L in w.seq_lens)
+            scan += sum(key_bytes * L + 512 + 2048 for L in w.seq_lens)
             if w.hier:
                 scan += 8192 * w.B
         elif m == "I":
-            scan += w.B * (2048 * 8 * 128 + 8192 + 512 + 2048)
+            scan += w.B * (2048 * 8 * key_bytes + 8192 + 512 + 2048)
     for li, m in enumerate(w.schedule):
         if not (m == "F" and w.hier and w.full_blocks_only):
             attn_layers += 1
@@ -160,21 +163,39 @@ def data_desc(w):
     return f"synthetic (seeded; {kv}; bf16 N(0,1) queries, indexer keys and windows{extra})"
 
 
-def measure(w, steps, warmup, n_replicas):
+def fp8_keys(inp):
+    """The workload's bf16 indexer keys as FP8 keys (input preparation, on the
+    GPU): per slot, scale = max |k| / 448 and codes = E4M3(k / scale) by
+    torch's float8 cast (nearest, ties to even); an all-zero key gets scale 0."""
+    import dataclasses
+    import torch
+    k = inp.k_idx.view(torch.bfloat16).float()
+    amax = k.abs().amax(dim=1)
+    scale = (amax / 448.0).float()
+    x = (k / torch.where(scale > 0, scale, torch.ones_like(scale))[:, None]).clamp(-448.0, 448.0)
+    codes = x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return dataclasses.replace(inp, k_idx=codes, k_scale=scale.contiguous())
+
+
+def measure(w, steps, warmup, n_replicas, fp8=False):
     """Times `steps` whole steps of workload w (every group once) and, apart,
     back-to-back launches of its dominant kernel (the Full layer's scan, with
-    the arguments, grid and outputs of the step).  Returns a dict."""
+    the arguments, grid and outputs of the step).  fp8: the indexer keys in
+    the FP8 form.  Returns a dict."""
     import torch
     from fp4_kv_cache_02_amd import csa2, group
 
     t_setup = time.perf_counter()
     base = group.build_inputs(w)
+    if fp8:
+        base = fp8_keys(base)
     reps = [base]
     # extra replicas of the per-position caches (the per-layer inputs are small)
     for _ in range(max(0, n_replicas - 1)):
         reps.append(group.GroupInputs(kv_fp4=base.kv_fp4.clone(), kv_scale=base.kv_scale.clone(),
                                       k_idx=base.k_idx.clone(), seq_len=base.seq_len, page_table=base.page_table,
-                                      seq_stride=base.seq_stride, row_seq=base.row_seq, layers=base.layers))
+                                      seq_stride=base.seq_stride, row_seq=base.row_seq, layers=base.layers,
+                                      k_scale=None if base.k_scale is None else base.k_scale.clone()))
     runners = [group.GroupRunner(w, inp) for inp in reps]
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
@@ -191,7 +212,8 @@ def measure(w, steps, warmup, n_replicas):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
 
-    algo, scan_bytes, attn_layers = algorithmic_bytes(w)
+    key_bytes = 68 if fp8 else 128
+    algo, scan_bytes, attn_layers = algorithmic_bytes(w, key_bytes)
     res = {"ms": ms, "value": w.R * attn_layers / (ms * 1e-3), "attn_layers": attn_layers, "algo": algo,
            "replicas": len(runners), "setup_s": t_setup}
     if w.prefill_rows:
@@ -215,7 +237,7 @@ def measure(w, steps, warmup, n_replicas):
     b.record(stream)
     torch.cuda.synchronize()
     kern_ms = a.elapsed_time(b) / n_scan
-    scan_algo = sum(128 * L + 512 for L in w.seq_lens)   # indexer keys + query, per launch
+    scan_algo = sum(key_bytes * L + 512 for L in w.seq_lens)   # indexer keys + query, per launch
     res.update({"kern_ms": kern_ms, "scan_algo": scan_algo})
     return res
 
@@ -350,6 +372,16 @@ def main():
                              "ms_per_step": m2["ms"], "step_gbps": m2["algo"] / (m2["ms"] * 1e-3) / 1e9,
                              "scan_avg_launch_ms": m2["kern_ms"], "scan_achieved_gbps": a2,
                              "scan_frac": a2 / HBM_PEAK_GBPS, "replicas": m2["replicas"]}
+    if args.config == 1 and not args.no_fp8:
+        # the same 128K group with the indexer keys in the FP8 form (68 B per
+        # position: 64 E4M3 codes and a float32 scale)
+        m8 = measure(w, args.steps, args.warmup, args.replicas, fp8=True)
+        a8 = m8["scan_algo"] / (m8["kern_ms"] * 1e-3) / 1e9
+        out["fp8_indexer_keys"] = {"workload": w.name + "_fp8keys", "value": m8["value"], "unit": "tokens/s/layer",
+                                   "ms_per_step": m8["ms"], "scan_avg_launch_ms": m8["kern_ms"],
+                                   "scan_algorithmic_bytes_per_launch": m8["scan_algo"],
+                                   "scan_achieved_gbps": a8, "scan_frac": a8 / HBM_PEAK_GBPS,
+                                   "replicas": m8["replicas"]}
     if args.config == 1 and not args.no_model:
         # the whole decode step's CSA2 layers: encoder (18, ratio 2) + decoder (20)
         ws = synth.model_step()

@@ -104,8 +104,15 @@ CSA2_DEV uint4 key_chunk(const uint4* __restrict__ kd, const StepGeo& s, int i, 
 template <bool FP8>
 CSA2_DEV void chunk_values(uint4 kw, float (&kf)[8]) {
   if (FP8) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kf[e] = e4m3_to_float(((e < 4 ? kw.x : kw.y) >> (8 * (e & 3))) & 0xFFu);
+    // the hardware conversion of two OCP E4M3 codes (bytes 0-1 or 2-3 of the
+    // word) to float32, exact
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)kw.x, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)kw.x, true);
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)kw.y, false);
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)kw.y, true);
+    kf[0] = a[0]; kf[1] = a[1]; kf[2] = b[0]; kf[3] = b[1];
+    kf[4] = c[0]; kf[5] = c[1]; kf[6] = d[0]; kf[7] = d[1];
   } else {
     kf[0] = bf16_lo(kw.x); kf[1] = bf16_hi(kw.x); kf[2] = bf16_lo(kw.y); kf[3] = bf16_hi(kw.y);
     kf[4] = bf16_lo(kw.z); kf[5] = bf16_hi(kw.z); kf[6] = bf16_lo(kw.w); kf[7] = bf16_hi(kw.w);

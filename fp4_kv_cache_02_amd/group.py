@@ -51,6 +51,7 @@ class GroupInputs:
     seq_stride: int
     row_seq: Optional[torch.Tensor]
     layers: List[LayerInputs]
+    k_scale: Optional[torch.Tensor] = None   # FP8 indexer keys: [n_slots] float32 (k_idx then holds E4M3 codes)
 
 
 def layer_inputs_from_synth(w: synth.Workload, device="cuda") -> List[LayerInputs]:
@@ -144,7 +145,7 @@ class GroupRunner:
         self.inp = inp
         R = w.R
         self.kv = csa2.make_cache(inp.kv_fp4, inp.kv_scale, inp.page_table, seq_stride=inp.seq_stride)
-        self.kidx = csa2.make_cache(inp.k_idx, None, inp.page_table, seq_stride=inp.seq_stride)
+        self.kidx = csa2.make_cache(inp.k_idx, inp.k_scale, inp.page_table, seq_stride=inp.seq_stride)
         self.topk_idx = torch.full((R, csa2.TOPK), -1, dtype=torch.int32, device=device)
         self.cand = torch.full((R, csa2.KEEP_BLOCKS), -1, dtype=torch.int32, device=device)
         self.shared = csa2.make_shared(self.kv, self.kidx, inp.seq_len, w.n_max, self.topk_idx, self.cand,
