@@ -33,7 +33,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=1,
                    help="workload id (1: 128K decode group; 2: 1M decode group; 3: prefill chunk; 4: mixed serving; "
-                        "5: the 38 CSA2 layers of one decode step, encoder at ratio 2 + decoder, batch 8 at 128K)")
+                        "5: the 38 CSA2 layers of one decode step, encoder at ratio 2 + decoder, batch 8 at 128K; "
+                        "6: the prefill chunk of 3 with its own compressed entries under the completion mask)")
     p.add_argument("--replicas", type=int, default=3,
                    help="input replicas cycled per step so the 256 MB last-level cache cannot serve them")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -121,7 +122,7 @@ def cpu_baseline(w, min_seconds):
             P[sl], S[sl] = pool_p[m], pool_s[m]
         else:
             P[sl], S[sl] = O.quantize_fp4(synth.gen_kv_values(w, b, 0, L))
-    cache = O.Cache(P, S, K, w.seq_lens, pt, 64, 0 if w.paged else w.n_max)
+    cache = O.Cache(P, S, K, w.seq_lens, pt, 64, w.slot_stride)
     layer_in = []
     for li, m in enumerate(w.schedule):
         k, v, _, st, ln = synth.gen_swa(w, li)
@@ -135,9 +136,10 @@ def cpu_baseline(w, min_seconds):
         for li, m in enumerate(w.schedule):
             qi, q, k, v, st, ln = layer_in[li]
             blocks_only = m == "F" and w.hier and w.full_blocks_only
-            row_seq = [0] * w.R if w.prefill_rows else list(range(w.R))
+            row_seq = list(w.row_seq())
             O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln,
-                         1.0 / math.sqrt(512), hier=w.hier, blocks_only=blocks_only, rows=rows)
+                         1.0 / math.sqrt(512), hier=w.hier, blocks_only=blocks_only, rows=rows,
+                         swa_shared=w.shared_slots)
             attended += 0 if blocks_only else len(rows)
         reps += 1
         dt = time.perf_counter() - t0
@@ -326,7 +328,8 @@ def main():
     m = measure(w, args.steps, args.warmup, args.replicas if not w.prefill_rows else 1)
     if w.prefill_rows:
         # indexer 512 flop per (row, entry); attention 20.97 MFLOP per row-layer
-        flops = w.R * w.n_max * 512 + m["attn_layers"] * w.R * 2 * 2 * 16 * 512 * (512 + 128)
+        visible = sum(w.seq_lens) if w.shared_slots else w.R * w.n_max
+        flops = visible * 512 + m["attn_layers"] * w.R * 2 * 2 * 16 * 512 * (512 + 128)
         tflops = flops / (m["ms"] * 1e-3) / 1e12
         roof = {"kernel": "whole prefill group step (MFMA indexer passes, selection, attention)", "bound": "mfma",
                 "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

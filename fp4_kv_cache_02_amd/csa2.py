@@ -45,7 +45,7 @@ class csa2_layer_args(ctypes.Structure):
     _fields_ = [("R", ctypes.c_int32), ("row_seq", c_ptr), ("q_idx", c_ptr), ("head_w", c_ptr), ("q", c_ptr),
                 ("swa_k", c_ptr), ("swa_v", c_ptr), ("S", ctypes.c_int32), ("swa_start", c_ptr),
                 ("swa_len", c_ptr), ("sm_scale", ctypes.c_float), ("blocks_only", ctypes.c_int32),
-                ("out", c_ptr), ("lse", c_ptr)]
+                ("out", c_ptr), ("lse", c_ptr), ("swa_shared", ctypes.c_int32)]
 
 
 def _sig(name, res, args):
@@ -210,7 +210,8 @@ def make_shared(kv: csa2_cache, k_idx: csa2_cache, seq_len, n_max: int, topk_idx
 
 
 def make_layer_args(q, swa_k, swa_v, swa_start, swa_len, sm_scale: float, out, lse=None, q_idx=None,
-                    head_w=None, row_seq=None, blocks_only: bool = False, R: Optional[int] = None) -> csa2_layer_args:
+                    head_w=None, row_seq=None, blocks_only: bool = False, R: Optional[int] = None,
+                    swa_shared: bool = False) -> csa2_layer_args:
     a = csa2_layer_args()
     a.R = int(R if R is not None else (q.shape[0] if q is not None else q_idx.shape[0]))
     a.row_seq = _p(row_seq)
@@ -226,6 +227,7 @@ def make_layer_args(q, swa_k, swa_v, swa_start, swa_len, sm_scale: float, out, l
     a.blocks_only = 1 if blocks_only else 0
     a.out = _p(out)
     a.lse = _p(lse)
+    a.swa_shared = 1 if swa_shared else 0
     a._keep = (q, swa_k, swa_v, swa_start, swa_len, out, lse, q_idx, head_w, row_seq)
     return a
 

@@ -238,6 +238,7 @@ struct AttnLayerIn {
   const int32_t *swa_start, *swa_len;
   float *out, *lse;
   float sm_scale;
+  int32_t swa_shared;
 };
 
 csa2_status do_attn(const AttnLayerIn* L, int n_layers, const csa2_cache* kv, const int32_t* row_seq,
@@ -254,6 +255,7 @@ csa2_status do_attn(const AttnLayerIn* L, int n_layers, const csa2_cache* kv, co
     a.layer[i].lse = L[i].lse;
     a.layer[i].S = L[i].S;
     a.layer[i].sm_scale = L[i].sm_scale;
+    a.layer[i].swa_shared = L[i].swa_shared ? 1 : 0;
   }
   a.n_layers = n_layers;
   a.kv = (const uint8_t*)kv->data;
@@ -277,7 +279,8 @@ bool attn_layer_ok(const csa2_layer_args* a) {
 }
 
 AttnLayerIn layer_in(const csa2_layer_args* a) {
-  return AttnLayerIn{a->q, a->swa_k, a->swa_v, a->S, a->swa_start, a->swa_len, a->out, a->lse, a->sm_scale};
+  return AttnLayerIn{a->q, a->swa_k, a->swa_v, a->S, a->swa_start, a->swa_len, a->out, a->lse, a->sm_scale,
+                     a->swa_shared};
 }
 
 // ------------------------------------------------------- layer index part --
@@ -340,8 +343,12 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
     float* scores = bp.take<float>((size_t)R * n_max);
     float* bmax = bp.take<float>((size_t)R * cdiv(n_max, 8));
     float* m64 = bp.take<float>((size_t)R * cdiv(n_max, 64));
-    // (one sequence: every row's row_seq entry is 0)
-    if (sh->B == 1 && a->row_seq && !blocks_only && !sh->k_idx.scale && prefill_shape(mode, R, n_max, sh->hier)) {
+    // every row reads the same slots: one sequence, or sequences that share
+    // them (contiguous caches with seq_stride 0: a chunk whose rows see
+    // different lengths of one context)
+    const bool one_context = sh->B == 1 || (!sh->kv.page_table && sh->kv.seq_stride == 0 &&
+                                            !sh->k_idx.page_table && sh->k_idx.seq_stride == 0);
+    if (one_context && a->row_seq && !blocks_only && !sh->k_idx.scale && prefill_shape(mode, R, n_max, sh->hier)) {
       // prefill chunk: matrix-core indexer with exact selection; the rows it
       // lists (too many candidates) take the exact scan and Top-k below
       const PrefWs pw = carve_prefill(bp, R, n_max);
@@ -351,6 +358,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       p.kdata = (const uint4*)sh->k_idx.data;
       p.map = make_slot_map(sh->k_idx);
       p.seq_len = sh->seq_len;
+      p.row_seq = a->row_seq;
       p.R = R;
       p.n_max = n_max;
       p.k = CSA2_TOPK;
@@ -548,7 +556,7 @@ csa2_status csa2_fp4_sparse_attn(const uint16_t* q, const csa2_cache* kv, const 
   if (ws_bytes < csa2_attn_workspace_bytes(R)) return CSA2_ERR_WORKSPACE;
   Bump bp{(char*)ws, kCtrlBytes};
   const AttnWs aw = carve_attn(bp, R, 1, k);
-  const AttnLayerIn L{q, swa_k, swa_v, S, swa_start, swa_len, out, lse, sm_scale};
+  const AttnLayerIn L{q, swa_k, swa_v, S, swa_start, swa_len, out, lse, sm_scale, 0};
   return do_attn(&L, 1, kv, row_seq, seq_len, idx, k, R, aw, (char*)ws, stream);
 }
 

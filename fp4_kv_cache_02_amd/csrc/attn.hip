@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     if (is_main)
       qk_main(sm, w, c, g, s);
     else
-      qk_win(Ly, sm, b, wst, wl, 32 * w, c, g, s);
+      qk_win(Ly, sm, Ly.swa_shared ? 0 : b, wst, wl, 32 * w, c, g, s);
     CSA2_MARK(a, 2);
 
     // ---- softmax statistics of the step (head c) ----
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     if (is_main)
       pv_main(sm, st, w, c, g);
     else
-      pv_win(Ly, sm, st, b, wst, wl, w, c, g);
+      pv_win(Ly, sm, st, Ly.swa_shared ? 0 : b, wst, wl, w, c, g);
     CSA2_MARK(a, 4);
     __syncthreads();    // P, slots and statistics may be overwritten by the next step
   }

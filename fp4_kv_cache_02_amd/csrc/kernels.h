@@ -64,24 +64,25 @@ constexpr int kTauMaxN = 131072;          // level-0 values per row it handles (
 // Prefill-chunk indexer on MFMA: every query row sees the positions of one
 // sequence (sequence 0).
 struct PrefArgs {
-  const uint32_t* q32;        // [R][4][32] bf16 pairs
-  const float* head_w;        // [R][4] or null
-  const uint4* kdata;         // indexer keys
-  SlotMap map;
-  const int32_t* seq_len;     // seq_len[0]: visible positions
-  int32_t R;
-  int32_t n_max;
-  int32_t k;
-  float* gmax;                // [R][ceil(n_max/64)] maxima of the approximate scores per 64 positions
-  int64_t gmax_stride;
-  float* kmax_part;           // [ceil(n_max/2048)] largest |key element| per chunk of 2048 positions
-  float* theta;               // [R] candidate threshold
-  uint32_t* cand_count;       // [R]
-  int32_t* cand;              // [R][cap] candidate positions
-  int32_t cap;
-  int32_t* fb_list;           // [R] rows whose candidates overflowed
-  uint32_t* fb_count;         // [1]
-  int32_t* out;               // [R][k] Top-k positions
+  const uint32_t* q32 = nullptr;        // [R][4][32] bf16 pairs
+  const float* head_w = nullptr;        // [R][4] or null
+  const uint4* kdata = nullptr;         // indexer keys
+  SlotMap map = {};
+  const int32_t* seq_len = nullptr;     // visible positions of row r: seq_len[row_seq[r]] (row_seq null: seq_len[0])
+  const int32_t* row_seq = nullptr;     // every row reads the same slots (one sequence, or sequences sharing them)
+  int32_t R = 0;
+  int32_t n_max = 0;
+  int32_t k = 0;
+  float* gmax = nullptr;                // [R][ceil(n_max/64)] maxima of the approximate scores per 64 positions
+  int64_t gmax_stride = 0;
+  float* kmax_part = nullptr;           // [ceil(n_max/2048)] largest |key element| per chunk of 2048 positions
+  float* theta = nullptr;               // [R] candidate threshold
+  uint32_t* cand_count = nullptr;       // [R]
+  int32_t* cand = nullptr;              // [R][cap] candidate positions
+  int32_t cap = 0;
+  int32_t* fb_list = nullptr;           // [R] rows whose candidates overflowed
+  uint32_t* fb_count = nullptr;         // [1]
+  int32_t* out = nullptr;               // [R][k] Top-k positions
 };
 
 struct MaximaArgs {
@@ -111,6 +112,7 @@ struct AttnLayer {
   float* lse;                   // [R][16] or null
   int32_t S;
   float sm_scale;
+  int32_t swa_shared;           // every row reads window buffer 0
 };
 
 struct AttnArgs {

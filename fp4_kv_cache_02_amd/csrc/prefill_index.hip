@@ -98,12 +98,20 @@ struct PassSmem {
 //   B (keys): column n = c = position, elements k = 8g .. 8g+7;
 //   D: lane holds rows 4g .. 4g+3 of column c = the four heads of row 4mt+g
 //     at position c, so each lane finishes one (row, position) score.
+// Visible positions of row r (rows past R: none).
+CSA2_DEV int pref_row_len(const PrefArgs& a, int r) {
+  if (r >= a.R) return 0;
+  return min(a.seq_len[a.row_seq ? a.row_seq[r] : 0], a.n_max);
+}
+
 template <int PASS, bool HAS_W>
 __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   __shared__ PassSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int L = min(a.seq_len[0], a.n_max);
+  // positions any row may see (rows with their own lengths: all up to n_max;
+  // each row's own length masks its scores below)
+  const int L = a.row_seq ? a.n_max : min(a.seq_len[0], a.n_max);
   const int64_t x0 = (int64_t)blockIdx.x * kPChunk;
   if (x0 >= L) return;
   const int n_here = (int)min((int64_t)kPChunk, (int64_t)L - x0);
@@ -119,13 +127,15 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) A[mt][kh] = to_bf16x8(qp[4 * kh + g]);
   }
-  // this lane's output rows
+  // this lane's output rows and their visible lengths
   int orow[4];
+  int olen[4];
   float w[4][4];
   float th[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     orow[mt] = rw0 + 4 * mt + g;
+    olen[mt] = pref_row_len(a, orow[mt]);
     const int rr = min(orow[mt], a.R - 1);
 #pragma unroll
     for (int h = 0; h < 4; ++h) w[mt][h] = HAS_W ? a.head_w[(int64_t)rr * 4 + h] : 1.0f;
@@ -138,10 +148,11 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
     const int row = rw0 + c;
     const float t = row < a.R ? a.theta[row] : __builtin_inff();
     const int rr = min(row, a.R - 1);
+    const int lrow = pref_row_len(a, row);
 #pragma unroll
     for (int i = 0; i < kPGroupsWG / 4; ++i) {
       const int64_t grp = x0 / kPGroup + g + 4 * i;
-      const bool ok = grp * kPGroup < L;
+      const bool ok = grp * kPGroup < lrow;
       const float gm = ok ? a.gmax[(int64_t)rr * a.gmax_stride + (ok ? grp : 0)] : -__builtin_inff();
       const uint64_t bits = __ballot(gm >= t);
       if (lane == 0) sm.act[wave][i] = bits;
@@ -225,8 +236,9 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
           sc = (w[mt][0] * r0 + w[mt][1] * r1) + (w[mt][2] * r2 + w[mt][3] * r3);
         else
           sc = (r0 + r1) + (r2 + r3);
-        if (PASS == 0) gm[mt] = fmaxf(gm[mt], pres ? sc : -__builtin_inff());
-        hit[mt] = PASS == 1 && pres && orow[mt] < a.R && sc >= th[mt];
+        const bool vis = pres && pos < olen[mt];
+        if (PASS == 0) gm[mt] = fmaxf(gm[mt], vis ? sc : -__builtin_inff());
+        hit[mt] = PASS == 1 && vis && orow[mt] < a.R && sc >= th[mt];
       }
       if (PASS == 1) {
         // hits as bits: lane (c, g) of tile mt is position 16 nt + c of row
@@ -249,7 +261,7 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const float v = row16_max(gm[mt]);
-          if (c == 0 && orow[mt] < a.R && grp * kPGroup < L) a.gmax[(int64_t)orow[mt] * a.gmax_stride + grp] = v;
+          if (c == 0 && orow[mt] < a.R && grp * kPGroup < olen[mt]) a.gmax[(int64_t)orow[mt] * a.gmax_stride + grp] = v;
           gm[mt] = -__builtin_inff();
         }
       }
@@ -310,7 +322,7 @@ __global__ __launch_bounds__(256) void pref_threshold_kernel(PrefArgs a) {
   const int r = blockIdx.x * 4 + wave;
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.fb_count = 0u;
   if (r >= a.R) return;
-  const int L = min(a.seq_len[0], a.n_max);
+  const int L = pref_row_len(a, r);
   const int G = (L + kPGroup - 1) / kPGroup;
   uint32_t key[NREG];
 #pragma unroll

@@ -68,6 +68,9 @@ def k_idx_slots_from_synth(w: synth.Workload, n_slots: int, page_table) -> np.nd
     """Indexer keys of every sequence placed at their slots ([n_slots, 64] bf16 bits)."""
     q_full = synth.gen_q_idx(w, 0) if w.planted > 0 else None
     out = np.zeros((n_slots, synth.DI), np.uint16)
+    if w.shared_slots:          # one set of keys that every row's sequence reads
+        out[:w.n_max] = synth.gen_k_idx_seq(w, 0, q_full, L=w.n_max)
+        return out
     for b in range(w.B):
         kb = synth.gen_k_idx_seq(w, b, q_full)
         out[synth.slot_index(w, page_table, b, np.arange(w.seq_lens[b]))] = kb
@@ -114,11 +117,11 @@ def build_inputs(w: synth.Workload, kv_fp4=None, kv_scale=None, device="cuda", k
         kv_fp4, kv_scale = _dev(kv_fp4, device), _dev(kv_scale, device)
     row_seq = None
     if w.prefill_rows:
-        row_seq = torch.zeros(w.R, dtype=torch.int32, device=device)
+        row_seq = _dev(w.row_seq().astype(np.int32), device)
     return GroupInputs(kv_fp4=kv_fp4, kv_scale=kv_scale, k_idx=_dev(kidx, device),
                        seq_len=_dev(np.array(w.seq_lens, np.int32), device),
                        page_table=_dev(page_table, device) if page_table is not None else None,
-                       seq_stride=0 if w.paged else w.n_max, row_seq=row_seq,
+                       seq_stride=w.slot_stride, row_seq=row_seq,
                        layers=layer_inputs_from_synth(w, device))
 
 
@@ -165,7 +168,7 @@ class GroupRunner:
             blocks_only = (m == "F" and w.hier and w.full_blocks_only)
             self.args.append(csa2.make_layer_args(L.q, L.swa_k, L.swa_v, L.swa_start, L.swa_len, SM_SCALE,
                                                   self.out[li], self.lse[li], q_idx=L.q_idx, row_seq=inp.row_seq,
-                                                  blocks_only=blocks_only, R=R))
+                                                  blocks_only=blocks_only, R=R, swa_shared=w.shared_slots))
 
         self.group_args = [csa2.make_layer_array(self.args[li0:li0 + n]) for li0, n in self.groups]
 

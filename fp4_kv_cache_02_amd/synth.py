@@ -68,6 +68,7 @@ class Workload:
     raw_fp4: bool = False        # main KV drawn directly as FP4 / E4M3 bytes
     kv_pool: int = 0             # >0: main-KV vectors drawn from a pool of this size
     full_blocks_only: bool = False  # Full layer stops after the candidate build
+    shared_slots: bool = False   # every sequence reads the same slots (prefill rows with their own lengths)
 
     @property
     def B(self) -> int:
@@ -84,6 +85,18 @@ class Workload:
     @property
     def layers(self) -> int:
         return len(self.schedule)
+
+    @property
+    def slot_stride(self) -> int:
+        """Contiguous caches: slot = seq * slot_stride + pos (0: shared slots)."""
+        return 0 if (self.paged or self.shared_slots) else self.n_max
+
+    def row_seq(self) -> np.ndarray:
+        """Sequence of every query row: one sequence for a prefill chunk, one
+        per row otherwise (rows of a chunk with their own lengths included)."""
+        if self.prefill_rows and not self.shared_slots:
+            return np.zeros(self.R, np.int64)
+        return np.arange(self.R, dtype=np.int64)
 
 
 def _loguniform_lengths(seed: int, B: int, lo: int, hi: int) -> List[int]:
@@ -115,6 +128,16 @@ def workload(cfg: int, reduced: bool = False) -> Workload:
                             prefill_rows=64, prefill_pos=16384, raw_fp4=True)
         return Workload("cfg3_prefill_F5R_C4096_E131072", seed, [131072], "FRRRRR",
                         prefill_rows=4096, prefill_pos=262144, raw_fp4=True)
+    if cfg == 6:
+        # config 3 with the chunk's own compressed entries (ratio 2: entry j
+        # of the chunk covers its tokens 2j, 2j+1): row i sees the 131072
+        # prior entries and the chunk entries completed by its token,
+        # j < floor((i + 1) / 2) -- a completion mask over one shared cache
+        C, E = (64, 8192) if reduced else (4096, 131072)
+        lens = [E + (i + 1) // 2 for i in range(C)]
+        name = f"cfg3c_causal_prefill_F5R_C{C}_E{E}+{C // 2}" + ("_reduced" if reduced else "")
+        return Workload(name, 1006 + 100, lens, "FRRRRR", prefill_rows=C, prefill_pos=2 * E, raw_fp4=True,
+                        shared_slots=True)
     if cfg == 4:
         if reduced:
             lens = _loguniform_lengths(seed, 5, 2048, 40000)
@@ -155,6 +178,8 @@ def slots_layout(w: Workload):
     physical page ids are a seeded permutation of all pages in use.
     Returns (n_slots, page_table [B, max_pages] int32 or None, max_pages).
     """
+    if w.shared_slots:
+        return w.n_max, None, 0
     if not w.paged:
         return w.B * w.n_max, None, 0
     npages = [(L + PAGE - 1) // PAGE for L in w.seq_lens]
@@ -172,7 +197,7 @@ def slots_layout(w: Workload):
 def slot_index(w: Workload, page_table, b: int, pos: np.ndarray) -> np.ndarray:
     pos = np.asarray(pos, dtype=np.int64)
     if page_table is None:
-        return b * w.n_max + pos
+        return b * w.slot_stride + pos
     return page_table[b, pos // PAGE].astype(np.int64) * PAGE + pos % PAGE
 
 
@@ -189,14 +214,14 @@ def gen_q_idx(w: Workload, layer: int) -> np.ndarray:
     return out
 
 
-def gen_k_idx_seq(w: Workload, b: int, q_idx_full: Optional[np.ndarray]) -> np.ndarray:
+def gen_k_idx_seq(w: Workload, b: int, q_idx_full: Optional[np.ndarray], L: Optional[int] = None) -> np.ndarray:
     """Indexer keys of sequence b, [L_b, 64] bf16 bits, with optional planted keys.
 
     Planted keys (a fraction ``w.planted`` of positions, chosen without
     replacement) are bf16(u + 0.5 z) with u = 8 * qbar / |qbar|, qbar the sum of
     the Full layer's four indexer query heads and z ~ N(0, I).
     """
-    L = w.seq_lens[b]
+    L = w.seq_lens[b] if L is None else L
     k = rng_for(w.seed, T_KIDX, b).standard_normal((L, DI), dtype=np.float32)
     if w.planted > 0:
         r = rng_for(w.seed, T_PLANT, b)

@@ -239,6 +239,10 @@ typedef struct {
   int32_t blocks_only;     /* Full + hier: stop after the candidate build          */
   float* out;              /* [R][16][512]                                         */
   float* lse;              /* [R][16] or NULL                                      */
+  int32_t swa_shared;      /* nonzero: swa_k/swa_v hold one buffer [1][S][512] that
+                              every row reads at its own swa_start (the rows of a
+                              prefill chunk given as sequences of their own that
+                              share the caches' slots, seq_stride 0)              */
 } csa2_layer_args;
 
 /*

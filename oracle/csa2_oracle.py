@@ -464,15 +464,16 @@ class GroupState:
 def layer_step(mode: int, cache: Cache, state: GroupState, row_seq, q_idx_bits, q_bits,
                swa_k, swa_v, swa_start, swa_len, sm_scale: float, hier: bool = False,
                head_w=None, k: int = 512, keep: int = 2048, blocks_only: bool = False,
-               rows=None):
+               rows=None, swa_shared: bool = False):
     """One CSA2 layer over the query rows `rows` (default all).
 
     Full: score every visible position with the layer's indexer query, keep
     Top-k (and, with `hier`, the candidate blocks), attend.  Reindex: score the
     candidate positions with the layer's own indexer query, keep Top-k, attend.
     Reuse: attend over the most recent Top-k.  Every mode attends with the
-    layer's own query and window.  `blocks_only` stops a Full layer after the
-    candidate build (no Top-k, no attention).
+    layer's own query and window (swa_k[b], or swa_k[0] for every row when
+    `swa_shared`).  `blocks_only` stops a Full layer after the candidate
+    build (no Top-k, no attention).
 
     Returns {row: (out, lse)} for the rows attended.
     """
@@ -498,5 +499,6 @@ def layer_step(mode: int, cache: Cache, state: GroupState, row_seq, q_idx_bits, 
         sel = state.topk[r]
         kv = cache.kv_rows(b, sel)
         st, ln = int(swa_start[r]), int(swa_len[r])
-        results[r] = attention(q_bits[r], kv, swa_k[b, st:st + ln], swa_v[b, st:st + ln], sm_scale)
+        bw = 0 if swa_shared else b
+        results[r] = attention(q_bits[r], kv, swa_k[bw, st:st + ln], swa_v[bw, st:st + ln], sm_scale)
     return results

@@ -33,7 +33,7 @@ def oracle_caches(w, K):
                 P[sl], S[sl] = pp[m], ps[m]
             else:
                 P[sl], S[sl] = O.quantize_fp4(synth.gen_kv_values(w, b, 0, L))
-    return O.Cache(P, S, K, w.seq_lens, pt, 64, 0 if w.paged else w.n_max), P, S, pt
+    return O.Cache(P, S, K, w.seq_lens, pt, 64, w.slot_stride), P, S, pt
 
 
 def run_fullsize(w, rows):
@@ -45,7 +45,7 @@ def run_fullsize(w, rows):
     run = group.GroupRunner(w, inp)
     cache, P, S, _ = oracle_caches(w, K)
     gP, gS = host(inp.kv_fp4), host(inp.kv_scale)
-    row_seq = np.zeros(w.R, np.int64) if w.prefill_rows else np.arange(w.R)
+    row_seq = w.row_seq()
     state = O.GroupState(w.R)
     for gi, (li0, n) in enumerate(run.groups):
         say(w.name, "group", gi, w.schedule[li0:li0 + n])
@@ -58,7 +58,7 @@ def run_fullsize(w, rows):
             q = synth.gen_q(w, li)
             blocks_only = m == "F" and w.hier and w.full_blocks_only
             res = O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln, group.SM_SCALE,
-                               hier=w.hier, blocks_only=blocks_only, rows=rows)
+                               hier=w.hier, blocks_only=blocks_only, rows=rows, swa_shared=w.shared_slots)
             if m == "F" and w.hier:
                 gc = host(run.cand)
                 for r in rows:
@@ -71,7 +71,7 @@ def run_fullsize(w, rows):
                 assert np.array_equal(gt[r], state.topk[r]), (w.name, li, r)
                 b = int(row_seq[r])
                 pos = state.topk[r][state.topk[r] >= 0]
-                sl = O.slot_of(b, pos, pt, 64, 0 if w.paged else w.n_max)
+                sl = O.slot_of(b, pos, pt, 64, w.slot_stride)
                 assert np.array_equal(gP[sl], P[sl]) and np.array_equal(gS[sl], S[sl]), (w.name, li, r)
                 e = rel_err(go[r], res[r][0])
                 assert np.all(e <= ATTN_TOL), (w.name, li, r, e.max())
@@ -99,4 +99,13 @@ def test_fullsize_cfg4_mixed_serving():
     w = synth.workload(4)
     lens = np.array(w.seq_lens)
     rows = sorted(set([int(lens.argmax()), int(lens.argmin()), 5, 17]))
+    run_fullsize(w, rows)
+
+
+def test_fullsize_cfg6_causal_prefill():
+    """Config 3 with the chunk's own 2048 entries under the completion mask
+    (matrix-core indexer with per-row lengths)."""
+    w = synth.workload(6)
+    rng = np.random.default_rng(8)
+    rows = sorted(set([0, 1, 2, 127, 2048, w.R - 2, w.R - 1] + list(rng.choice(w.R, size=5, replace=False))))
     run_fullsize(w, rows)

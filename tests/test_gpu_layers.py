@@ -40,8 +40,8 @@ def run_and_compare(w, by_group: bool, check_rows=None):
     P, S, K, pt, n_slots = numpy_caches(w)
     inp = group.build_inputs(w, kv_fp4=P, kv_scale=S)
     run = group.GroupRunner(w, inp)
-    cache = O.Cache(P, S, K, w.seq_lens, pt, 64, 0 if w.paged else w.n_max)
-    row_seq = np.zeros(w.R, np.int64) if w.prefill_rows else np.arange(w.R)
+    cache = O.Cache(P, S, K, w.seq_lens, pt, 64, w.slot_stride)
+    row_seq = w.row_seq()
     state = O.GroupState(w.R)
     rows = list(range(w.R)) if check_rows is None else check_rows
     units = run.groups if by_group else [(li, 1) for li in range(len(w.schedule))]
@@ -59,7 +59,7 @@ def run_and_compare(w, by_group: bool, check_rows=None):
             q = synth.gen_q(w, li)
             blocks_only = m == "F" and w.hier and w.full_blocks_only
             res = O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln, group.SM_SCALE,
-                               hier=w.hier, blocks_only=blocks_only, rows=rows)
+                               hier=w.hier, blocks_only=blocks_only, rows=rows, swa_shared=w.shared_slots)
             if m == "F" and w.hier:
                 gc = host(run.cand)
                 for r in rows:
@@ -87,6 +87,14 @@ def test_group_reduced_by_group(cfg):
 
 def test_group_prefill_reduced():
     run_and_compare(synth.workload(3, reduced=True), by_group=True)
+
+
+def test_group_causal_prefill_reduced():
+    """A prefill chunk whose rows also see the chunk's own compressed entries
+    once complete (each row a sequence of its own over shared slots, one
+    shared window buffer)."""
+    run_and_compare(synth.workload(6, reduced=True), by_group=True)
+    run_and_compare(synth.workload(6, reduced=True), by_group=False, check_rows=[0, 1, 2, 31, 62, 63])
 
 
 def test_group_prefill_rows_mode():

@@ -106,3 +106,38 @@ def test_prefill_indexer_near_ties(C):
 
 def test_prefill_indexer_duplicates_fallback(C):
     _run(C, R=288, L=90000, n_max=90000, kind="dup", paged=False, weighted=True, seed=504, n_check=24)
+
+
+def test_prefill_indexer_causal_rows(C):
+    """Rows with their own visible lengths (row i sees L0 + floor((i + 1) / 2)
+    positions of one shared cache: each row a sequence of its own with
+    seq_stride 0) on the matrix-core indexer."""
+    rng = np.random.default_rng(505)
+    R, L0 = 288, 66000
+    lens = [L0 + (i + 1) // 2 for i in range(R)]
+    n_max = max(lens)
+    keys = _keys(rng, n_max, "random")
+    q_idx = bf16(rng, (R, 4, 64))
+    P, S = rand_fp4(rng, n_max)
+    q = bf16(rng, (R, 16, 512))
+    Sw = R + 127
+    swk, swv = bf16(rng, (1, Sw, 512)), bf16(rng, (1, Sw, 512))
+    say("prefill indexer, causal rows R", R, "L0", L0, "n_max", n_max)
+    kv = C.make_cache(dev(P), dev(S), seq_stride=0)
+    kc = C.make_cache(dev(keys), seq_stride=0)
+    seq_len = dev(np.array(lens, np.int32))
+    topk = torch.full((R, 512), -7, dtype=torch.int32, device="cuda")
+    sh = C.make_shared(kv, kc, seq_len, n_max, topk)
+    out = torch.zeros((R, 16, 512), device="cuda")
+    args = C.make_layer_args(dev(q), dev(swk), dev(swv), dev(np.arange(R, dtype=np.int32)),
+                             dev(np.full(R, 128, np.int32)), 512 ** -0.5, out, q_idx=dev(q_idx),
+                             row_seq=dev(np.arange(R, dtype=np.int32)), swa_shared=True)
+    ws = workspace(C.csa2_workspace_bytes(FULL, R, n_max, False))
+    C.csa2_layer_step(FULL, args, sh, ws)
+    torch.cuda.synchronize()
+    g = host(topk)
+    rows = sorted(set([0, 1, 2, R - 2, R - 1] + list(rng.choice(R, size=20, replace=False))))
+    for r in rows:
+        ref = O.topk(O.index_scores_chunked(q_idx[r], keys[:lens[r]]), 512)
+        assert np.array_equal(g[r], ref), (r, np.setdiff1d(g[r], ref)[:8], np.setdiff1d(ref, g[r])[:8])
+    assert np.all(np.isfinite(host(out)))
