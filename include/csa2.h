@@ -64,7 +64,7 @@ typedef enum {
   CSA2_OK = 0,
   CSA2_ERR_NULL = 1,        /* a required pointer is NULL                    */
   CSA2_ERR_SHAPE = 2,       /* a size or count is out of range               */
-  CSA2_ERR_UNSUPPORTED = 3, /* a layout this build does not implement        */
+  CSA2_ERR_UNSUPPORTED = 3, /* a layout the library does not implement      */
   CSA2_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required    */
   CSA2_ERR_HIP = 5          /* a HIP launch failed                           */
 } csa2_status;

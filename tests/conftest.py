@@ -14,8 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run only where a GPU is present; on a CPU machine they are skipped
-    # (the round-end GPU run selects them with -m gpu on a GPU machine).
+    # GPU tests run only where a GPU is present; on a machine without one they
+    # are skipped (select them with -m gpu where a GPU is present).
     try:
         import torch
         have_gpu = torch.cuda.is_available()
