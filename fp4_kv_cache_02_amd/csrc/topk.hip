@@ -75,6 +75,11 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
 
   // ---- top level: 4 values per thread ----
   RegKeys top;
+  // top level built from level 0 (T == 1 without stored maxima): the 32
+  // level-0 values of this thread's 4 groups stay in registers and are the
+  // children of the descent (no reload, no compaction of the top level)
+  const bool from0 = !direct && T == 1;
+  float v0[kRegPer * 8];
   if (direct) {
     const float* base = lv_row(a, T, r);
     float v[kRegPer];
@@ -90,7 +95,7 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
   } else {
     const float* base = lv_row(a, T - 1, r);
     const int64_t nb = lv_count(n0, T - 1);
-    float v[kRegPer * 8];
+    float (&v)[kRegPer * 8] = v0;
     if (((uintptr_t)base & 15u) == 0 && 8 * kRegPer * tid + 8 * kRegPer <= nb) {
 #pragma unroll
       for (int q = 0; q < 2 * kRegPer; ++q) {
@@ -131,8 +136,11 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
   ge.n_eq = 0;
   ge.exact = false;
   int cur = 0;
-  int n_par = (int)block_compact(sm, top, ge, K, [&](uint32_t pos, int e) { par[0][pos] = e; });
-  __syncthreads();
+  int n_par = 0;
+  if (!from0) {
+    n_par = (int)block_compact(sm, top, ge, K, [&](uint32_t pos, int e) { par[0][pos] = e; });
+    __syncthreads();
+  }
 
   // ---- descend: children of the kept groups with value >= tau ----
   for (int l = T - 1; l >= 0; --l) {
@@ -141,17 +149,29 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
     // children of this thread's parents kRegPer*t .. +kRegPer-1; every load
     // is unconditional (clamped index) so all of them are in flight at once
     // (a load under a branch is waited for before the next branch)
-    int64_t idx[kRegPer * 8];
+    int32_t idx[kRegPer * 8];       // (level counts stay below 2^31)
     float v[kRegPer * 8];
+    if (from0) {
+      // parents: this thread's own top-level groups kRegPer*t + p
 #pragma unroll
-    for (int p = 0; p < kRegPer; ++p) {
-      const int pi = kRegPer * tid + p;
-      const int64_t g = (pi < n_par) ? (int64_t)par[cur][pi] : -1;
+      for (int p = 0; p < kRegPer; ++p) {
+        const int64_t g = top.v[p] >= tau ? (int64_t)(kRegPer * tid + p) : -1;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) idx[8 * p + c] = (g >= 0 && g * 8 + c < n) ? g * 8 + c : -1;
+        for (int c = 0; c < 8; ++c) idx[8 * p + c] = (g >= 0 && g * 8 + c < n) ? (int32_t)(g * 8 + c) : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kRegPer * 8; ++j) v[j] = v0[j];
+    } else {
+#pragma unroll
+      for (int p = 0; p < kRegPer; ++p) {
+        const int pi = kRegPer * tid + p;
+        const int64_t g = (pi < n_par) ? (int64_t)par[cur][pi] : -1;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) idx[8 * p + c] = (g >= 0 && g * 8 + c < n) ? (int32_t)(g * 8 + c) : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kRegPer * 8; ++j) v[j] = base[idx[j] >= 0 ? idx[j] : 0];
     }
-#pragma unroll
-    for (int j = 0; j < kRegPer * 8; ++j) v[j] = base[idx[j] >= 0 ? idx[j] : 0];
     uint32_t cnt = 0;
     uint32_t keepm = 0;           // bit j: child j kept
 #pragma unroll
