@@ -87,7 +87,7 @@ csa2_status do_index_score(const uint16_t* q_idx, const float* head_w, const csa
   a.n_max = n_max;
   a.steps_per_row = cand ? (int32_t)cdiv(n_cand, 8) : (int32_t)cdiv(n_max, 64);
   a.score_stride = cand ? (int64_t)n_cand * 8 : n_max;
-  a.bmax_stride = cdiv(n_max, 8);
+  a.bmax_stride = cand ? (int64_t)n_cand : cdiv(n_max, 8);
   a.max64_stride = cdiv(n_max, 64);
   a.scores = scores;
   a.block_max = bmax;
@@ -114,7 +114,26 @@ struct TopkWs {
   uint32_t* seg_cnt = nullptr;
   uint32_t* seg_key = nullptr;
   int32_t* seg_pos = nullptr;
+  uint32_t* desc_cnt = nullptr;   // split path (per-segment lists)
+  uint32_t* desc_key = nullptr;
+  int32_t* desc_pos = nullptr;
 };
+
+// Top-k spread over the CUs: k below 1024, rows of 2049 .. kDescMaxN values,
+// a bounded number of rows (the lists take 256 KiB per row).
+constexpr int kDescMaxRows = 256;
+bool topk_desc_shape(int R, int64_t n_max, int k) {
+  return k < 1024 && R <= kDescMaxRows && n_max > 2048 && n_max <= kDescMaxN;
+}
+// its top level for the longest row: 1 up to 16384 values, else 2
+int desc_top_level(int64_t n_max) { return n_max <= 16384 ? 1 : 2; }
+
+void carve_desc(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
+  if (!topk_desc_shape(R, n_max, k)) return;
+  t.desc_cnt = bp.take<uint32_t>((size_t)R * kDescMaxSeg);
+  t.desc_key = bp.take<uint32_t>((size_t)R * kDescMaxSeg * kDescCap);
+  t.desc_pos = bp.take<int32_t>((size_t)R * kDescMaxSeg * kDescCap);
+}
 
 // Large k over long rows: segment thresholds, then a gather above them.
 bool topk_large_shape(int64_t n_max, int k) { return k >= 1024 && n_max > kSelCapHost && n_max <= kTauMaxN; }
@@ -129,12 +148,20 @@ void carve_large(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
 }
 
 // Workspace for the levels of maxima a generic Top-k must build itself.
+// (the split path needs its top level stored)
+int topk_levels_built(int R, int64_t n_max, int k) {
+  int need = topk_levels_needed(n_max);
+  if (topk_desc_shape(R, n_max, k) && !topk_large_shape(n_max, k)) need = max(need, desc_top_level(n_max));
+  return need;
+}
+
 TopkWs carve_topk(Bump& bp, int R, int64_t n_max, int k) {
   TopkWs t;
-  const int need = topk_levels_needed(n_max);
+  const int need = topk_levels_built(R, n_max, k);
   if (need >= 1) t.lv1 = bp.take<float>((size_t)R * cdiv(n_max, 8));
   if (need >= 2) t.lv2 = bp.take<float>((size_t)R * cdiv(n_max, 64));
   carve_large(bp, t, R, n_max, k);
+  carve_desc(bp, t, R, n_max, k);
   return t;
 }
 
@@ -174,9 +201,10 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
 
 // Builds the missing levels of maxima into the workspace, then selects.
 csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
-  const int need = topk_levels_needed(a.n_max);
+  const int need = topk_levels_built(a.R, a.n_max, a.k);
   for (int l = 1; l <= need; ++l) {
     if (a.lv[l]) continue;
+    if (!((l == 1) ? tw.lv1 : tw.lv2)) break;     // (a caller's levels only)
     float* dst = (l == 1) ? tw.lv1 : tw.lv2;
     MaximaArgs m;
     m.in = a.lv[l - 1];
@@ -202,6 +230,14 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
     a.seg_key = tw.seg_key;
     a.seg_pos = tw.seg_pos;
     return hip_status(launch_topk_large(a, st));
+  }
+  if (tw.desc_cnt && !a.row_list && topk_desc_shape(a.R, a.n_max, a.k) && a.lv[1] &&
+      (desc_top_level(a.n_max) < 2 || a.lv[2])) {
+    a.nseg = (int32_t)cdiv(a.n_max, desc_seg_len(a.n_max));
+    a.seg_cnt = tw.desc_cnt;
+    a.seg_key = tw.desc_key;
+    a.seg_pos = tw.desc_pos;
+    return hip_status(launch_topk_desc(a, st));
   }
   return hip_status(launch_topk(a, st));
 }
@@ -322,12 +358,14 @@ size_t index_region(csa2_mode mode, int R, int n_max, int hier) {
     bp.take<float>((size_t)R * cdiv(n_max, 8));
     bp.take<float>((size_t)R * cdiv(n_max, 64));
     if (prefill_shape(mode, R, n_max, hier)) carve_prefill(bp, R, n_max);
-    if (mode == CSA2_FULL && hier) {
-      TopkWs t;
-      carve_large(bp, t, R, cdiv(n_max, 8), CSA2_KEEP_BLOCKS);
-    }
+    TopkWs t;
+    carve_desc(bp, t, R, n_max, CSA2_TOPK);
+    if (mode == CSA2_FULL && hier) carve_large(bp, t, R, cdiv(n_max, 8), CSA2_KEEP_BLOCKS);
   } else if (mode == CSA2_REINDEX) {
     bp.take<float>((size_t)R * CSA2_KEEP_BLOCKS * 8);
+    bp.take<float>((size_t)R * CSA2_KEEP_BLOCKS);
+    TopkWs t;
+    carve_desc(bp, t, R, CSA2_KEEP_BLOCKS * 8, CSA2_TOPK);
   }
   return bp.off;
 }
@@ -408,11 +446,13 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
     s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max, scores,
                        bmax, m64, st);
     if (s) return s;
+    TopkWs dw;
+    carve_desc(bp, dw, R, n_max, CSA2_TOPK);
     if (!blocks_only) {
       TopkArgs t = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
       t.lv[1] = bmax;
       t.lv[2] = m64;
-      s = run_topk(t, TopkWs{}, st);
+      s = run_topk(t, dw, st);
       if (s) return s;
     }
     if (mode == CSA2_FULL && sh->hier) {
@@ -430,13 +470,17 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
   // Reindex over the candidate blocks of the last (hierarchical) Full layer
   const int nc = CSA2_KEEP_BLOCKS * 8;
   float* scores = bp.take<float>((size_t)R * nc);
+  float* cmax = bp.take<float>((size_t)R * CSA2_KEEP_BLOCKS);     // maxima of the candidate blocks
+  TopkWs dw;
+  carve_desc(bp, dw, R, nc, CSA2_TOPK);
   s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, sh->cand_blocks, CSA2_KEEP_BLOCKS,
-                     R, n_max, scores, nullptr, nullptr, st);
+                     R, n_max, scores, cmax, nullptr, st);
   if (s) return s;
   TopkArgs t = topk_args(scores, nc, nullptr, nullptr, 1, R, nc, CSA2_TOPK, sh->topk_idx);
+  t.lv[1] = cmax;
   t.cand_blocks = sh->cand_blocks;
   t.cand_stride = CSA2_KEEP_BLOCKS;
-  return run_topk(t, TopkWs{}, st);
+  return run_topk(t, dw, st);
 }
 
 csa2_status check_shared(const csa2_shared* sh, int R) {

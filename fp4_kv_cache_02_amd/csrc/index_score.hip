@@ -233,6 +233,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
       const int64_t ci8 = (int64_t)cur.t * 64 + g * 8 + pj;     // 8 * candidate index + pj
       if (ci8 < (int64_t)a.n_cand * 8)
         a.scores[(int64_t)cur.r * a.score_stride + ci8] = present ? sc : -__builtin_inff();
+      if (MAXIMA) {
+        // maximum of the candidate block (the lane group's 8 positions)
+        uint32_t k = present ? order_key(sc) : 0u;
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x141, 0xF, 0xF, false));
+        const int ci = cur.t * 8 + g;
+        if (j == 0 && ci < a.n_cand)
+          a.block_max[(int64_t)cur.r * a.bmax_stride + ci] = k ? key_to_float(k) : -__builtin_inff();
+      }
     } else {
       const int64_t p = cur.pos0 + pj;
       if (p < cur.L) a.scores[(int64_t)cur.r * a.score_stride + p] = present ? sc : -__builtin_inff();
@@ -281,7 +291,9 @@ hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxi
     if (fp8) CSA2_IDX_LAUNCH4(C, Wt, M, true); \
     else CSA2_IDX_LAUNCH4(C, Wt, M, false);    \
   } while (0)
-  if (cand) {
+  if (cand && maxima) {
+    if (has_w) CSA2_IDX_LAUNCH(true, true, true); else CSA2_IDX_LAUNCH(true, false, true);
+  } else if (cand) {
     if (has_w) CSA2_IDX_LAUNCH(true, true, false); else CSA2_IDX_LAUNCH(true, false, false);
   } else if (maxima) {
     if (has_w) CSA2_IDX_LAUNCH(false, true, true); else CSA2_IDX_LAUNCH(false, false, true);

@@ -60,6 +60,12 @@ struct TopkArgs {
 
 constexpr int kSegLen = 8192;             // level-0 values per segment of the large-k path
 constexpr int kTauMaxN = 131072;          // level-0 values per row it handles (8 x 16384)
+// Top-k spread over the CUs (k below 1024): rows of at most kDescMaxN values,
+// at most 16 segments per row, kDescCap listed values per segment
+constexpr int kDescMaxN = 131072;
+constexpr int kDescCap = 2048;
+constexpr int kDescMaxSeg = 16;
+inline int desc_seg_len(int64_t n_max) { return n_max <= 16 * 1024 ? 1024 : 8192; }
 
 // Prefill-chunk indexer on MFMA: every query row sees the positions of one
 // sequence (sequence 0).
@@ -136,6 +142,7 @@ struct AttnArgs {
 hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxima, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st);
+hipError_t launch_topk_desc(const TopkArgs& a, hipStream_t st);
 hipError_t launch_maxima(const MaximaArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,

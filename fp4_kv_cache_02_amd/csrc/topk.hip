@@ -508,6 +508,207 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
   for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
 }
 
+// ---- Top-k spread over the CUs: k below 1024 over rows of at most kDescMaxN
+// values whose top level (the lowest level with at most kRegCap values) is
+// stored ----
+//
+// One block per row descending the tree is bound by the cache misses one CU
+// keeps in flight (the children of ~1000 groups at two levels).  Instead:
+// desc_seg_kernel, grid (segments, rows), segments of SEGPER * 512 level-0
+// values: every block of a row loads the row's top level and finds the same
+// bin edge tau with k <= #{top-level values >= tau} <= 1.5 k (tau = 1, every
+// present value, when at most k are present).  Each of those top-level values
+// is the maximum of its own group of level-0 values, so at least k level-0
+// values are >= tau: the row's k-th largest value is >= tau and its top k lie
+// among the level-0 values >= tau.  The block's segment of level 0, loaded in
+// full at the start (in flight while tau is found), is filtered at tau into
+// the segment's list in index order; a segment with more than kDescCap such
+// values marks the row.  desc_final_kernel, one block per row: the lists
+// concatenated in segment order (= index order) and the exact top k; a marked
+// row, or one with more than kTauCap listed values, takes the general path in
+// the same block.
+
+template <int SEGPER>
+__global__ __launch_bounds__(kSelThreads) void desc_seg_kernel(TopkArgs a) {
+  constexpr int kSeg = SEGPER * kSelThreads;
+  __shared__ SelSmemT<1> sm;                  // the keys stay in registers
+  __shared__ uint32_t cnt[SEGPER * kSelWaves];
+  __shared__ int32_t cm[kSeg / 8];            // the segment's candidate blocks
+  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const uint32_t K = (uint32_t)a.k;
+  const int64_t n0 = row_count(a, r);
+  const int64_t rs = (int64_t)r * a.nseg + s;
+  const int64_t lo = (int64_t)s * kSeg;
+  const int n = (int)max((int64_t)0, min(n0 - lo, (int64_t)kSeg));
+  if (n == 0) {
+    if (tid == 0) a.seg_cnt[rs] = 0u;
+    return;
+  }
+  CSA2_MARK(a, 0);
+  int T = 0;
+  while (T < 2 && lv_count(n0, T) > kRegCap) ++T;
+  const int64_t nT = lv_count(n0, T);
+  // every load at once: the top level, the segment, its candidate blocks
+  const float* tb = lv_row(a, T, r);
+  float tv[kRegPer];
+  if (((uintptr_t)tb & 15u) == 0 && kRegPer * tid + kRegPer <= nT) {
+    const float4 x = *(const float4*)(tb + kRegPer * tid);
+    tv[0] = x.x; tv[1] = x.y; tv[2] = x.z; tv[3] = x.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) tv[j] = tb[min((int64_t)(kRegPer * tid + j), nT - 1)];
+  }
+  const float* base = a.lv[0] + (int64_t)r * a.lv_stride[0] + lo;
+  float v[SEGPER];
+#pragma unroll
+  for (int j = 0; j < SEGPER; ++j) v[j] = base[min(tid + j * kSelThreads, n - 1)];
+  int32_t cbv = 0;
+  if (a.cand_blocks && tid < kSeg / 8) {
+    const int64_t cb = min((lo >> 3) + tid, (int64_t)a.cand_stride - 1);
+    cbv = a.cand_blocks[(int64_t)r * a.cand_stride + cb];
+  }
+  RegKeys top;
+#pragma unroll
+  for (int j = 0; j < kRegPer; ++j) top.v[j] = (kRegPer * tid + j < nT) ? order_key(tv[j]) : 0u;
+  const SelResult sr = block_select(sm, top, K, K + K / 2);
+  const uint32_t tau = max(sr.T, 1u);
+  CSA2_MARK(a, 1);
+  if (a.cand_blocks && tid < kSeg / 8) cm[tid] = cbv;
+  // the kept values in (round, wave, lane) order = index order
+  uint32_t keepm = 0u;
+#pragma unroll
+  for (int j = 0; j < SEGPER; ++j) {
+    const bool kp = tid + j * kSelThreads < n && order_key(v[j]) >= tau;
+    keepm |= kp ? (1u << j) : 0u;
+    const uint64_t b = __ballot(kp);
+    if (lane == 0) cnt[j * kSelWaves + wv] = (uint32_t)__popcll(b);
+  }
+  __syncthreads();
+  uint32_t tot;
+  const uint32_t off = block_excl_scan(sm, tid < SEGPER * kSelWaves ? cnt[tid] : 0u, tot);
+  if (tid < SEGPER * kSelWaves) cnt[tid] = off;
+  __syncthreads();
+  if (tot > (uint32_t)kDescCap) {           // uniform
+    if (tid == 0) a.seg_cnt[rs] = (uint32_t)kDescCap + 1u;
+    return;
+  }
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  uint32_t* kd = a.seg_key + rs * kDescCap;
+  int32_t* pd = a.seg_pos + rs * kDescCap;
+#pragma unroll
+  for (int j = 0; j < SEGPER; ++j) {
+    const bool kp = (keepm >> j) & 1u;
+    const uint64_t b = __ballot(kp);
+    if (kp) {
+      const uint32_t p = cnt[j * kSelWaves + wv] + (uint32_t)__popcll(b & lt_mask);
+      const int e = tid + j * kSelThreads;
+      kd[p] = order_key(v[j]);
+      pd[p] = a.cand_blocks ? cm[e >> 3] * 8 + (e & 7) : (int32_t)(lo + e);
+    }
+  }
+  if (tid == 0) a.seg_cnt[rs] = tot;
+  CSA2_MARK(a, 2);
+}
+
+struct DescGeneralSmem {          // the general path of a marked row
+  SelSmem sel;
+  int32_t par[2][kSelCap / 8];
+  int32_t cmap[kSelCap / 8];
+};
+union DescFinalSmem {
+  FinalSmem f;
+  DescGeneralSmem g;
+};
+
+__global__ __launch_bounds__(kSelThreads) void desc_final_kernel(TopkArgs a) {
+  __shared__ DescFinalSmem u;
+  FinalSmem& sm = u.f;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint32_t K = (uint32_t)a.k;
+  int32_t* out = a.out + (int64_t)r * a.out_stride;
+  const int64_t n0 = row_count(a, r);
+  if (n0 == 0) {
+    for (int i = tid; i < a.k; i += kSelThreads) out[i] = -1;
+    return;
+  }
+  CSA2_MARK(a, 3);
+  // list lengths and their offsets (one segment per lane; every wave alike)
+  const uint32_t c = lane < a.nseg ? a.seg_cnt[(int64_t)r * a.nseg + lane] : 0u;
+  const bool marked = __ballot(c > (uint32_t)kDescCap) != 0ull;
+  const uint32_t inc = wave_incl_scan_u32(c);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  if (marked || total > (uint32_t)kTauCap) {
+    if (a.cand_blocks)
+      for (int i = tid; i < a.cand_stride; i += kSelThreads) u.g.cmap[i] = a.cand_blocks[(int64_t)r * a.cand_stride + i];
+    __syncthreads();
+    if (!topk_threshold(a, r, n0, u.g.sel, u.g.par, u.g.cmap, out)) {
+      __syncthreads();
+      topk_general(a, r, n0, u.g.sel, u.g.par, u.g.cmap, out);
+    }
+    return;
+  }
+  const int64_t rb = (int64_t)r * a.nseg * kDescCap;
+  // list element e: segment sidx = #{segments whose inclusive end is <= e}
+  auto where = [&](uint32_t e) -> int64_t {
+    uint32_t sidx = 0u, start = 0u;
+    for (int q = 0; q < a.nseg; ++q) {
+      const uint32_t end_q = (uint32_t)__builtin_amdgcn_readlane((int)inc, q);
+      const bool past = end_q <= e;
+      sidx += past ? 1u : 0u;
+      start = past ? end_q : start;
+    }
+    return (e < total) ? rb + (int64_t)sidx * kDescCap + (e - start) : rb;
+  };
+  if (total <= (uint32_t)kRegCap) {
+    // thread t holds elements 4t .. 4t+3 (registers)
+    RegKeys ks;
+    int32_t ps[kRegPer];
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      const uint32_t e = (uint32_t)(kRegPer * tid + j);
+      const int64_t g = where(e);
+      ks.v[j] = a.seg_key[g];
+      ps[j] = a.seg_pos[g];
+    }
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) ks.v[j] = (uint32_t)(kRegPer * tid + j) < total ? ks.v[j] : 0u;
+    CSA2_MARK(a, 4);
+    const SelResult res = block_select(sm.sel, ks, K, 0u);
+    const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) {
+      const int j = e & (kRegPer - 1);
+      out[o] = (j == 0) ? ps[0] : (j == 1) ? ps[1] : (j == 2) ? ps[2] : ps[3];
+    });
+    for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
+    CSA2_MARK(a, 5);
+    return;
+  }
+  constexpr int kJ = kTauCap / kSelThreads;
+  uint32_t key[kJ];
+  int32_t ps[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int64_t g = where((uint32_t)(tid + j * kSelThreads));
+    key[j] = a.seg_key[g];
+    ps[j] = a.seg_pos[g];
+  }
+  const int n_pad = sel_padded((int)total);
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int e = tid + j * kSelThreads;
+    if (e < n_pad) {
+      sm.sel.key[skew(e)] = e < (int)total ? key[j] : 0u;
+      sm.pos[e] = ps[j];
+    }
+  }
+  __syncthreads();
+  const LdsKeysT<SelSmemT<kTauKeyWords>> ks{&sm.sel, n_pad};
+  const SelResult res = block_select(sm.sel, ks, K, 0u);
+  const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
+  for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
+}
+
 // out[r][g] = maximum (in the Top-k order) of in[r][8g .. 8g+7] below the
 // row's count, -inf when none is present.  The row's count at this level is
 // ceil(n0 / div) with n0 the level-0 count of the row.
@@ -545,6 +746,18 @@ hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(seg_kth_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(seg_gather_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(seg_final_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// Top-k spread over the CUs: segments of 1024 values for rows of at most
+// 16384 (top level 1), else of 8192 (top level 2).
+hipError_t launch_topk_desc(const TopkArgs& a, hipStream_t st) {
+  if (a.R == 0) return hipSuccess;
+  if (a.n_max <= 16 * 2 * kSelThreads)
+    hipLaunchKernelGGL(desc_seg_kernel<2>, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(desc_seg_kernel<16>, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(desc_final_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 

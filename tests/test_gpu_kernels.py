@@ -175,6 +175,44 @@ def test_topk_bitexact(C, k):
     assert np.array_equal(host(out), g)
 
 
+@pytest.mark.parametrize("k", [7, 512])
+@pytest.mark.parametrize("mapped", [False, True])
+def test_topk_bitexact_short_rows(C, k, mapped):
+    """Rows of at most 16384 values (the Reindex candidates' size): the
+    selection split over 1024-value segments, with and without a candidate
+    block map (output position = 8 * cand_blocks[i // 8] + i % 8)."""
+    rng = np.random.default_rng(700 + k + 7 * mapped)
+    kinds = ["normal", "ties", "zeros", "equal", "clustered", "neginf", "copies"]
+    ns = [0, 5, k, 2048, 2049, 9000, 16383, 16384]
+    rows = [(kd, n) for kd in kinds for n in ns]
+    R = len(rows)
+    n_max = 16384
+    scores = np.full((R, n_max), np.nan, np.float32)
+    nv = np.zeros(R, np.int32)
+    for r, (kd, n) in enumerate(rows):
+        scores[r, :n] = _topk_case(rng, kd, n)
+        if n < n_max:
+            scores[r, n:] = -np.inf if mapped else np.nan
+        nv[r] = n
+    cand = None
+    if mapped:
+        cand = np.sort(np.stack([rng.choice(1 << 20, n_max // 8, replace=False) for _ in range(R)]), axis=1)
+        cand = cand.astype(np.int32)
+    say("topk short rows k", k, "mapped", mapped, "R", R)
+    ws = workspace(C.csa2_topk_workspace_bytes(R, n_max, k))
+    out = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    # (a candidate map covers whole rows: every value is present or -inf)
+    C.csa2_topk(dev(scores), k, out, ws, n_valid=None if mapped else dev(nv),
+                cand_blocks=dev(cand) if mapped else None)
+    torch.cuda.synchronize()
+    g = host(out)
+    for r, (kd, n) in enumerate(rows):
+        ref = O.topk(scores[r] if mapped else scores[r, :n], k)
+        if mapped:
+            ref = np.where(ref >= 0, cand[r][np.maximum(ref, 0) // 8] * 8 + np.maximum(ref, 0) % 8, -1)
+        assert np.array_equal(g[r], ref), (kd, n, k)
+
+
 def test_hier_candidates_bitexact(C):
     rng = np.random.default_rng(505)
     lens = [1048576 // 4, 16384, 12345, 7]
