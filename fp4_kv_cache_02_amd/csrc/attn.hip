@@ -148,22 +148,34 @@ CSA2_DEV void qk_main(const AttnSmem& sm, int w, int c, int g, float (&s)[8]) {
   }
 }
 
-CSA2_DEV void qk_win(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int kk0, int c, int g,
-                     float (&s)[8]) {
-  const uint4* qrow = sm.q + c * kQRow + 16 * g;
-#pragma unroll 1
+// Window keys of this wave's two 16-key groups: lane (c, g) holds key
+// kk0 + 16u + c, dims 128g .. 128g+127 (entry 0 of the buffer stands in for
+// an absent key; its words are zeroed at use).  Loaded at the head of the
+// window step, with the query, so that one round trip brings both.
+struct WinK {
+  uint4 k[2][16];
+  uint32_t ok[2];     // all-ones when the key is present
+};
+CSA2_DEV void win_k_load(const AttnLayer& Ly, int b, int wst, int wl, int kk0, int c, int g, WinK& wk) {
+#pragma unroll
   for (int u = 0; u < 2; ++u) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int kk = kk0 + 16 * u + c;
     const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
-    // unconditional loads (entry 0 stands in for an absent one), zeroed after
     const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
-    uint4 kr[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) kr[t] = src[t];
+    for (int t = 0; t < 16; ++t) wk.k[u][t] = src[t];
+    wk.ok[u] = ok ? 0xFFFFFFFFu : 0u;
+  }
+}
+
+CSA2_DEV void qk_win(const AttnSmem& sm, const WinK& wk, int c, int g, float (&s)[8]) {
+  const uint4* qrow = sm.q + c * kQRow + 16 * g;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint4 kz = mask4(kr[t], ok ? 0xFFFFFFFFu : 0u);
+      const uint4 kz = mask4(wk.k[u][t], wk.ok[u]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kz), as_bf8(qrow[t]), acc, 0, 0, 0);
     }
 #pragma unroll
@@ -202,37 +214,191 @@ CSA2_DEV void pv_main(const AttnSmem& sm, RowState& st, int w, int c, int g) {
   }
 }
 
-CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int w, int c,
-                     int g) {
-#pragma unroll 1
-  for (int ks = 0; ks < 4; ++ks) {
-    const int key0 = 32 * ks + 8 * g;
-    uint4 vr[8];
+// Window V words of keys 32 ks + 8g + i (i < 8), dims 128w + 8c .. 128w + 8c + 7
+// (zero for an absent key).
+CSA2_DEV void win_v_load(const AttnLayer& Ly, int b, int wst, int wl, int ks, int w, int c, int g, uint4 (&vr)[8]) {
+  const int key0 = 32 * ks + 8 * g;
+  uint4 v[8];
+  bool okv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = key0 + i;
-      const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
-      const uint4 v = Ly.swa_v[((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + 16 * w + c];
-      vr[i] = mask4(v, ok ? 0xFFFFFFFFu : 0u);
-    }
-    const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
-    const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
+  for (int i = 0; i < 8; ++i) {
+    const int kk = key0 + i;
+    okv[i] = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
+    v[i] = Ly.swa_v[((int64_t)b * Ly.S + (okv[i] ? wst + kk : 0)) * 64 + 16 * w + c];
+  }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t x[8];
+  for (int i = 0; i < 8; ++i) vr[i] = mask4(v[i], okv[i] ? 0xFFFFFFFFu : 0u);
+}
+
+// O += P V over keys 32 ks .. 32 ks + 31 of the window step.
+CSA2_DEV void pv_win_part(const AttnSmem& sm, RowState& st, int ks, int c, int g, const uint4 (&vr)[8]) {
+  const int key0 = 32 * ks + 8 * g;
+  const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
+  const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (m == 0) ? vr[i].x : (m == 1) ? vr[i].y : (m == 2) ? vr[i].z : vr[i].w;
-      const uint4 b0 = make_uint4(pack_lo(x[0], x[1]), pack_lo(x[2], x[3]), pack_lo(x[4], x[5]), pack_lo(x[6], x[7]));
-      const uint4 b1 = make_uint4(pack_hi(x[0], x[1]), pack_hi(x[2], x[3]), pack_hi(x[4], x[5]), pack_hi(x[6], x[7]));
-      st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b0), st.o[2 * m], 0, 0, 0);
-      st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), as_bf8(b0), st.o[2 * m], 0, 0, 0);
-      st.o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b1), st.o[2 * m + 1], 0, 0, 0);
-      st.o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), as_bf8(b1), st.o[2 * m + 1], 0, 0, 0);
-    }
+  for (int m = 0; m < 4; ++m) {
+    uint32_t x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (m == 0) ? vr[i].x : (m == 1) ? vr[i].y : (m == 2) ? vr[i].z : vr[i].w;
+    const uint4 b0 = make_uint4(pack_lo(x[0], x[1]), pack_lo(x[2], x[3]), pack_lo(x[4], x[5]), pack_lo(x[6], x[7]));
+    const uint4 b1 = make_uint4(pack_hi(x[0], x[1]), pack_hi(x[2], x[3]), pack_hi(x[4], x[5]), pack_hi(x[6], x[7]));
+    st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b0), st.o[2 * m], 0, 0, 0);
+    st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), as_bf8(b0), st.o[2 * m], 0, 0, 0);
+    st.o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b1), st.o[2 * m + 1], 0, 0, 0);
+    st.o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), as_bf8(b1), st.o[2 * m + 1], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fp4_attn_kernel(AttnArgs a) {
+// The window step's P V: the first two 32-key parts were loaded before the
+// softmax statistics; the later parts are loaded ahead of the MFMAs that
+// precede their use.
+CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int w, int c,
+                     int g, const uint4 (&v0)[8], const uint4 (&v1)[8]) {
+  uint4 v2[8], v3[8];
+  win_v_load(Ly, b, wst, wl, 2, w, c, g, v2);
+  pv_win_part(sm, st, 0, c, g, v0);
+  win_v_load(Ly, b, wst, wl, 3, w, c, g, v3);
+  pv_win_part(sm, st, 1, c, g, v1);
+  pv_win_part(sm, st, 2, c, g, v2);
+  pv_win_part(sm, st, 3, c, g, v3);
+}
+
+// Window step with loads issued part by part (the variant with two blocks
+// per CU, whose register budget does not hold the batched loads).
+CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int kk0, int c, int g,
+                         float (&s)[8]) {
+  const uint4* qrow = sm.q + c * kQRow + 16 * g;
+#pragma unroll 1
+  for (int u = 0; u < 2; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int kk = kk0 + 16 * u + c;
+    const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
+    const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
+    uint4 kr[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) kr[t] = src[t];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint4 kz = mask4(kr[t], ok ? 0xFFFFFFFFu : 0u);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kz), as_bf8(qrow[t]), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
+  }
+}
+CSA2_DEV void pv_win_seq(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int w,
+                         int c, int g) {
+#pragma unroll 1
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 vr[8];
+    win_v_load(Ly, b, wst, wl, ks, w, c, g, vr);
+    pv_win_part(sm, st, ks, c, g, vr);
+  }
+}
+
+// ---- phase 2: softmax statistics of the step (head c), P into LDS, running
+// statistics of this lane's output heads 4g+i (O rescaled) ----
+template <bool MAIN>
+CSA2_DEV void step_softmax(AttnSmem& sm, RowState& st, float (&s)[8], uint64_t vmask, float sm_scale, int w, int c,
+                           int g) {
+    float cmax = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
+      const bool ok = (vmask >> key) & 1ull;
+      s[e] = ok ? s[e] * sm_scale : -__builtin_inff();
+      cmax = fmaxf(cmax, s[e]);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    if (g == 0) sm.red_m[w][c] = cmax;
+    __syncthreads();
+    float mstep = sm.red_m[0][c];
+#pragma unroll
+    for (int v = 1; v < kAttnWaves; ++v) mstep = fmaxf(mstep, sm.red_m[v][c]);
+    // running max of head c before this step: kept in st.m[c & 3] by the lanes
+    // of group c >> 2 (lane 16 * (c >> 2) + c evaluates pick4 with its own c)
+    const float mold_c = __shfl(pick4(st.m, c & 3), 16 * (c >> 2) + c, 64);
+    const float mnew_c = fmaxf(mold_c, mstep);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = (mnew_c == -__builtin_inff()) ? 0.f : __expf(s[e] - mnew_c);
+      psum += p[e];
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    if (g == 0) sm.red_l[w][c] = psum;
+    // P hi/lo -> LDS [head c][key 32w + sigma(g, e)]
+    {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t h0, h1, l0, l1;
+        if (MAIN) {
+          const _Float16 a0 = (_Float16)p[e], a1 = (_Float16)p[e + 1];
+          h0 = __builtin_bit_cast(uint16_t, a0);
+          h1 = __builtin_bit_cast(uint16_t, a1);
+          l0 = __builtin_bit_cast(uint16_t, (_Float16)(p[e] - (float)a0));
+          l1 = __builtin_bit_cast(uint16_t, (_Float16)(p[e + 1] - (float)a1));
+        } else {
+          h0 = f32_to_bf16_rne(p[e]);
+          h1 = f32_to_bf16_rne(p[e + 1]);
+          l0 = f32_to_bf16_rne(p[e] - __uint_as_float(h0 << 16));
+          l1 = f32_to_bf16_rne(p[e + 1] - __uint_as_float(h1 << 16));
+        }
+        hw[e / 2] = h0 | (h1 << 16);
+        lw[e / 2] = l0 | (l1 << 16);
+      }
+      uint16_t* ph = &sm.p_hi[c * kPRow + 32 * w];
+      uint16_t* pl = &sm.p_lo[c * kPRow + 32 * w];
+      *(uint2*)(ph + 4 * g) = make_uint2(hw[0], hw[1]);
+      *(uint2*)(ph + 16 + 4 * g) = make_uint2(hw[2], hw[3]);
+      *(uint2*)(pl + 4 * g) = make_uint2(lw[0], lw[1]);
+      *(uint2*)(pl + 16 + 4 * g) = make_uint2(lw[2], lw[3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      float mh = sm.red_m[0][h], lh = sm.red_l[0][h];
+#pragma unroll
+      for (int v = 1; v < kAttnWaves; ++v) {
+        mh = fmaxf(mh, sm.red_m[v][h]);
+        lh += sm.red_l[v][h];
+      }
+      const float mn = fmaxf(st.m[i], mh);
+      const float alpha = (st.m[i] == -__builtin_inff()) ? 0.f : __expf(st.m[i] - mn);
+      st.l[i] = st.l[i] * alpha + lh;
+      st.m[i] = mn;
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.o[j][i] *= alpha;
+      }
+    }
+}
+
+// The query of the row into LDS from loads issued earlier: fp16 for main
+// steps, bf16 for the window step (per-word selects: a select of whole uint4s
+// becomes a branch per load, each waiting for its load).
+CSA2_DEV void store_q(AttnSmem& sm, const uint4 (&qv)[4], bool to_f16, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    const uint4 h = bf16x8_to_f16x8(qv[i]);
+    sm.q[(e >> 6) * kQRow + (e & 63)] = make_uint4(to_f16 ? h.x : qv[i].x, to_f16 ? h.y : qv[i].y,
+                                                   to_f16 ? h.z : qv[i].z, to_f16 ? h.w : qv[i].w);
+  }
+}
+
+// WPE: waves per SIMD (blocks per CU).  WPE = 1 (a launch whose blocks all
+// fit on the CUs at once, as in decode) doubles the registers of a wave: the
+// window step then issues its keys with the query and its values ahead of
+// use, and a main step its indices with the query.  WPE = 2 (many blocks,
+// prefill) loads them part by part.
+template <int WPE>
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fp4_attn_kernel(AttnArgs a) {
+  constexpr bool kEarly = WPE == 1;
   __shared__ AttnSmem sm;
   // flat grid: block id = (li * R + r) * n_blocks + blk
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so
@@ -276,149 +442,85 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   }
 
   const uint4* qsrc = Ly.q + (int64_t)r * 16 * 64;
+  const int wb = Ly.swa_shared ? 0 : b;
+  // The two kinds of step are separate code paths (their registers do not
+  // overlap).  In each, the loads that head its longest chain go first -- the
+  // main keys' indices (their slots, then their rows), or the window keys --
+  // with the query in flight beside them.
   for (int step = st0; step < st1; ++step) {
     const bool is_main = step < n_main;
-    // query of the row into LDS: fp16 for main steps, bf16 for the window
-    // step (the previous step ended with a barrier)
-    if (step == st0 || !is_main) {
-      // all four loads first, then per-word selects (a select of whole uint4s
-      // becomes a branch per load, each waiting for its load)
-      uint4 qv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];   // uint4 e: head e / 64, piece e % 64
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = tid + 256 * i;
-        const uint4 h = bf16x8_to_f16x8(qv[i]);
-        sm.q[(e >> 6) * kQRow + (e & 63)] = make_uint4(is_main ? h.x : qv[i].x, is_main ? h.y : qv[i].y,
-                                                       is_main ? h.z : qv[i].z, is_main ? h.w : qv[i].w);
-      }
-    }
-    // ---- keys of this wave: 32w .. 32w+31 of the step ----
-    bool valid;
+    const bool need_q = step == st0 || !is_main;
     if (is_main) {
+      int pos = -1;
       if (tid < kStepKeys) {
         const int kk = step * kStepKeys + tid;
-        const int pos = kk < a.k ? idx_row[kk] : -1;
-        sm.slot[tid] = (pos >= 0 && pos < L) ? (int32_t)a.map(b, pos) : -1;
+        pos = kk < a.k ? idx_row[kk] : -1;
       }
+      uint4 qv[4];
+      if (need_q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];   // uint4 e: head e / 64, piece e % 64
+        if (!kEarly) store_q(sm, qv, true, tid);
+      }
+      if (tid < kStepKeys) sm.slot[tid] = (pos >= 0 && pos < L) ? (int32_t)a.map(b, pos) : -1;
       __syncthreads();
-      // stage the step's FP4 rows: thread t loads half (t & 1) of key t >> 1
+      // the step's FP4 rows: thread t loads half (t & 1) of key t >> 1
       // (unconditional loads from slot 0 for absent keys, zeroed after)
-      {
-        const int key = tid >> 1, half = tid & 1;
-        const int32_t sl = sm.slot[key];
-        const int64_t ss = sl >= 0 ? sl : 0;
-        const uint4* src = (const uint4*)(a.kv + ss * 256 + 128 * half);
-        uint4 v[8];
+      const int key = tid >> 1, half = tid & 1;
+      const int32_t sl = sm.slot[key];
+      const int64_t ss = sl >= 0 ? sl : 0;
+      const uint4* src = (const uint4*)(a.kv + ss * 256 + 128 * half);
+      uint4 rv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = src[i];
-        const uint4 sc = *(const uint4*)(a.kv_scale + ss * 32 + 16 * half);
-        const uint32_t m = sl >= 0 ? 0xFFFFFFFFu : 0u;    // (a select of whole uint4s goes through scratch)
-        uint4* dst = (uint4*)&sm.code[key * kCodeRow + 32 * half];
+      for (int i = 0; i < 8; ++i) rv[i] = src[i];
+      const uint4 rsc = *(const uint4*)(a.kv_scale + ss * 32 + 16 * half);
+      const uint32_t rmask = sl >= 0 ? 0xFFFFFFFFu : 0u;    // (a select of whole uint4s goes through scratch)
+      if (kEarly && need_q) store_q(sm, qv, true, tid);
+      uint4* dst = (uint4*)&sm.code[key * kCodeRow + 32 * half];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = mask4(v[i], m);
-        *(uint4*)&sm.scale[key * 8 + 4 * half] = mask4(sc, m);
-      }
-      valid = sm.slot[32 * w + (lane & 31)] >= 0;
-    } else {
-      const int e = 32 * w + (lane & 31);
-      valid = e < wl && wst >= 0 && (int64_t)wst + e < Ly.S;
-    }
-    const uint64_t vmask = __ballot(valid);
-    __syncthreads();    // query, codes and scales visible
-    CSA2_MARK(a, 1);
-    float s[8];
-    if (is_main)
+      for (int i = 0; i < 8; ++i) dst[i] = mask4(rv[i], rmask);
+      *(uint4*)&sm.scale[key * 8 + 4 * half] = mask4(rsc, rmask);
+      const uint64_t vmask = __ballot(sm.slot[32 * w + (lane & 31)] >= 0);
+      __syncthreads();    // query, codes and scales visible
+      CSA2_MARK(a, 1);
+      float s[8];
       qk_main(sm, w, c, g, s);
-    else
-      qk_win(Ly, sm, Ly.swa_shared ? 0 : b, wst, wl, 32 * w, c, g, s);
-    CSA2_MARK(a, 2);
-
-    // ---- softmax statistics of the step (head c) ----
-    const float sm_scale = Ly.sm_scale;
-    float cmax = -__builtin_inff();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
-      const bool ok = (vmask >> key) & 1ull;
-      s[e] = ok ? s[e] * sm_scale : -__builtin_inff();
-      cmax = fmaxf(cmax, s[e]);
-    }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    if (g == 0) sm.red_m[w][c] = cmax;
-    __syncthreads();
-    float mstep = sm.red_m[0][c];
-#pragma unroll
-    for (int v = 1; v < kAttnWaves; ++v) mstep = fmaxf(mstep, sm.red_m[v][c]);
-    // running max of head c before this step: kept in st.m[c & 3] by the lanes
-    // of group c >> 2 (lane 16 * (c >> 2) + c evaluates pick4 with its own c)
-    const float mold_c = __shfl(pick4(st.m, c & 3), 16 * (c >> 2) + c, 64);
-    const float mnew_c = fmaxf(mold_c, mstep);
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = (mnew_c == -__builtin_inff()) ? 0.f : __expf(s[e] - mnew_c);
-      psum += p[e];
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    if (g == 0) sm.red_l[w][c] = psum;
-    // P hi/lo -> LDS [head c][key 32w + sigma(g, e)]
-    {
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        uint32_t h0, h1, l0, l1;
-        if (is_main) {
-          const _Float16 a0 = (_Float16)p[e], a1 = (_Float16)p[e + 1];
-          h0 = __builtin_bit_cast(uint16_t, a0);
-          h1 = __builtin_bit_cast(uint16_t, a1);
-          l0 = __builtin_bit_cast(uint16_t, (_Float16)(p[e] - (float)a0));
-          l1 = __builtin_bit_cast(uint16_t, (_Float16)(p[e + 1] - (float)a1));
-        } else {
-          h0 = f32_to_bf16_rne(p[e]);
-          h1 = f32_to_bf16_rne(p[e + 1]);
-          l0 = f32_to_bf16_rne(p[e] - __uint_as_float(h0 << 16));
-          l1 = f32_to_bf16_rne(p[e + 1] - __uint_as_float(h1 << 16));
-        }
-        hw[e / 2] = h0 | (h1 << 16);
-        lw[e / 2] = l0 | (l1 << 16);
-      }
-      uint16_t* ph = &sm.p_hi[c * kPRow + 32 * w];
-      uint16_t* pl = &sm.p_lo[c * kPRow + 32 * w];
-      *(uint2*)(ph + 4 * g) = make_uint2(hw[0], hw[1]);
-      *(uint2*)(ph + 16 + 4 * g) = make_uint2(hw[2], hw[3]);
-      *(uint2*)(pl + 4 * g) = make_uint2(lw[0], lw[1]);
-      *(uint2*)(pl + 16 + 4 * g) = make_uint2(lw[2], lw[3]);
-    }
-    __syncthreads();
-    // running statistics of this lane's output heads 4g+i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g + i;
-      float mh = sm.red_m[0][h], lh = sm.red_l[0][h];
-#pragma unroll
-      for (int v = 1; v < kAttnWaves; ++v) {
-        mh = fmaxf(mh, sm.red_m[v][h]);
-        lh += sm.red_l[v][h];
-      }
-      const float mn = fmaxf(st.m[i], mh);
-      const float alpha = (st.m[i] == -__builtin_inff()) ? 0.f : __expf(st.m[i] - mn);
-      st.l[i] = st.l[i] * alpha + lh;
-      st.m[i] = mn;
-      if (alpha != 1.f) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st.o[j][i] *= alpha;
-      }
-    }
-    CSA2_MARK(a, 3);
-    if (is_main)
+      CSA2_MARK(a, 2);
+      step_softmax<true>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
+      CSA2_MARK(a, 3);
       pv_main(sm, st, w, c, g);
-    else
-      pv_win(Ly, sm, st, Ly.swa_shared ? 0 : b, wst, wl, w, c, g);
-    CSA2_MARK(a, 4);
+      CSA2_MARK(a, 4);
+    } else if (!kEarly) {
+      uint4 qv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];
+      store_q(sm, qv, false, tid);
+      const int e = 32 * w + (lane & 31);
+      const uint64_t vmask = __ballot(e < wl && wst >= 0 && (int64_t)wst + e < Ly.S);
+      __syncthreads();    // query visible
+      float s[8];
+      qk_win_seq(Ly, sm, wb, wst, wl, 32 * w, c, g, s);
+      step_softmax<false>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
+      pv_win_seq(Ly, sm, st, wb, wst, wl, w, c, g);
+    } else {
+      WinK wk;
+      win_k_load(Ly, wb, wst, wl, 32 * w, c, g, wk);
+      uint4 qv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];
+      store_q(sm, qv, false, tid);
+      const int e = 32 * w + (lane & 31);
+      const uint64_t vmask = __ballot(e < wl && wst >= 0 && (int64_t)wst + e < Ly.S);
+      __syncthreads();    // query visible
+      float s[8];
+      qk_win(sm, wk, c, g, s);
+      // the first half of the window values, in flight during the statistics
+      uint4 v0[8], v1[8];
+      win_v_load(Ly, wb, wst, wl, 0, w, c, g, v0);
+      win_v_load(Ly, wb, wst, wl, 1, w, c, g, v1);
+      step_softmax<false>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
+      pv_win(Ly, sm, st, wb, wst, wl, w, c, g, v0, v1);
+    }
     __syncthreads();    // P, slots and statistics may be overwritten by the next step
   }
 
@@ -525,7 +627,11 @@ int attn_blocks(int k, int rows_x_layers, int* steps_per_block) {
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.R == 0 || a.n_layers == 0) return hipSuccess;
-  hipLaunchKernelGGL(fp4_attn_kernel, dim3(a.n_blocks * a.R * a.n_layers), dim3(kAttnWaves * 64), 0, st, a);
+  const int64_t blocks = (int64_t)a.n_blocks * a.R * a.n_layers;
+  if (blocks <= 256)   // one block per CU
+    hipLaunchKernelGGL(fp4_attn_kernel<1>, dim3((unsigned)blocks), dim3(kAttnWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL(fp4_attn_kernel<2>, dim3((unsigned)blocks), dim3(kAttnWaves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_blocks == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(4 * a.n_layers * a.R), dim3(256), 0, st, a);

@@ -61,11 +61,11 @@ struct TopkArgs {
 constexpr int kSegLen = 8192;             // level-0 values per segment of the large-k path
 constexpr int kTauMaxN = 131072;          // level-0 values per row it handles (8 x 16384)
 // Top-k spread over the CUs (k below 1024): rows of at most kDescMaxN values,
-// at most 16 segments per row, kDescCap listed values per segment
+// at most 32 segments per row, kDescCap listed values per segment
 constexpr int kDescMaxN = 131072;
-constexpr int kDescCap = 2048;
-constexpr int kDescMaxSeg = 16;
-inline int desc_seg_len(int64_t n_max) { return n_max <= 16 * 1024 ? 1024 : 8192; }
+constexpr int kDescCap = 1024;
+constexpr int kDescMaxSeg = 32;
+inline int desc_seg_len(int64_t n_max) { return n_max <= 16 * 1024 ? 1024 : 4096; }
 
 // Prefill-chunk indexer on MFMA: every query row sees the positions of one
 // sequence (sequence 0).

@@ -634,8 +634,16 @@ __global__ __launch_bounds__(kSelThreads) void desc_final_kernel(TopkArgs a) {
     return;
   }
   CSA2_MARK(a, 3);
-  // list lengths and their offsets (one segment per lane; every wave alike)
+  // list lengths (one segment per lane; every wave alike) and, in the same
+  // round of loads, the fixed register slots of the fast path below: segment
+  // s owns slots [spp s, spp (s+1)), thread t slots 4t .. 4t+3
   const uint32_t c = lane < a.nseg ? a.seg_cnt[(int64_t)r * a.nseg + lane] : 0u;
+  const int64_t rb = (int64_t)r * a.nseg * kDescCap;
+  const int spp = min(kRegCap / a.nseg, kDescCap) & ~(kRegPer - 1);
+  const int sg = kRegPer * tid / spp, sl0 = kRegPer * tid - sg * spp;
+  const int64_t g0 = sg < a.nseg ? rb + (int64_t)sg * kDescCap + sl0 : rb;
+  const uint4 kk = *(const uint4*)(a.seg_key + g0);
+  const int4 pp = *(const int4*)(a.seg_pos + g0);
   const bool marked = __ballot(c > (uint32_t)kDescCap) != 0ull;
   const uint32_t inc = wave_incl_scan_u32(c);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
@@ -649,7 +657,28 @@ __global__ __launch_bounds__(kSelThreads) void desc_final_kernel(TopkArgs a) {
     }
     return;
   }
-  const int64_t rb = (int64_t)r * a.nseg * kDescCap;
+  // Fast path: every list fits its slots.  Thread order is then (segment,
+  // list position) order = index order; slots past a list's length are absent.
+  {
+    const bool fits = __ballot(c > (uint32_t)spp) == 0ull;
+    if (fits) {
+      const uint32_t cs = (uint32_t)__shfl((int)c, sg < a.nseg ? sg : 0, 64);
+      RegKeys ks;
+      ks.v[0] = (sg < a.nseg && (uint32_t)sl0 + 0u < cs) ? kk.x : 0u;
+      ks.v[1] = (sg < a.nseg && (uint32_t)sl0 + 1u < cs) ? kk.y : 0u;
+      ks.v[2] = (sg < a.nseg && (uint32_t)sl0 + 2u < cs) ? kk.z : 0u;
+      ks.v[3] = (sg < a.nseg && (uint32_t)sl0 + 3u < cs) ? kk.w : 0u;
+      CSA2_MARK(a, 4);
+      const SelResult res = block_select(sm.sel, ks, K, 0u);
+      const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) {
+        const int j = e & (kRegPer - 1);
+        out[o] = (j == 0) ? pp.x : (j == 1) ? pp.y : (j == 2) ? pp.z : pp.w;
+      });
+      for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
+      CSA2_MARK(a, 5);
+      return;
+    }
+  }
   // list element e: segment sidx = #{segments whose inclusive end is <= e}
   auto where = [&](uint32_t e) -> int64_t {
     uint32_t sidx = 0u, start = 0u;
@@ -750,13 +779,13 @@ hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st) {
 }
 
 // Top-k spread over the CUs: segments of 1024 values for rows of at most
-// 16384 (top level 1), else of 8192 (top level 2).
+// 16384 (top level 1), else of 4096 (top level 2).
 hipError_t launch_topk_desc(const TopkArgs& a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   if (a.n_max <= 16 * 2 * kSelThreads)
     hipLaunchKernelGGL(desc_seg_kernel<2>, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(desc_seg_kernel<16>, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+    hipLaunchKernelGGL(desc_seg_kernel<8>, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(desc_final_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
