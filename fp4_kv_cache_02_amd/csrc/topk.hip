@@ -446,6 +446,43 @@ union FinalOrGeneral {
   GeneralSmem g;
 };
 
+// The per-segment lists of a row (segment s: length c and inclusive prefix
+// inc in lane s, list at rb + s * stride) into LDS at their offsets in the
+// concatenation (segment order = index order), keys padded with absent ones to
+// a multiple of kSelPad.  Thread t takes element t of every list (all loads at
+// once; a segment's lane is a constant, so its length and offset are two
+// readlanes), then, rarely, the elements past 512 of a longer list.
+template <int MAXSEG>
+CSA2_DEV void lists_to_lds(FinalSmem& sm, const uint32_t* keys, const int32_t* pos, int64_t rb, int64_t stride,
+                           int nseg, uint32_t c, uint32_t inc, uint32_t total) {
+  const int tid = threadIdx.x;
+  uint32_t kv[MAXSEG];
+  int32_t pv[MAXSEG];
+#pragma unroll
+  for (int q = 0; q < MAXSEG; ++q) {
+    const uint32_t cq = q < nseg ? (uint32_t)__builtin_amdgcn_readlane((int)c, q) : 0u;
+    const int64_t g = (uint32_t)tid < cq ? rb + (int64_t)q * stride + tid : rb;
+    kv[q] = keys[g];
+    pv[q] = pos[g];
+  }
+  const int n_pad = sel_padded((int)total);
+  for (int e = (int)total + tid; e < n_pad; e += kSelThreads) sm.sel.key[skew(e)] = 0u;
+#pragma unroll
+  for (int q = 0; q < MAXSEG; ++q) {
+    const uint32_t cq = q < nseg ? (uint32_t)__builtin_amdgcn_readlane((int)c, q) : 0u;
+    const uint32_t sq = q < nseg ? (uint32_t)__builtin_amdgcn_readlane((int)inc, q) - cq : 0u;
+    if ((uint32_t)tid < cq) {
+      sm.sel.key[skew((int)(sq + tid))] = kv[q];
+      sm.pos[sq + tid] = pv[q];
+    }
+    for (uint32_t i = tid + kSelThreads; i < cq; i += kSelThreads) {
+      const int64_t g = rb + (int64_t)q * stride + i;
+      sm.sel.key[skew((int)(sq + i))] = keys[g];
+      sm.pos[sq + i] = pos[g];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
   __shared__ FinalOrGeneral u;
   FinalSmem& sm = u.f;
@@ -458,6 +495,7 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
     for (int i = tid; i < a.k; i += kSelThreads) out[i] = -1;
     return;
   }
+  CSA2_MARK(a, 20);
   // segment counts and their offsets (one segment per lane; every wave alike)
   const int nseg = (int)((n0 + kSegLen - 1) / kSegLen);
   const uint32_t c = lane < nseg ? a.seg_cnt[(int64_t)r * a.nseg + lane] : 0u;
@@ -472,40 +510,17 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
     }
     return;
   }
-  // element e of the concatenation lies in segment s = #{segments whose
-  // inclusive end is <= e}; thread t takes e = t + 512 j (all loads at once)
-  constexpr int kJ = kTauCap / kSelThreads;
-  const int64_t rb = (int64_t)r * a.nseg * kSegLen;
-  uint32_t key[kJ];
-  int32_t ps[kJ];
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    const uint32_t e = tid + j * kSelThreads;
-    uint32_t sidx = 0u, start = 0u;
-    for (int q = 0; q < nseg; ++q) {
-      const uint32_t end_q = (uint32_t)__builtin_amdgcn_readlane((int)inc, q);
-      const bool past = end_q <= e;
-      sidx += past ? 1u : 0u;
-      start = past ? end_q : start;
-    }
-    const int64_t g = (e < total) ? rb + (int64_t)sidx * kSegLen + (e - start) : rb;
-    key[j] = a.seg_key[g];
-    ps[j] = a.seg_pos[g];
-  }
   const int n_pad = sel_padded((int)total);
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    const int e = tid + j * kSelThreads;
-    if (e < n_pad) {
-      sm.sel.key[skew(e)] = e < (int)total ? key[j] : 0u;
-      sm.pos[e] = ps[j];
-    }
-  }
+  lists_to_lds<kTauMaxN / kSegLen>(sm, a.seg_key, a.seg_pos, (int64_t)r * a.nseg * kSegLen, kSegLen, nseg, c, inc,
+                                   total);
   __syncthreads();
+  CSA2_MARK(a, 21);
   const LdsKeysT<SelSmemT<kTauKeyWords>> ks{&sm.sel, n_pad};
-  const SelResult res = block_select(sm.sel, ks, K, 0u);
+  const SelResult res = block_select(sm.sel, ks, K, 0u, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 24 : nullptr);
+  CSA2_MARK(a, 22);
   const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
   for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
+  CSA2_MARK(a, 23);
 }
 
 // ---- Top-k spread over the CUs: k below 1024 over rows of at most kDescMaxN
@@ -679,58 +694,9 @@ __global__ __launch_bounds__(kSelThreads) void desc_final_kernel(TopkArgs a) {
       return;
     }
   }
-  // list element e: segment sidx = #{segments whose inclusive end is <= e}
-  auto where = [&](uint32_t e) -> int64_t {
-    uint32_t sidx = 0u, start = 0u;
-    for (int q = 0; q < a.nseg; ++q) {
-      const uint32_t end_q = (uint32_t)__builtin_amdgcn_readlane((int)inc, q);
-      const bool past = end_q <= e;
-      sidx += past ? 1u : 0u;
-      start = past ? end_q : start;
-    }
-    return (e < total) ? rb + (int64_t)sidx * kDescCap + (e - start) : rb;
-  };
-  if (total <= (uint32_t)kRegCap) {
-    // thread t holds elements 4t .. 4t+3 (registers)
-    RegKeys ks;
-    int32_t ps[kRegPer];
-#pragma unroll
-    for (int j = 0; j < kRegPer; ++j) {
-      const uint32_t e = (uint32_t)(kRegPer * tid + j);
-      const int64_t g = where(e);
-      ks.v[j] = a.seg_key[g];
-      ps[j] = a.seg_pos[g];
-    }
-#pragma unroll
-    for (int j = 0; j < kRegPer; ++j) ks.v[j] = (uint32_t)(kRegPer * tid + j) < total ? ks.v[j] : 0u;
-    CSA2_MARK(a, 4);
-    const SelResult res = block_select(sm.sel, ks, K, 0u);
-    const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) {
-      const int j = e & (kRegPer - 1);
-      out[o] = (j == 0) ? ps[0] : (j == 1) ? ps[1] : (j == 2) ? ps[2] : ps[3];
-    });
-    for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
-    CSA2_MARK(a, 5);
-    return;
-  }
-  constexpr int kJ = kTauCap / kSelThreads;
-  uint32_t key[kJ];
-  int32_t ps[kJ];
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    const int64_t g = where((uint32_t)(tid + j * kSelThreads));
-    key[j] = a.seg_key[g];
-    ps[j] = a.seg_pos[g];
-  }
+  // lists longer than their slots: concatenated in LDS
   const int n_pad = sel_padded((int)total);
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    const int e = tid + j * kSelThreads;
-    if (e < n_pad) {
-      sm.sel.key[skew(e)] = e < (int)total ? key[j] : 0u;
-      sm.pos[e] = ps[j];
-    }
-  }
+  lists_to_lds<kDescMaxSeg>(sm, a.seg_key, a.seg_pos, rb, kDescCap, a.nseg, c, inc, total);
   __syncthreads();
   const LdsKeysT<SelSmemT<kTauKeyWords>> ks{&sm.sel, n_pad};
   const SelResult res = block_select(sm.sel, ks, K, 0u);
