@@ -353,6 +353,26 @@ __global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
     return;
   }
   const uint32_t m_s = (uint32_t)(((int64_t)a.k * n + n0 - 1) / n0);
+  if (a.lv[1] && n0 >= 32 * (int64_t)a.k) {
+    // the segment's level-1 values (maxima of 8): each is the maximum of its
+    // own group of level-0 values, so a key with m_s of them at or above it
+    // has m_s level-0 values at or above it (1024 keys in registers; on rows
+    // of at least 32 k values, m_s is at most a quarter of them)
+    const int64_t n1 = lv_count(n0, 1);
+    const int64_t lo1 = lo / 8;
+    const int m1 = (int)max((int64_t)0, min(n1 - lo1, (int64_t)(kSegLen / 8)));
+    const float* b1 = a.lv[1] + (int64_t)r * a.lv_stride[1] + lo1;
+    RegKeys ks;
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      const int e = kRegPer * tid + j;
+      const float x = b1[min(e, m1 - 1)];
+      ks.v[j] = e < m1 ? order_key(x) : 0u;
+    }
+    const SelResult res = block_select(sm, ks, m_s, 2u * m_s);
+    if (tid == 0) a.seg_kth[(int64_t)r * a.nseg + s] = res.T;
+    return;
+  }
   const float* base = a.lv[0] + (int64_t)r * a.lv_stride[0] + lo;
   float v[kSegPer];
 #pragma unroll

@@ -235,6 +235,32 @@ def test_hier_candidates_bitexact(C):
         assert np.array_equal(g[r], O.topk(bm[r, :(L + 7) // 8], 2048)), r
 
 
+def test_hier_candidates_long_rows(C):
+    """Rows of 65536 .. 131072 block maxima (512K .. 1M positions): segment
+    thresholds taken on the maxima of 8 block maxima."""
+    rng = np.random.default_rng(506)
+    lens = [1048576, 1048576, 600000, 524288]
+    R = len(lens)
+    n_max = max(lens)
+    nb_max = (n_max + 7) // 8
+    bm = np.full((R, nb_max), np.nan, np.float32)
+    for r, L in enumerate(lens):
+        if r == 1:      # ~8 copies of each value: ties at the selection edge
+            pool = rng.standard_normal(L // 8).astype(np.float32)
+            s = pool[rng.integers(0, len(pool), size=L)]
+        else:
+            s = rng.standard_normal(L).astype(np.float32)
+        bm[r, :(L + 7) // 8] = O.block_max(s, L)
+    say("hier candidates long rows R", R)
+    ws = workspace(C.csa2_topk_workspace_bytes(R, nb_max, 2048))
+    out = torch.full((R, 2048), -7, dtype=torch.int32, device="cuda")
+    C.csa2_hier_candidates(dev(bm), dev(np.array(lens, np.int32)), n_max, 2048, out, ws)
+    torch.cuda.synchronize()
+    g = host(out)
+    for r, L in enumerate(lens):
+        assert np.array_equal(g[r], O.topk(bm[r, :(L + 7) // 8], 2048)), r
+
+
 # -------------------------------------------------------------- attention --
 
 @pytest.mark.parametrize("paged", [False, True])
