@@ -136,7 +136,7 @@ void carve_desc(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
 }
 
 // Large k over long rows: segment thresholds, then a gather above them.
-bool topk_large_shape(int64_t n_max, int k) { return k >= 1024 && n_max > kSelCapHost && n_max <= kTauMaxN; }
+bool topk_large_shape(int64_t n_max, int k) { return k >= 1024 && n_max >= kSelCapHost && n_max <= kTauMaxN; }
 
 void carve_large(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
   if (!topk_large_shape(n_max, k)) return;

@@ -235,11 +235,12 @@ def test_hier_candidates_bitexact(C):
         assert np.array_equal(g[r], O.topk(bm[r, :(L + 7) // 8], 2048)), r
 
 
-def test_hier_candidates_long_rows(C):
+@pytest.mark.parametrize("lens", [[1048576, 1048576, 600000, 524288], [131072, 131072, 100000, 70000]])
+def test_hier_candidates_long_rows(C, lens):
     """Rows of 65536 .. 131072 block maxima (512K .. 1M positions): segment
-    thresholds taken on the maxima of 8 block maxima."""
-    rng = np.random.default_rng(506)
-    lens = [1048576, 1048576, 600000, 524288]
+    thresholds taken on the maxima of 8 block maxima; rows of at most 16384
+    block maxima (128K positions): two segments."""
+    rng = np.random.default_rng(506 + len(str(lens)))
     R = len(lens)
     n_max = max(lens)
     nb_max = (n_max + 7) // 8
