@@ -27,7 +27,8 @@
 //      each of its 8 keys -- V is read straight from the cache in that layout.
 // A block that covers every step of its row (many rows) keeps an online
 // softmax over the steps and writes the output; otherwise (few rows: decode)
-// each block takes one step and writes a partial (O, max, sum), and
+// each block takes one step (the window step split over two blocks of 64
+// keys, halving the window K/V one CU fetches) and writes a partial (O, max, sum), and
 // attn_merge_kernel combines the partials of each row as one softmax.  (A
 // cross-block hand-off inside one kernel would need a device-scope release,
 // which on this chip writes back the whole L2 of the issuing XCD.)  Several
@@ -149,18 +150,19 @@ CSA2_DEV void qk_main(const AttnSmem& sm, int w, int c, int g, float (&s)[8]) {
 }
 
 // Window keys of this wave's two 16-key groups: lane (c, g) holds key
-// kk0 + 16u + c, dims 128g .. 128g+127 (entry 0 of the buffer stands in for
+// 32w + 16u + c of the step (window entry koff + that), dims 128g .. 128g+127 (entry 0 of the buffer stands in for
 // an absent key; its words are zeroed at use).  Loaded at the head of the
 // window step, with the query, so that one round trip brings both.
 struct WinK {
   uint4 k[2][16];
   uint32_t ok[2];     // all-ones when the key is present
 };
-CSA2_DEV void win_k_load(const AttnLayer& Ly, int b, int wst, int wl, int kk0, int c, int g, WinK& wk) {
+CSA2_DEV void win_k_load(const AttnLayer& Ly, int b, int wst, int wl, int koff, int nkeys, int w, int c, int g,
+                         WinK& wk) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int kk = kk0 + 16 * u + c;
-    const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
+    const int e = 32 * w + 16 * u + c, kk = koff + e;
+    const bool ok = e < nkeys && kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
     const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
 #pragma unroll
     for (int t = 0; t < 16; ++t) wk.k[u][t] = src[t];
@@ -214,10 +216,11 @@ CSA2_DEV void pv_main(const AttnSmem& sm, RowState& st, int w, int c, int g) {
   }
 }
 
-// Window V words of keys 32 ks + 8g + i (i < 8), dims 128w + 8c .. 128w + 8c + 7
-// (zero for an absent key).
-CSA2_DEV void win_v_load(const AttnLayer& Ly, int b, int wst, int wl, int ks, int w, int c, int g, uint4 (&vr)[8]) {
-  const int key0 = 32 * ks + 8 * g;
+// Window V words of keys 32 ks + 8g + i (i < 8) of the step (window entries
+// koff + those), dims 128w + 8c .. 128w + 8c + 7 (zero for an absent key).
+CSA2_DEV void win_v_load(const AttnLayer& Ly, int b, int wst, int wl, int koff, int ks, int w, int c, int g,
+                         uint4 (&vr)[8]) {
+  const int key0 = koff + 32 * ks + 8 * g;
   uint4 v[8];
   bool okv[8];
 #pragma unroll
@@ -249,15 +252,20 @@ CSA2_DEV void pv_win_part(const AttnSmem& sm, RowState& st, int ks, int c, int g
   }
 }
 
-// The window step's P V: the first two 32-key parts were loaded before the
-// softmax statistics; the later parts are loaded ahead of the MFMAs that
-// precede their use.
-CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int w, int c,
-                     int g, const uint4 (&v0)[8], const uint4 (&v1)[8]) {
+// The window step's P V over its 32-key parts (4, or 2 for half a window):
+// the first two were loaded before the softmax statistics; the later ones are
+// loaded ahead of the MFMAs that precede their use.
+CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int koff,
+                     int nparts, int w, int c, int g, const uint4 (&v0)[8], const uint4 (&v1)[8]) {
+  if (nparts <= 2) {
+    pv_win_part(sm, st, 0, c, g, v0);
+    pv_win_part(sm, st, 1, c, g, v1);
+    return;
+  }
   uint4 v2[8], v3[8];
-  win_v_load(Ly, b, wst, wl, 2, w, c, g, v2);
+  win_v_load(Ly, b, wst, wl, koff, 2, w, c, g, v2);
   pv_win_part(sm, st, 0, c, g, v0);
-  win_v_load(Ly, b, wst, wl, 3, w, c, g, v3);
+  win_v_load(Ly, b, wst, wl, koff, 3, w, c, g, v3);
   pv_win_part(sm, st, 1, c, g, v1);
   pv_win_part(sm, st, 2, c, g, v2);
   pv_win_part(sm, st, 3, c, g, v3);
@@ -265,14 +273,14 @@ CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int 
 
 // Window step with loads issued part by part (the variant with two blocks
 // per CU, whose register budget does not hold the batched loads).
-CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int kk0, int c, int g,
-                         float (&s)[8]) {
+CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int koff, int nkeys, int w,
+                         int c, int g, float (&s)[8]) {
   const uint4* qrow = sm.q + c * kQRow + 16 * g;
 #pragma unroll 1
   for (int u = 0; u < 2; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int kk = kk0 + 16 * u + c;
-    const bool ok = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
+    const int e = 32 * w + 16 * u + c, kk = koff + e;
+    const bool ok = e < nkeys && kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
     const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
     uint4 kr[16];
 #pragma unroll
@@ -286,12 +294,12 @@ CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst
     for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
   }
 }
-CSA2_DEV void pv_win_seq(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int w,
-                         int c, int g) {
+CSA2_DEV void pv_win_seq(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int koff,
+                         int nparts, int w, int c, int g) {
 #pragma unroll 1
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < nparts; ++ks) {
     uint4 vr[8];
-    win_v_load(Ly, b, wst, wl, ks, w, c, g, vr);
+    win_v_load(Ly, b, wst, wl, koff, ks, w, c, g, vr);
     pv_win_part(sm, st, ks, c, g, vr);
   }
 }
@@ -424,8 +432,21 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int b = a.row_seq ? a.row_seq[r] : r;
   const int L = a.seq_len[b];
   const int n_main = (a.k + kStepKeys - 1) / kStepKeys;
-  const int st0 = blk * a.steps_per_block;
-  const int st1 = min(n_main + 1, st0 + a.steps_per_block);
+  // one step per block (decode) with n_main + 2 blocks per row-layer: the
+  // window step is split over two blocks of 64 keys (whalf 0, 1); otherwise
+  // whole steps (whalf -1)
+  int st0, st1, whalf = -1;
+  if (a.steps_per_block == 1 && a.n_blocks == n_main + 2 && blk >= n_main) {
+    st0 = n_main;
+    st1 = n_main + 1;
+    whalf = blk - n_main;
+  } else {
+    st0 = blk * a.steps_per_block;
+    st1 = min(n_main + 1, st0 + a.steps_per_block);
+  }
+  const int koff = whalf < 0 ? 0 : (kStepKeys / 2) * whalf;        // the step's first window entry
+  const int nwk = whalf < 0 ? kStepKeys : kStepKeys / 2;           // its window keys
+  const int nwp = nwk / 32;                                         // 32-key parts
   const int32_t* idx_row = a.idx + (int64_t)r * a.k;
   const int wst = Ly.swa_start[r];
   const int wl = min(Ly.swa_len[r], CSA2_MAX_WINDOW);
@@ -496,30 +517,30 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];
       store_q(sm, qv, false, tid);
       const int e = 32 * w + (lane & 31);
-      const uint64_t vmask = __ballot(e < wl && wst >= 0 && (int64_t)wst + e < Ly.S);
+      const uint64_t vmask = __ballot(e < nwk && koff + e < wl && wst >= 0 && (int64_t)wst + koff + e < Ly.S);
       __syncthreads();    // query visible
       float s[8];
-      qk_win_seq(Ly, sm, wb, wst, wl, 32 * w, c, g, s);
+      qk_win_seq(Ly, sm, wb, wst, wl, koff, nwk, w, c, g, s);
       step_softmax<false>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
-      pv_win_seq(Ly, sm, st, wb, wst, wl, w, c, g);
+      pv_win_seq(Ly, sm, st, wb, wst, wl, koff, nwp, w, c, g);
     } else {
       WinK wk;
-      win_k_load(Ly, wb, wst, wl, 32 * w, c, g, wk);
+      win_k_load(Ly, wb, wst, wl, koff, nwk, w, c, g, wk);
       uint4 qv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];
       store_q(sm, qv, false, tid);
       const int e = 32 * w + (lane & 31);
-      const uint64_t vmask = __ballot(e < wl && wst >= 0 && (int64_t)wst + e < Ly.S);
+      const uint64_t vmask = __ballot(e < nwk && koff + e < wl && wst >= 0 && (int64_t)wst + koff + e < Ly.S);
       __syncthreads();    // query visible
       float s[8];
       qk_win(sm, wk, c, g, s);
-      // the first half of the window values, in flight during the statistics
+      // the first two 32-key parts of the values, in flight during the statistics
       uint4 v0[8], v1[8];
-      win_v_load(Ly, wb, wst, wl, 0, w, c, g, v0);
-      win_v_load(Ly, wb, wst, wl, 1, w, c, g, v1);
+      win_v_load(Ly, wb, wst, wl, koff, 0, w, c, g, v0);
+      win_v_load(Ly, wb, wst, wl, koff, 1, w, c, g, v1);
       step_softmax<false>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
-      pv_win(Ly, sm, st, wb, wst, wl, w, c, g, v0, v1);
+      pv_win(Ly, sm, st, wb, wst, wl, koff, nwp, w, c, g, v0, v1);
     }
     __syncthreads();    // P, slots and statistics may be overwritten by the next step
   }
@@ -622,6 +643,9 @@ int attn_blocks(int k, int rows_x_layers, int* steps_per_block) {
   // per row-layer writes its output directly
   const int spb = (rows_x_layers >= 512) ? n_steps : 1;
   if (steps_per_block) *steps_per_block = spb;
+  // one step per block: the window step in two halves when the launch still
+  // fits on the CUs at one block each
+  if (spb == 1) return (int64_t)rows_x_layers * (n_steps + 1) <= 256 ? n_steps + 1 : n_steps;
   return (n_steps + spb - 1) / spb;
 }
 
