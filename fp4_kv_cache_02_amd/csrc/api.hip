@@ -135,7 +135,7 @@ void carve_desc(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
   t.desc_pos = bp.take<int32_t>((size_t)R * kDescMaxSeg * kDescCap);
 }
 
-// Large k over long rows: segment thresholds, then a gather above them.
+// Large k over long rows: per-segment gathers above one threshold per row.
 bool topk_large_shape(int64_t n_max, int k) { return k >= 1024 && n_max >= kSelCapHost && n_max <= kTauMaxN; }
 
 void carve_large(Bump& bp, TopkWs& t, int R, int64_t n_max, int k) {
@@ -191,8 +191,8 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
   a.out_stride = k;
   a.row_list = nullptr;
   a.row_list_count = nullptr;
-  a.seg_kth = nullptr;
   a.nseg = 0;
+  a.seg_kth = nullptr;
   a.seg_cnt = nullptr;
   a.seg_key = nullptr;
   a.seg_pos = nullptr;
@@ -223,7 +223,7 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
     a.lv[l] = dst;
   }
   CSA2_SET_TRACE(a, 1);
-  if (tw.seg_kth && a.lv[1] && !a.cand_blocks && !a.row_list && topk_large_shape(a.n_max, a.k)) {
+  if (tw.seg_cnt && a.lv[1] && !a.cand_blocks && !a.row_list && topk_large_shape(a.n_max, a.k)) {
     a.seg_kth = tw.seg_kth;
     a.nseg = (int32_t)cdiv(a.n_max, kSegLen);
     a.seg_cnt = tw.seg_cnt;

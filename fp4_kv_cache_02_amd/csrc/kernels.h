@@ -49,7 +49,8 @@ struct TopkArgs {
   int32_t out_stride;
   const int32_t* row_list;    // optional: select only rows row_list[0 .. *row_list_count)
   const uint32_t* row_list_count;
-  // large-k path: per (row, segment) thresholds and gathered values
+  // segmented paths: per (row, segment) thresholds (rows of more than 16384
+  // values) and lists of gathered values
   uint32_t* seg_kth;          // [R][nseg] or null
   int32_t nseg;
   uint32_t* seg_cnt;          // [R][nseg]: values >= tau gathered per segment

@@ -50,20 +50,23 @@ constexpr int kSelBatch = 8;
 constexpr int kSelPad = kSelBatch * kSelThreads;    // 4096
 CSA2_DEV int sel_padded(int n) { return (n + kSelPad - 1) / kSelPad * kSelPad; }
 
-// Keys in registers: thread t holds elements kRegPer*t + j.
-struct RegKeys {
-  uint32_t v[kRegPer];
+// Keys in registers: thread t holds elements N*t .. N*t+N-1 (the element
+// order matters only to block_compact).
+template <int N>
+struct RegKeysN {
+  uint32_t v[N];
   template <class F>
   CSA2_DEV void each(const F& f) const {
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) f(v[j]);
+    for (int j = 0; j < N; ++j) f(v[j]);
   }
   template <class F>
   CSA2_DEV void each_owned(const F& f) const {       // contiguous, in element order
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) f(v[j], kRegPer * (int)threadIdx.x + j);
+    for (int j = 0; j < N; ++j) f(v[j], N * (int)threadIdx.x + j);
   }
 };
+using RegKeys = RegKeysN<kRegPer>;
 
 // Keys in LDS: sm.key[skew(e)] for e < n (n a multiple of kSelPad).
 template <class Sm>

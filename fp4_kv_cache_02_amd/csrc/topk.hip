@@ -322,16 +322,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
 // ---- large k over a long row (the 2048 candidate blocks of a hierarchical
 // indexer at up to 1M positions) ----
 //
-// seg_kth_kernel, grid (segments, rows): segment s of kSegLen level-0 values
-// (n_s of the row's n0) takes a key t_s with at least m_s = ceil(k n_s / n0)
-// of its values >= t_s (a bin edge near its m_s-th largest; 0 when it holds at
-// most m_s present values; all-ones for an empty segment).  Their minimum tau
-// has at least m_s values >= tau in every segment, sum m_s >= k of them in the
-// row, so the row's k-th largest value is >= tau and the row's top k lie among
-// the values >= tau -- typically a little more than k values.
-// seg_gather_kernel, grid (segments, rows): the values >= tau of each segment,
-// in index order, into the segment's own list (every segment on its own CU:
-// one CU fetching the whole row is bound by the misses it keeps in flight).
+// seg_tau_gather_kernel, grid (segments of kSegLen level-0 values, rows):
+// every block of a row takes the same threshold tau from the row's lowest
+// level of at most kSelCap values (level 0 on rows of at most kSelCap values,
+// else the maxima of 8), held in registers: a bin edge with k <= #{level
+// values >= tau} <= 1.5 k (tau = 1, every present value, when at most k are
+// present).  Each level value >= tau is the maximum of its own group, so at
+// least k level-0 values are >= tau and the row's top k lie among them.  The
+// block gathers its segment's values >= tau, in index order, into the
+// segment's own list (every segment on its own CU: one CU fetching the whole
+// row is bound by the misses it keeps in flight).
 // seg_final_kernel, one block per row: the lists concatenated in segment
 // order (= index order) and the exact top k of them; a row with more than
 // kTauCap gathered values takes the general path in the same block.
@@ -339,8 +339,79 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
 constexpr int kTauCap = 8192;             // gathered values a row's final selection holds
 constexpr int kTauKeyWords = kTauCap + kTauCap / 32;
 constexpr int kSegPer = kSegLen / kSelThreads;   // values per thread of a segment
-static_assert(kSegLen == 2 * kSelPad, "a segment is two LDS key batches");
+constexpr int kTopPer = kSelCap / kSelThreads;   // values per thread of the threshold level
 static_assert(kTauMaxN / kSegLen <= kWave, "one segment per lane of a wave");
+static_assert(kSegLen == 2 * kSelPad, "a segment is two LDS key batches");
+static_assert(kTauMaxN <= 8 * kSelCap, "the maxima of 8 of a row fit the threshold level");
+
+__global__ __launch_bounds__(kSelThreads) void seg_tau_gather_kernel(TopkArgs a) {
+  __shared__ SelSmemT<1> sm;                       // (the keys stay in registers)
+  __shared__ uint32_t cnt[kSegPer * kSelWaves];    // values kept per (round, wave)
+  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t n0 = row_count(a, r);
+  const int64_t lo = (int64_t)s * kSegLen;
+  const int n = (int)max((int64_t)0, min(n0 - lo, (int64_t)kSegLen));
+  const int64_t rs = (int64_t)r * a.nseg + s;
+  if (n == 0) {
+    if (tid == 0) a.seg_cnt[rs] = 0u;
+    return;
+  }
+  // every load at once: the threshold level (element t + 512 j) and the
+  // segment (element t + 512 j: coalesced; index order = (round, wave, lane))
+  const int T = n0 <= kSelCap ? 0 : 1;
+  const int64_t nT = lv_count(n0, T);
+  const float* tb = lv_row(a, T, r);
+  float tv[kTopPer];
+#pragma unroll
+  for (int j = 0; j < kTopPer; ++j) tv[j] = tb[min((int64_t)(tid + j * kSelThreads), nT - 1)];
+  const float* base = a.lv[0] + (int64_t)r * a.lv_stride[0] + lo;
+  float v[kSegPer];
+#pragma unroll
+  for (int j = 0; j < kSegPer; ++j) v[j] = base[min(tid + j * kSelThreads, n - 1)];
+  RegKeysN<kTopPer> top;
+#pragma unroll
+  for (int j = 0; j < kTopPer; ++j) top.v[j] = (tid + j * kSelThreads < nT) ? order_key(tv[j]) : 0u;
+  const uint32_t K = (uint32_t)a.k;
+  const SelResult sr = block_select(sm, top, K, K + K / 2);
+  const uint32_t tau = max(sr.T, 1u);
+  uint32_t keepm = 0u;
+#pragma unroll
+  for (int j = 0; j < kSegPer; ++j) {
+    const bool kp = tid + j * kSelThreads < n && order_key(v[j]) >= tau;
+    keepm |= kp ? (1u << j) : 0u;
+    const uint64_t b = __ballot(kp);
+    if (lane == 0) cnt[j * kSelWaves + wv] = (uint32_t)__popcll(b);
+  }
+  __syncthreads();
+  // offsets of the (round, wave) runs: an exclusive scan in that order
+  uint32_t tot;
+  const uint32_t off = block_excl_scan(sm, tid < kSegPer * kSelWaves ? cnt[tid] : 0u, tot);
+  if (tid < kSegPer * kSelWaves) cnt[tid] = off;
+  __syncthreads();
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  uint32_t* kd = a.seg_key + rs * kSegLen;
+  int32_t* pd = a.seg_pos + rs * kSegLen;
+#pragma unroll
+  for (int j = 0; j < kSegPer; ++j) {
+    const bool kp = (keepm >> j) & 1u;
+    const uint64_t b = __ballot(kp);
+    if (kp) {
+      const uint32_t p = cnt[j * kSelWaves + wv] + (uint32_t)__popcll(b & lt_mask);
+      kd[p] = order_key(v[j]);
+      pd[p] = (int32_t)(lo + tid + j * kSelThreads);
+    }
+  }
+  if (tid == 0) a.seg_cnt[rs] = tot;
+}
+
+// Rows longer than kSelCap values: the threshold per segment instead, from
+// the segment's own values, in a launch of its own (seg_kth_kernel: on rows of
+// at least 32 k values from the segment's 1024 maxima of 8, in registers); the
+// minimum over the row's segments tau has at least k values at or above it,
+// and seg_gather_kernel gathers each segment's values >= tau.  (One block
+// per segment selecting over the row's 16384 maxima of 8 costs more than the
+// extra launch.)
 
 __global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
   __shared__ SelSmemT<kSegLen + kSegLen / 32> sm;
@@ -754,12 +825,16 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Large k over rows of at most kTauMaxN values: segment thresholds, the
-// per-segment gather above their minimum, the final selection.
+// Large k over rows of at most kTauMaxN values: the per-segment gather above
+// the row's threshold, the final selection.
 hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
-  hipLaunchKernelGGL(seg_kth_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
-  hipLaunchKernelGGL(seg_gather_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+  if (a.n_max <= kSelCap) {
+    hipLaunchKernelGGL(seg_tau_gather_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(seg_kth_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+    hipLaunchKernelGGL(seg_gather_kernel, dim3(a.nseg, a.R), dim3(kSelThreads), 0, st, a);
+  }
   hipLaunchKernelGGL(seg_final_kernel, dim3(a.R), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
