@@ -58,7 +58,7 @@ CSA2_DEV StepGeo step_geo(const IdxArgs& a, uint32_t item, int g) {
   s.t = __builtin_amdgcn_readfirstlane((int)(item - (uint32_t)s.r * (uint32_t)a.steps_per_row));
   if (a.row_list) s.r = __builtin_amdgcn_readfirstlane(a.row_list[s.r]);
   s.b = a.row_seq ? a.row_seq[s.r] : s.r;
-  s.L = min(a.seq_len[s.b], a.n_max);
+  s.L = __builtin_amdgcn_readfirstlane(min(a.seq_len[s.b], a.n_max));
   int64_t pos0;
   if (CAND) {
     const int ci = s.t * 8 + g;
@@ -137,6 +137,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IdxArgs a) 
   const uint4* __restrict__ kd = a.kdata;
   uint4 regs[8];
   StepGeo cur = step_geo<CAND>(a, item, g);
+  // a scan step past its row's visible positions writes nothing: leave before
+  // any load (rows of a batch differ in length; the grid covers the longest)
+  if (!CAND && !PERSIST && cur.t * 64 >= cur.L) return;
 #pragma unroll
   for (int i = 0; i < 8; ++i) regs[i] = key_chunk<FP8>(kd, cur, i, j);
   // FP8 keys: the scale of the position this lane finishes (slot 0 when absent)
