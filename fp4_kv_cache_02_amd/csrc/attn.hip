@@ -643,9 +643,13 @@ int attn_blocks(int k, int rows_x_layers, int* steps_per_block) {
   // per row-layer writes its output directly
   const int spb = (rows_x_layers >= 512) ? n_steps : 1;
   if (steps_per_block) *steps_per_block = spb;
-  // one step per block: the window step in two halves when the launch still
-  // fits on the CUs at one block each
-  if (spb == 1) return (int64_t)rows_x_layers * (n_steps + 1) <= 256 ? n_steps + 1 : n_steps;
+  // one step per block: the window step in two halves, unless that alone would
+  // take the launch past one block per CU
+  if (spb == 1) {
+    const int64_t rl = rows_x_layers;
+    if (rl * (n_steps + 1) <= 256 || rl * n_steps > 256) return n_steps + 1;
+    return n_steps;
+  }
   return (n_steps + spb - 1) / spb;
 }
 
