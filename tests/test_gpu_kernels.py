@@ -315,6 +315,57 @@ def test_attention_parity(C, paged):
         assert lse_ok(gl[r], rl), (r, gl[r], rl)
 
 
+@pytest.mark.parametrize("R", [7, 64])
+def test_attention_window_lengths(C, R):
+    """Window lengths across the two 64-key halves of the window step (0, 1,
+    40, 64, 65, 100, 128; windows ending at the buffer's last entry), one
+    launch of R rows: 7 rows run one block per CU, 64 rows two blocks per CU
+    (both with the window step split over two blocks)."""
+    rng = np.random.default_rng(909 + R)
+    lens = [3000, 700, 2000, 1200]
+    B = len(lens)
+    n_max = max(lens)
+    kvp = [rand_fp4(rng, L) for L in lens]
+    pt, stride, n_slots = None, n_max, B * n_max
+    P = place([p for p, _ in kvp], lens, n_slots, pt, stride, 256, np.uint8)
+    Sc = place([s for _, s in kvp], lens, n_slots, pt, stride, 32, np.uint8)
+    row_seq = (np.arange(R) % B).astype(np.int32)
+    k = 512
+    idx = np.full((R, k), -1, np.int32)
+    for r in range(R):
+        L = lens[row_seq[r]]
+        m = int(rng.integers(0, min(L, k) + 1))
+        idx[r, :m] = np.sort(rng.choice(L, size=m, replace=False))
+    S = 140
+    swk, swv = bf16(rng, (B, S, 512)), bf16(rng, (B, S, 512))
+    choices = [0, 1, 40, 64, 65, 100, 128]
+    ln = np.array([choices[r % len(choices)] for r in range(R)], np.int32)
+    st = np.array([S - ln[r] if r % 2 else int(rng.integers(0, S - ln[r] + 1)) for r in range(R)], np.int32)
+    q = bf16(rng, (R, 16, 512))
+    sm = 1.0 / math.sqrt(512)
+    say("attention window lengths R", R)
+    kv = C.make_cache(dev(P), dev(Sc), seq_stride=stride)
+    out = torch.full((R, 16, 512), float("nan"), device="cuda")
+    lse = torch.full((R, 16), float("nan"), device="cuda")
+    ws = workspace(C.csa2_attn_workspace_bytes(R))
+    C.csa2_fp4_sparse_attn(dev(q), kv, dev(np.array(lens, np.int32)), dev(idx), dev(swk), dev(swv), dev(st),
+                           dev(ln), sm, out, lse, ws, row_seq=dev(row_seq))
+    torch.cuda.synchronize()
+    g, gl = host(out), host(lse)
+    cache = O.Cache(P, Sc, np.zeros((n_slots, 64), np.uint16), lens, pt, 64, stride)
+    for r in range(R):
+        b = row_seq[r]
+        sel = idx[r][idx[r] >= 0]
+        ref, rl = O.attention(q[r], cache.kv_rows(b, sel), swk[b, st[r]:st[r] + ln[r]],
+                              swv[b, st[r]:st[r] + ln[r]], sm)
+        if sel.size == 0 and ln[r] == 0:
+            assert np.all(g[r] == 0) and np.all(np.isneginf(gl[r])), r
+            continue
+        e = rel_err(g[r], ref)
+        assert np.all(e <= ATTN_TOL), (r, ln[r], e.max())
+        assert lse_ok(gl[r], rl), (r, gl[r], rl)
+
+
 def test_attention_empty_row_and_single_key(C):
     rng = np.random.default_rng(707)
     P, Sc = rand_fp4(rng, 10)
