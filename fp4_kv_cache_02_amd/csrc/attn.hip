@@ -416,14 +416,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int per = a.n_layers * a.n_blocks;                // blocks of one row
   const int full = (a.R / 8) * 8 * per;                   // ids in complete runs of 8 rows
   int r, sub;
-  if (a.steps_per_block > 1 && (a.R & 7) == 0) {
-    // many rows (prefill chunk): XCD x takes the contiguous rows
-    // [x R/8, (x+1) R/8), so the rows resident on an XCD at once are
-    // neighbours, whose windows share all but one entry
-    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
-    r = x * (a.R >> 3) + i / per;
-    sub = i - (i / per) * per;
-  } else if ((int)blockIdx.x < full) {
+  if ((int)blockIdx.x < full) {
     const int q = blockIdx.x / (8 * per), rem = blockIdx.x - q * 8 * per;
     r = 8 * q + (rem & 7);
     sub = rem >> 3;
