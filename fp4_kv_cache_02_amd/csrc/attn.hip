@@ -432,17 +432,25 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int b = a.row_seq ? a.row_seq[r] : r;
   const int L = a.seq_len[b];
   const int n_main = (a.k + kStepKeys - 1) / kStepKeys;
-  // one step per block (decode) with n_main + 2 blocks per row-layer: the
-  // window step is split over two blocks of 64 keys (whalf 0, 1); otherwise
-  // whole steps (whalf -1)
+  // One block per row-layer (n_blocks 1, many rows): every step.  Otherwise
+  // (decode) the main steps in blocks of steps_per_block (1 or 2), then the
+  // window step in one block, or split over two blocks of 64 keys (whalf 0,
+  // 1) when the row-layer has one block more.
   int st0, st1, whalf = -1;
-  if (a.steps_per_block == 1 && a.n_blocks == n_main + 2 && blk >= n_main) {
-    st0 = n_main;
+  if (a.n_blocks == 1) {
+    st0 = 0;
     st1 = n_main + 1;
-    whalf = blk - n_main;
   } else {
-    st0 = blk * a.steps_per_block;
-    st1 = min(n_main + 1, st0 + a.steps_per_block);
+    const int mpb = a.steps_per_block;
+    const int nmb = (n_main + mpb - 1) / mpb;           // blocks of main steps
+    if (blk < nmb) {
+      st0 = blk * mpb;
+      st1 = min(n_main, st0 + mpb);
+    } else {
+      st0 = n_main;
+      st1 = n_main + 1;
+      if (a.n_blocks == nmb + 2) whalf = blk - nmb;
+    }
   }
   const int koff = whalf < 0 ? 0 : (kStepKeys / 2) * whalf;        // the step's first window entry
   const int nwk = whalf < 0 ? kStepKeys : kStepKeys / 2;           // its window keys
@@ -638,19 +646,29 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 int attn_steps(int k) { return (k + kStepKeys - 1) / kStepKeys + 1; }
 
 int attn_blocks(int k, int rows_x_layers, int* steps_per_block) {
-  const int n_steps = attn_steps(k);
-  // few row-layers: one step per block (partials + merge); many: one block
-  // per row-layer writes its output directly
-  const int spb = (rows_x_layers >= 512) ? n_steps : 1;
-  if (steps_per_block) *steps_per_block = spb;
-  // one step per block: the window step in two halves, unless that alone would
-  // take the launch past one block per CU
-  if (spb == 1) {
-    const int64_t rl = rows_x_layers;
-    if (rl * (n_steps + 1) <= 256 || rl * n_steps > 256) return n_steps + 1;
-    return n_steps;
+  const int n_steps = attn_steps(k), n_main = n_steps - 1;
+  // many row-layers: one block per row-layer writes its output directly
+  if (rows_x_layers >= 512) {
+    if (steps_per_block) *steps_per_block = n_steps;
+    return 1;
   }
-  return (n_steps + spb - 1) / spb;
+  // few (decode): partials + merge.  One main step per block and the window
+  // step in two halves while the launch fits on the CUs at one block each
+  // (else the window step whole, if that fits); past that, two blocks per CU:
+  // the window step in halves, and two main steps per block when one each
+  // would take the launch past one round of two blocks per CU.
+  const int64_t rl = rows_x_layers;
+  int mpb = 1, nb = n_main + 2;
+  if (rl * (n_main + 2) > 256) {
+    if (rl * (n_main + 1) <= 256) {
+      nb = n_main + 1;
+    } else if (rl * (n_main + 2) > 512 && n_main > 1) {
+      mpb = 2;
+      nb = (n_main + 1) / 2 + 2;
+    }
+  }
+  if (steps_per_block) *steps_per_block = mpb;
+  return nb;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {

@@ -315,12 +315,13 @@ def test_attention_parity(C, paged):
         assert lse_ok(gl[r], rl), (r, gl[r], rl)
 
 
-@pytest.mark.parametrize("R", [7, 64])
+@pytest.mark.parametrize("R", [7, 64, 96])
 def test_attention_window_lengths(C, R):
     """Window lengths across the two 64-key halves of the window step (0, 1,
     40, 64, 65, 100, 128; windows ending at the buffer's last entry), one
     launch of R rows: 7 rows run one block per CU, 64 rows two blocks per CU
-    (both with the window step split over two blocks)."""
+    (both with the window step split over two blocks), 96 rows two main steps
+    per block."""
     rng = np.random.default_rng(909 + R)
     lens = [3000, 700, 2000, 1200]
     B = len(lens)
