@@ -176,6 +176,32 @@ def test_topk_bitexact(C, k):
 
 
 @pytest.mark.parametrize("k", [7, 512])
+def test_topk_bitexact_long_rows(C, k):
+    """Rows of 131073 .. 1048576 values (one block per row descending three
+    levels of maxima), every distribution, beside a short row in the same
+    launch."""
+    rng = np.random.default_rng(800 + k)
+    kinds = ["normal", "ties", "zeros", "equal", "clustered", "neginf", "copies"]
+    ns = [131073, 1048576, 300000]
+    rows = [(kd, n) for kd in kinds for n in ns] + [("normal", 5000)]
+    R = len(rows)
+    n_max = max(n for _, n in rows)
+    scores = np.full((R, n_max), np.nan, np.float32)
+    nv = np.zeros(R, np.int32)
+    for r, (kd, n) in enumerate(rows):
+        scores[r, :n] = _topk_case(rng, kd, n)
+        nv[r] = n
+    say("topk long rows k", k, "R", R)
+    ws = workspace(C.csa2_topk_workspace_bytes(R, n_max, k))
+    out = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    C.csa2_topk(dev(scores), k, out, ws, n_valid=dev(nv))
+    torch.cuda.synchronize()
+    g = host(out)
+    for r, (kd, n) in enumerate(rows):
+        assert np.array_equal(g[r], O.topk(scores[r, :n], k)), (kd, n, k)
+
+
+@pytest.mark.parametrize("k", [7, 512])
 @pytest.mark.parametrize("mapped", [False, True])
 def test_topk_bitexact_short_rows(C, k, mapped):
     """Rows of at most 16384 values (the Reindex candidates' size): the
