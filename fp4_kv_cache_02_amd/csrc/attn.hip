@@ -476,6 +476,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   // overlap).  In each, the loads that head its longest chain go first -- the
   // main keys' indices (their slots, then their rows), or the window keys --
   // with the query in flight beside them.
+  // a block with several main steps loads the next step's index while the
+  // current step runs (the index heads each step's chain of loads)
+  int pos_next = -1;
   for (int step = st0; step < st1; ++step) {
     const bool is_main = step < n_main;
     const bool need_q = step == st0 || !is_main;
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       int pos = -1;
       if (tid < kStepKeys) {
         const int kk = step * kStepKeys + tid;
-        pos = kk < a.k ? idx_row[kk] : -1;
+        pos = (step > st0) ? pos_next : (kk < a.k ? idx_row[kk] : -1);
       }
       uint4 qv[4];
       if (need_q) {
@@ -504,6 +507,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       for (int i = 0; i < 8; ++i) rv[i] = src[i];
       const uint4 rsc = *(const uint4*)(a.kv_scale + ss * 32 + 16 * half);
       const uint32_t rmask = sl >= 0 ? 0xFFFFFFFFu : 0u;    // (a select of whole uint4s goes through scratch)
+      if (tid < kStepKeys && step + 1 < min(st1, n_main)) {
+        const int kk = (step + 1) * kStepKeys + tid;
+        pos_next = kk < a.k ? idx_row[kk] : -1;
+      }
       if (kEarly && need_q) store_q(sm, qv, true, tid);
       uint4* dst = (uint4*)&sm.code[key * kCodeRow + 32 * half];
 #pragma unroll
