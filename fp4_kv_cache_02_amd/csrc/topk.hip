@@ -588,8 +588,25 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
   }
   CSA2_MARK(a, 20);
   // segment counts and their offsets (one segment per lane; every wave alike)
+  // and, in the same round of loads, the fixed register slots of the fast
+  // path below: segment s owns slots [spp s, spp (s+1)), thread t slots
+  // 16t .. 16t+15
   const int nseg = (int)((n0 + kSegLen - 1) / kSegLen);
   const uint32_t c = lane < nseg ? a.seg_cnt[(int64_t)r * a.nseg + lane] : 0u;
+  constexpr int kPer = kTauCap / kSelThreads;
+  const int spp = min(kTauCap / nseg, kSegLen) & ~(kPer - 1);
+  const int sg = kPer * tid / spp, sl0 = kPer * tid - sg * spp;
+  const int64_t rb0 = (int64_t)r * a.nseg * kSegLen;
+  const int64_t g0 = sg < nseg ? rb0 + (int64_t)sg * kSegLen + sl0 : rb0;
+  uint32_t kk[kPer];
+  int32_t pp[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer / 4; ++q) {
+    const uint4 x = *(const uint4*)(a.seg_key + g0 + 4 * q);
+    const int4 y = *(const int4*)(a.seg_pos + g0 + 4 * q);
+    kk[4 * q] = x.x; kk[4 * q + 1] = x.y; kk[4 * q + 2] = x.z; kk[4 * q + 3] = x.w;
+    pp[4 * q] = y.x; pp[4 * q + 1] = y.y; pp[4 * q + 2] = y.z; pp[4 * q + 3] = y.w;
+  }
   const uint32_t inc = wave_incl_scan_u32(c);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
   if (total > (uint32_t)kTauCap) {
@@ -601,9 +618,23 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
     }
     return;
   }
+  // fast path: every list fits its slots; thread order is then (segment,
+  // list position) order = index order, slots past a list's length absent
+  if (__ballot(c > (uint32_t)spp) == 0ull) {
+    const uint32_t cs = (uint32_t)__shfl((int)c, sg < nseg ? sg : 0, 64);
+    RegKeysN<kPer> ks;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) ks.v[j] = (sg < nseg && (uint32_t)(sl0 + j) < cs) ? kk[j] : 0u;
+    CSA2_MARK(a, 21);
+    const SelResult res = block_select(sm.sel, ks, K, 0u);
+    CSA2_MARK(a, 22);
+    const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) { out[o] = pp[e & (kPer - 1)]; });
+    for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;
+    CSA2_MARK(a, 23);
+    return;
+  }
   const int n_pad = sel_padded((int)total);
-  lists_to_lds<kTauMaxN / kSegLen>(sm, a.seg_key, a.seg_pos, (int64_t)r * a.nseg * kSegLen, kSegLen, nseg, c, inc,
-                                   total);
+  lists_to_lds<kTauMaxN / kSegLen>(sm, a.seg_key, a.seg_pos, rb0, kSegLen, nseg, c, inc, total);
   __syncthreads();
   CSA2_MARK(a, 21);
   const LdsKeysT<SelSmemT<kTauKeyWords>> ks{&sm.sel, n_pad};
