@@ -5,7 +5,12 @@
 // Order: value descending, index ascending (-0 below +0); -inf = absent;
 // output ascending indices, -1 padding.
 //
-// One block per row descends a tree of maxima.  Level 0 holds the n values;
+// Three paths share the selection primitives of select.h: the split path
+// (desc_seg_kernel + desc_final_kernel, below) for k below 1024 on rows of up
+// to 131072 values, the large-k path (seg_*_kernel) for the 2048 candidate
+// blocks, and topk_kernel for every other shape and as the fallback of both.
+//
+// topk_kernel: one block per row descends a tree of maxima.  Level 0 holds the n values;
 // level l+1 holds the maximum of each group of 8 consecutive level-l values
 // (the indexer scan emits levels 1 and 2 as it scores; `maxima_kernel` builds
 // them for other callers).  The descent rests on one fact: if a group holds an
