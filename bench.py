@@ -287,6 +287,28 @@ def measure_model(ws, steps, warmup, n_replicas):
             "replicas": len(runners), "setup_s": t_setup}
 
 
+def copy_bandwidth_gbps(nbytes=1 << 30, reps=5):
+    """Device-to-device copy of nbytes (read + write = 2 x nbytes moved) timed
+    with events on the current stream: the HBM rate a plain streaming kernel
+    reaches on this GPU, beside the vendor peak."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -339,10 +361,12 @@ def main():
         traffic = traffic_from_profiles(os.path.join(ROOT, "fp4_kv_cache_02_amd", "csrc", "index_score.hip"))
         if w.name != "cfg1_F3R_b8_L131072":
             traffic = None          # the committed counter summary covers the 128K decode scan only
+        copy_gbps = copy_bandwidth_gbps()
         roof = {"kernel": "index_scan_kernel (Full-layer indexer scan)", "bound": "hbm",
                 "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                "algorithmic_bytes_per_launch": m["scan_algo"], "avg_launch_ms": m["kern_ms"]}
+                "algorithmic_bytes_per_launch": m["scan_algo"], "avg_launch_ms": m["kern_ms"],
+                "copy_gbps_measured": copy_gbps, "frac_of_copy": achieved / copy_gbps}
 
     out = {
         "metric": "CSA2 decode tokens/s/layer + % of HBM roofline at 128K and 1M ctx",
