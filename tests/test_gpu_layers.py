@@ -35,10 +35,19 @@ def numpy_caches(w):
     return P, S, K, pt, n_slots
 
 
-def run_and_compare(w, by_group: bool, check_rows=None):
+def run_and_compare(w, by_group: bool, check_rows=None, equal_keys=False, zero_query=False):
+    """equal_keys: every indexer key the same vector; zero_query: every
+    indexer query zero -- both tie every score of a row (the Top-k and the
+    candidate blocks are then the lowest positions / blocks)."""
     from fp4_kv_cache_02_amd import group
     P, S, K, pt, n_slots = numpy_caches(w)
-    inp = group.build_inputs(w, kv_fp4=P, kv_scale=S)
+    if equal_keys:
+        K[:] = K[0]
+    inp = group.build_inputs(w, kv_fp4=P, kv_scale=S, k_idx=K if equal_keys else None)
+    if zero_query:
+        for L in inp.layers:
+            if L.q_idx is not None:
+                L.q_idx.zero_()
     run = group.GroupRunner(w, inp)
     cache = O.Cache(P, S, K, w.seq_lens, pt, 64, w.slot_stride)
     row_seq = w.row_seq()
@@ -56,6 +65,8 @@ def run_and_compare(w, by_group: bool, check_rows=None):
             m = w.schedule[li]
             k, v, _, st, ln = synth.gen_swa(w, li)
             qi = synth.gen_q_idx(w, li) if m in "FI" else None
+            if qi is not None and zero_query:
+                qi = np.zeros_like(qi)
             q = synth.gen_q(w, li)
             blocks_only = m == "F" and w.hier and w.full_blocks_only
             res = O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln, group.SM_SCALE,
@@ -104,3 +115,13 @@ def test_group_prefill_rows_mode():
     w = synth.Workload("cfg3_reduced_prefill_F5R_C128_E8192", w.seed, [8192], "FRRRRR", prefill_rows=128,
                        prefill_pos=16384, raw_fp4=True)
     run_and_compare(w, by_group=True, check_rows=list(range(0, 128, 9)) + [127])
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("kind", ["equal_keys", "zero_query"])
+def test_group_tied_scores(cfg, kind):
+    """Degenerate indexer inputs: every score of a row tied, so the Top-512
+    (and the candidate blocks) must be the lowest positions; the selections
+    overflow their fast paths and take the general ones."""
+    run_and_compare(synth.workload(cfg, reduced=True), by_group=True, equal_keys=kind == "equal_keys",
+                    zero_query=kind == "zero_query")
