@@ -48,6 +48,27 @@ def test_workspace_sizes_are_monotone(C):
     assert C.csa2_attn_workspace_bytes(16) > C.csa2_attn_workspace_bytes(8)
 
 
+def test_workspace_covers_the_split_and_large_k_paths(C):
+    """The workspace of a Top-k holds the split path's per-segment lists
+    (32 segments x 1024 values x (key, position) per row, for k below 1024 on
+    rows of 2049 .. 131072 values and at most 256 rows) and the large-k path's
+    (16 segments x 8192 per row, k of 1024 and more on rows of 16384 ..
+    131072); shapes outside them need no lists."""
+    lists = 32 * 1024 * 8
+    split_8 = C.csa2_topk_workspace_bytes(8, 131072, 512)
+    split_16 = C.csa2_topk_workspace_bytes(16, 131072, 512)
+    assert split_16 - split_8 >= 8 * lists                    # per-row lists grow with the rows
+    assert C.csa2_topk_workspace_bytes(8, 2048, 512) < 8 * lists   # short rows: one block per row
+    assert C.csa2_topk_workspace_bytes(300, 131072, 512) < 300 * lists      # too many rows: no lists
+    large = C.csa2_topk_workspace_bytes(1, 131072, 2048)
+    assert large >= 16 * 8192 * 8                              # 16 segment lists of 8192
+    assert C.csa2_topk_workspace_bytes(1, 16384, 2048) >= 2 * 8192 * 8
+    # a group's workspace holds its Full layer's lists
+    assert C.csa2_group_workspace_bytes(C.FULL, 4, 8, 131072, 0) >= C.csa2_group_workspace_bytes(C.REUSE, 4, 8,
+                                                                                                 131072, 0) \
+        + 8 * lists
+
+
 def _lib(C):
     return ctypes.CDLL(C.LIB_PATH)
 
