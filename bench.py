@@ -31,10 +31,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=1,
-                   help="workload id (1: 128K decode group; 2: 1M decode group; 3: prefill chunk; 4: mixed serving; "
-                        "5: the 38 CSA2 layers of one decode step, encoder at ratio 2 + decoder, batch 8 at 128K; "
-                        "6: the prefill chunk of 3 with its own compressed entries under the completion mask)")
+    p.add_argument("--workload", default="decode_128k",
+                   choices=["decode_128k", "decode_1m", "prefill", "serving", "model38", "causal_prefill"],
+                   help="decode_128k: Full + 3 Reuse, batch 8 at 131072; decode_1m: hierarchical group at 1048576; "
+                        "prefill: 4096-row chunk over 131072 entries; serving: 20 decoder layers, batch 32, paged; "
+                        "model38: the 38 CSA2 layers of one decode step, encoder at ratio 2 + decoder, batch 8 at "
+                        "128K; causal_prefill: the prefill chunk with its own compressed entries under the "
+                        "completion mask")
     p.add_argument("--replicas", type=int, default=3,
                    help="input replicas cycled per step so the 256 MB last-level cache cannot serve them")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -351,7 +354,7 @@ def main():
 
     from fp4_kv_cache_02_amd import synth
 
-    if args.config == 5:
+    if args.workload == "model38":
         ws = synth.model_step()
         m5 = measure_model(ws, args.steps, args.warmup, args.replicas)
         out = {
@@ -369,7 +372,7 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
-    w = synth.workload(args.config)
+    w = synth.workload(args.workload)
     m = measure(w, args.steps, args.warmup, args.replicas if not w.prefill_rows else 1)
     if w.prefill_rows:
         # indexer 512 flop per (row, entry); attention 20.97 MFLOP per row-layer
@@ -382,7 +385,7 @@ def main():
     else:
         achieved = m["scan_algo"] / (m["kern_ms"] * 1e-3) / 1e9
         traffic = traffic_from_profiles(os.path.join(ROOT, "fp4_kv_cache_02_amd", "csrc", "index_score.hip"))
-        if w.name != "cfg1_F3R_b8_L131072":
+        if args.workload != "decode_128k":
             traffic = None          # the committed counter summary covers the 128K decode scan only
         copy_gbps = copy_bandwidth_gbps()
         roof = {"kernel": "index_scan_kernel (Full-layer indexer scan)", "bound": "hbm",
@@ -412,17 +415,17 @@ def main():
         "roofline": roof,
         "setup_s": m["setup_s"],
     }
-    if args.config == 1 and not args.no_1m:
+    if args.workload == "decode_128k" and not args.no_1m:
         # the metric's second context: the 1M decode group (hierarchical Full
         # layer building 2048 candidate blocks, then Reindex + 3 Reuse)
-        w2 = synth.workload(2)
+        w2 = synth.workload("decode_1m")
         m2 = measure(w2, args.steps, args.warmup, args.replicas)
         a2 = m2["scan_algo"] / (m2["kern_ms"] * 1e-3) / 1e9
         out["context_1m"] = {"workload": w2.name, "value": m2["value"], "unit": "tokens/s/layer",
                              "ms_per_step": m2["ms"], "step_gbps": m2["algo"] / (m2["ms"] * 1e-3) / 1e9,
                              "scan_avg_launch_ms": m2["kern_ms"], "scan_achieved_gbps": a2,
                              "scan_frac": a2 / HBM_PEAK_GBPS, "replicas": m2["replicas"]}
-    if args.config == 1 and not args.no_fp8:
+    if args.workload == "decode_128k" and not args.no_fp8:
         # the same 128K group with the indexer keys in the FP8 form (68 B per
         # position: 64 E4M3 codes and a float32 scale)
         m8 = measure(w, args.steps, args.warmup, args.replicas, fp8=True)
@@ -432,7 +435,7 @@ def main():
                                    "scan_algorithmic_bytes_per_launch": m8["scan_algo"],
                                    "scan_achieved_gbps": a8, "scan_frac": a8 / HBM_PEAK_GBPS,
                                    "replicas": m8["replicas"]}
-    if args.config == 1 and not args.no_model:
+    if args.workload == "decode_128k" and not args.no_model:
         # the whole decode step's CSA2 layers: encoder (18, ratio 2) + decoder (20)
         ws = synth.model_step()
         m5 = measure_model(ws, args.steps, args.warmup, args.replicas)

@@ -10,7 +10,7 @@ indexer, Top-512 selection, a 128-token sliding window, hierarchical
 candidates of 2048 blocks of 8 positions, pages of 64 positions.
 
 Random streams: ``np.random.SeedSequence(seed, spawn_key=(tensor, seq, layer))``
-with ``seed = 1000 + workload id`` -- one independent stream per
+with a fixed seed per workload kind -- one independent stream per
 (tensor, sequence, layer), so any slice can be regenerated on its own.
 """
 from __future__ import annotations
@@ -105,48 +105,51 @@ def _loguniform_lengths(seed: int, B: int, lo: int, hi: int) -> List[int]:
     return [int(round(math.exp(v))) for v in u]
 
 
-def workload(cfg: int, reduced: bool = False) -> Workload:
-    """The five workloads. ``reduced`` keeps the structure at test-friendly sizes."""
-    seed = 1000 + cfg
-    if cfg == 0:
-        return Workload("cfg0_full_b1_L4096", seed, [4096], "F")
-    if cfg == 1:
+WORKLOADS = ("full_4k", "decode_128k", "decode_1m", "prefill", "causal_prefill", "serving")
+
+
+def workload(kind: str, reduced: bool = False) -> Workload:
+    """The seeded workloads, by kind (one of ``WORKLOADS``).  ``reduced`` keeps
+    the structure at test-friendly sizes."""
+    if kind == "full_4k":
+        return Workload("full_b1_L4096", 1000, [4096], "F")
+    if kind == "decode_128k":
         if reduced:
-            return Workload("cfg1_reduced_F3R_b3_L12000", seed, [12000, 9001, 4096], "FRRR",
+            return Workload("decode_reduced_F3R_b3_L12000", 1001, [12000, 9001, 4096], "FRRR",
                             planted=0.01)
-        return Workload("cfg1_F3R_b8_L131072", seed, [131072] * 8, "FRRR", planted=0.01,
+        return Workload("decode_F3R_b8_L131072", 1001, [131072] * 8, "FRRR", planted=0.01,
                         kv_pool=65536)
-    if cfg == 2:
+    if kind == "decode_1m":
         if reduced:
-            return Workload("cfg2_reduced_hierIRRR_b1_L40000", seed, [40000], "FIRRR", hier=True,
+            return Workload("decode_reduced_hier_FIRRR_b1_L40000", 1002, [40000], "FIRRR", hier=True,
                             full_blocks_only=True)
-        return Workload("cfg2_hierIRRR_b1_L1048576", seed, [1048576], "FIRRR", hier=True,
+        return Workload("decode_hier_FIRRR_b1_L1048576", 1002, [1048576], "FIRRR", hier=True,
                         full_blocks_only=True, kv_pool=65536)
-    if cfg == 3:
+    if kind == "prefill":
         if reduced:
-            return Workload("cfg3_reduced_prefill_F5R_C64_E8192", seed, [8192], "FRRRRR",
+            return Workload("prefill_reduced_F5R_C64_E8192", 1003, [8192], "FRRRRR",
                             prefill_rows=64, prefill_pos=16384, raw_fp4=True)
-        return Workload("cfg3_prefill_F5R_C4096_E131072", seed, [131072], "FRRRRR",
+        return Workload("prefill_F5R_C4096_E131072", 1003, [131072], "FRRRRR",
                         prefill_rows=4096, prefill_pos=262144, raw_fp4=True)
-    if cfg == 6:
-        # config 3 with the chunk's own compressed entries (ratio 2: entry j
-        # of the chunk covers its tokens 2j, 2j+1): row i sees the 131072
-        # prior entries and the chunk entries completed by its token,
+    if kind == "causal_prefill":
+        # the prefill chunk with its own compressed entries (ratio 2: entry j
+        # of the chunk covers its tokens 2j, 2j+1): row i sees the E prior
+        # entries and the chunk entries completed by its token,
         # j < floor((i + 1) / 2) -- a completion mask over one shared cache
         C, E = (64, 8192) if reduced else (4096, 131072)
         lens = [E + (i + 1) // 2 for i in range(C)]
-        name = f"cfg3c_causal_prefill_F5R_C{C}_E{E}+{C // 2}" + ("_reduced" if reduced else "")
-        return Workload(name, 1006 + 100, lens, "FRRRRR", prefill_rows=C, prefill_pos=2 * E, raw_fp4=True,
+        name = f"causal_prefill_F5R_C{C}_E{E}+{C // 2}" + ("_reduced" if reduced else "")
+        return Workload(name, 1106, lens, "FRRRRR", prefill_rows=C, prefill_pos=2 * E, raw_fp4=True,
                         shared_slots=True)
-    if cfg == 4:
+    if kind == "serving":
         if reduced:
-            lens = _loguniform_lengths(seed, 5, 2048, 40000)
-            return Workload("cfg4_reduced_20L_b5_paged", seed, lens, "FRRR" + "IRRR" * 4,
+            lens = _loguniform_lengths(1004, 5, 2048, 40000)
+            return Workload("serving_reduced_20L_b5_paged", 1004, lens, "FRRR" + "IRRR" * 4,
                             hier=True, paged=True)
-        lens = _loguniform_lengths(seed, 32, 32768, 1048576)
-        return Workload("cfg4_20L_b32_loguniform_paged", seed, lens, "FRRR" + "IRRR" * 4,
+        lens = _loguniform_lengths(1004, 32, 32768, 1048576)
+        return Workload("serving_20L_b32_loguniform_paged", 1004, lens, "FRRR" + "IRRR" * 4,
                         hier=True, paged=True, kv_pool=65536)
-    raise ValueError(cfg)
+    raise ValueError(f"unknown workload kind {kind!r}; expected one of {WORKLOADS}")
 
 
 def model_step(reduced: bool = False) -> List[Workload]:

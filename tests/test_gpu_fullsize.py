@@ -78,34 +78,34 @@ def run_fullsize(w, rows):
                 assert lse_ok(gl[r], res[r][1]), (w.name, li, r)
 
 
-def test_fullsize_cfg1_decode_128k():
-    w = synth.workload(1)
+def test_fullsize_decode_128k():
+    w = synth.workload("decode_128k")
     run_fullsize(w, list(range(w.R)))
 
 
-def test_fullsize_cfg2_decode_1m():
-    w = synth.workload(2)
+def test_fullsize_decode_1m():
+    w = synth.workload("decode_1m")
     run_fullsize(w, [0])
 
 
-def test_fullsize_cfg3_prefill():
-    w = synth.workload(3)
+def test_fullsize_prefill():
+    w = synth.workload("prefill")
     rng = np.random.default_rng(7)
     rows = sorted(set([0, 1, 127, 2048, w.R - 1] + list(rng.choice(w.R, size=5, replace=False))))
     run_fullsize(w, rows)
 
 
-def test_fullsize_cfg4_mixed_serving():
-    w = synth.workload(4)
+def test_fullsize_mixed_serving():
+    w = synth.workload("serving")
     lens = np.array(w.seq_lens)
     rows = sorted(set([int(lens.argmax()), int(lens.argmin()), 5, 17]))
     run_fullsize(w, rows)
 
 
-def test_fullsize_cfg6_causal_prefill():
+def test_fullsize_causal_prefill():
     """Config 3 with the chunk's own 2048 entries under the completion mask
     (matrix-core indexer with per-row lengths)."""
-    w = synth.workload(6)
+    w = synth.workload("causal_prefill")
     rng = np.random.default_rng(8)
     rows = sorted(set([0, 1, 2, 127, 2048, w.R - 2, w.R - 1] + list(rng.choice(w.R, size=5, replace=False))))
     run_fullsize(w, rows)

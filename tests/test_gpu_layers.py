@@ -86,42 +86,42 @@ def run_and_compare(w, by_group: bool, check_rows=None, equal_keys=False, zero_q
                 assert lse_ok(gl[r], res[r][1]), (w.name, li, r)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
-def test_group_reduced_by_layer(cfg):
-    run_and_compare(synth.workload(cfg, reduced=True), by_group=False)
+@pytest.mark.parametrize("kind", ["full_4k", "decode_128k", "decode_1m", "serving"])
+def test_group_reduced_by_layer(kind):
+    run_and_compare(synth.workload(kind, reduced=True), by_group=False)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
-def test_group_reduced_by_group(cfg):
-    run_and_compare(synth.workload(cfg, reduced=True), by_group=True)
+@pytest.mark.parametrize("kind", ["full_4k", "decode_128k", "decode_1m", "serving"])
+def test_group_reduced_by_group(kind):
+    run_and_compare(synth.workload(kind, reduced=True), by_group=True)
 
 
 def test_group_prefill_reduced():
-    run_and_compare(synth.workload(3, reduced=True), by_group=True)
+    run_and_compare(synth.workload("prefill", reduced=True), by_group=True)
 
 
 def test_group_causal_prefill_reduced():
     """A prefill chunk whose rows also see the chunk's own compressed entries
     once complete (each row a sequence of its own over shared slots, one
     shared window buffer)."""
-    run_and_compare(synth.workload(6, reduced=True), by_group=True)
-    run_and_compare(synth.workload(6, reduced=True), by_group=False, check_rows=[0, 1, 2, 31, 62, 63])
+    run_and_compare(synth.workload("causal_prefill", reduced=True), by_group=True)
+    run_and_compare(synth.workload("causal_prefill", reduced=True), by_group=False, check_rows=[0, 1, 2, 31, 62, 63])
 
 
 def test_group_prefill_rows_mode():
     """Enough rows x layers (128 x 6) that every (layer, row) is one block
     writing its output directly (no partials)."""
-    w = synth.workload(3, reduced=True)
-    w = synth.Workload("cfg3_reduced_prefill_F5R_C128_E8192", w.seed, [8192], "FRRRRR", prefill_rows=128,
+    w = synth.workload("prefill", reduced=True)
+    w = synth.Workload("prefill_reduced_F5R_C128_E8192", w.seed, [8192], "FRRRRR", prefill_rows=128,
                        prefill_pos=16384, raw_fp4=True)
     run_and_compare(w, by_group=True, check_rows=list(range(0, 128, 9)) + [127])
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("wl", ["decode_128k", "decode_1m"])
 @pytest.mark.parametrize("kind", ["equal_keys", "zero_query"])
-def test_group_tied_scores(cfg, kind):
+def test_group_tied_scores(wl, kind):
     """Degenerate indexer inputs: every score of a row tied, so the Top-512
     (and the candidate blocks) must be the lowest positions; the selections
     overflow their fast paths and take the general ones."""
-    run_and_compare(synth.workload(cfg, reduced=True), by_group=True, equal_keys=kind == "equal_keys",
+    run_and_compare(synth.workload(wl, reduced=True), by_group=True, equal_keys=kind == "equal_keys",
                     zero_query=kind == "zero_query")
