@@ -125,3 +125,17 @@ def test_group_tied_scores(wl, kind):
     overflow their fast paths and take the general ones."""
     run_and_compare(synth.workload(wl, reduced=True), by_group=True, equal_keys=kind == "equal_keys",
                     zero_query=kind == "zero_query")
+
+
+@pytest.mark.parametrize("sched,hier,blocks_only", [("FRRR", False, False), ("FIRRR", True, True),
+                                                    ("FRRRIRRR", True, False)])
+@pytest.mark.parametrize("by_group", [True, False])
+def test_group_ragged_short_rows(sched, hier, blocks_only, by_group):
+    """A batch of rows around the kernels' boundaries: an empty sequence (no
+    Top-k entry, no window: lse -inf), rows shorter than one 8-position block,
+    than one 64-position step and than the Top-512, and rows just past each;
+    every Top-k keeps min(L, 512) positions, the candidate set min(ceil(L/8),
+    2048) blocks."""
+    w = synth.Workload(f"ragged_{sched}", 1201, [0, 1, 7, 63, 64, 65, 511, 512, 513, 2047, 5000], sched,
+                       hier=hier, full_blocks_only=blocks_only)
+    run_and_compare(w, by_group=by_group)
