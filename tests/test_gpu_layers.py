@@ -139,3 +139,17 @@ def test_group_ragged_short_rows(sched, hier, blocks_only, by_group):
     w = synth.Workload(f"ragged_{sched}", 1201, [0, 1, 7, 63, 64, 65, 511, 512, 513, 2047, 5000], sched,
                        hier=hier, full_blocks_only=blocks_only)
     run_and_compare(w, by_group=by_group)
+
+
+@pytest.mark.parametrize("R", [160, 300])
+def test_group_many_decode_rows(R):
+    """Decode batches past the split layouts: 160 rows x 4 layers = 640
+    row-layers (one attention block per row-layer, per-sequence windows;
+    split Top-512 over up to 256 rows) and 300 rows (one Top-k block per
+    row); lengths uniform in [0, 5000], one empty sequence, raw FP4 bytes
+    as the main KV, sampled rows checked."""
+    r = np.random.default_rng(1300 + R)
+    lens = [int(x) for x in r.integers(0, 5001, size=R)]
+    lens[0], lens[1] = 0, 5000
+    w = synth.Workload(f"decode_many_rows_b{R}", 1300 + R, lens, "FRRR", planted=0.01, raw_fp4=True)
+    run_and_compare(w, by_group=True, check_rows=[0, 1, 2, 57, 101, 159, R - 1])
