@@ -46,6 +46,9 @@ def parse():
                    help="skip the 38-layer decode step (reported beside the default)")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the 128K group on FP8 indexer keys (reported beside the default)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="report the default workload alone (no 1M, 4K, prefill, serving, FP8-key or 38-layer "
+                        "sub-objects)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (for counter scaling)")
@@ -94,90 +97,180 @@ def traffic_from_profiles(kernel_src):
         return None
 
 
-def cpu_baseline(w, min_seconds, threads=1):
-    """The oracle, untuned, on the same workload: every row through every layer
-    of the group (scan + Top-512 + attention per layer), repeated until at
-    least `min_seconds` of CPU time has been spent; one host thread.  Input
-    generation (and the oracle's quantisation of the main-KV pool) is set-up
-    and not timed."""
+def _oracle_inputs(w):
+    """The workload's inputs as the oracle takes them (numpy, host): the FP4
+    main KV and indexer keys at their slots, and every layer's own inputs.
+    Set-up, not timed."""
     import numpy as np
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
     from fp4_kv_cache_02_amd import synth
     from oracle import csa2_oracle as O
 
-    rows = list(range(w.R if not w.prefill_rows else 4))   # prefill: a sample of 4 chunk rows
     n_slots, pt, _ = synth.slots_layout(w)
     K = np.zeros((n_slots, 64), np.uint16)
     q_full = synth.gen_q_idx(w, 0) if w.planted > 0 else None
     P = np.zeros((n_slots, 256), np.uint8)
     S = np.zeros((n_slots, 32), np.uint8)
-    if w.kv_pool:
+    if w.raw_fp4:
+        P, S = synth.gen_fp4_raw(w, n_slots)
+    elif w.kv_pool:
         pool_p, pool_s = O.quantize_fp4(synth.gen_kv_pool(w))
-    for b in range(w.B):
+    if w.shared_slots:
+        K[:w.n_max] = synth.gen_k_idx_seq(w, 0, q_full, L=w.n_max)
+    for b in range(0 if w.shared_slots else w.B):
         L = w.seq_lens[b]
         sl = synth.slot_index(w, pt, b, np.arange(L))
         K[sl] = synth.gen_k_idx_seq(w, b, q_full)
+        if w.raw_fp4:
+            continue
         if w.kv_pool:
             m = synth.gen_kv_pool_map(w, b)
             P[sl], S[sl] = pool_p[m], pool_s[m]
         else:
             P[sl], S[sl] = O.quantize_fp4(synth.gen_kv_values(w, b, 0, L))
-    cache = O.Cache(P, S, K, w.seq_lens, pt, 64, w.slot_stride)
-    layer_in = []
+    arrays = {"P": P, "S": S, "K": K}
+    if pt is not None:
+        arrays["pt"] = pt
     for li, m in enumerate(w.schedule):
         k, v, _, st, ln = synth.gen_swa(w, li)
-        layer_in.append((synth.gen_q_idx(w, li) if m in "FI" else None, synth.gen_q(w, li), k, v, st, ln))
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    row_seq = list(w.row_seq())
+        arrays.update({f"q{li}": synth.gen_q(w, li), f"k{li}": k, f"v{li}": v, f"st{li}": st, f"ln{li}": ln})
+        if m in "FI":
+            arrays[f"qi{li}"] = synth.gen_q_idx(w, li)
+    return arrays
 
-    def run_rows(rs):
+
+class _OracleGroup:
+    """Runs the oracle's layer steps of workload w for chosen rows."""
+
+    def __init__(self, w, arrays):
+        from oracle import csa2_oracle as O
+        self.w = w
+        self.a = arrays
+        self.cache = O.Cache(arrays["P"], arrays["S"], arrays["K"], w.seq_lens, arrays.get("pt"), 64,
+                             w.slot_stride)
+        self.row_seq = list(w.row_seq())
+
+    def run_rows(self, rs):
         """The group's layers over rows rs (their own Top-k state); returns
         the number of row-layers attended."""
+        from fp4_kv_cache_02_amd import synth
+        from oracle import csa2_oracle as O
+        w, a = self.w, self.a
         state = O.GroupState(w.R)
         n = 0
         for li, m in enumerate(w.schedule):
-            qi, q, k, v, st, ln = layer_in[li]
             blocks_only = m == "F" and w.hier and w.full_blocks_only
-            O.layer_step(synth.MODES[m], cache, state, row_seq, qi, q, k, v, st, ln,
-                         1.0 / math.sqrt(512), hier=w.hier, blocks_only=blocks_only, rows=rs,
-                         swa_shared=w.shared_slots)
+            O.layer_step(synth.MODES[m], self.cache, state, self.row_seq, a.get(f"qi{li}"), a[f"q{li}"],
+                         a[f"k{li}"], a[f"v{li}"], a[f"st{li}"], a[f"ln{li}"], 1.0 / math.sqrt(512), hier=w.hier,
+                         blocks_only=blocks_only, rows=rs, swa_shared=w.shared_slots)
             n += 0 if blocks_only else len(rs)
         return n
 
-    # threads > 1: the rows dealt round-robin to host threads (numpy releases
-    # the interpreter lock inside its array operations)
-    parts = [rows[i::threads] for i in range(threads)] if threads > 1 else [rows]
-    parts = [p for p in parts if p]
-    pool = None
-    if len(parts) > 1:
-        from concurrent.futures import ThreadPoolExecutor
-        pool = ThreadPoolExecutor(max_workers=len(parts))
-    t0 = time.perf_counter()
-    attended = 0
-    reps = 0
-    while True:
-        if pool is None:
-            attended += run_rows(parts[0])
-        else:
-            attended += sum(pool.map(run_rows, parts))
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    if pool is not None:
-        pool.shutdown()
-    if ctx is not None:
-        ctx.restore_original_limits()
-    n_thr = len(parts)
-    return {"value": attended / dt, "unit": "tokens/s/layer", "cores": n_thr, "kind": "oracle",
-            "sample": f"{'the whole workload' if len(rows) == w.R else f'{len(rows)} of the {w.R} rows of the workload'} "
-                      f"({len(rows)} rows x {len(w.schedule)} layers) run {reps} times, "
-                      f"{attended} row-layers in {dt:.1f} s on {n_thr} host thread{'s' if n_thr > 1 else ''} "
-                      f"(numpy elementwise float32 scores, float64 attention"
-                      f"{'; rows dealt round-robin to the threads' if n_thr > 1 else ''}); input generation not timed"}
+
+_WORKER = {}
+
+
+def _oracle_worker_init(kind, folder, names):
+    """Process-pool worker set-up: one numpy thread, the inputs memory-mapped
+    from the files the parent wrote."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        _WORKER["limits"] = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        pass
+    from fp4_kv_cache_02_amd import synth
+    w = synth.workload(kind)
+    arrays = {n: np.load(os.path.join(folder, n + ".npy"), mmap_mode="r") for n in names}
+    _WORKER["group"] = _OracleGroup(w, arrays)
+
+
+def _oracle_worker_rows(rs):
+    return _WORKER["group"].run_rows(rs)
+
+
+def cpu_baseline(w, kind, min_seconds, procs=1, arrays=None):
+    """The oracle, untuned, on the same workload: rows through every layer of
+    the group (scan + Top-512 + attention per layer, each row with its own
+    Top-k state), repeated until at least `min_seconds` have passed.  procs =
+    1: in this process, one numpy thread.  procs > 1: a pool of that many
+    processes (spawned, one numpy thread each, the inputs memory-mapped from
+    files the parent writes), one row per task, kept busy until the time is
+    up.  Input generation (and the oracle's quantisation of the main KV) is
+    set-up and not timed."""
+    import numpy as np
+    rows = list(range(w.R if not w.prefill_rows else 4))   # prefill: a sample of 4 chunk rows
+    if arrays is None:
+        arrays = _oracle_inputs(w)
+    if procs <= 1:
+        try:
+            from threadpoolctl import threadpool_limits
+            ctx = threadpool_limits(limits=1)
+        except Exception:  # pragma: no cover
+            ctx = None
+        grp = _OracleGroup(w, arrays)
+        t0 = time.perf_counter()
+        attended = reps = 0
+        while True:
+            attended += grp.run_rows(rows)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+        if ctx is not None:
+            ctx.restore_original_limits()
+        how = "in one process, one numpy thread"
+    else:
+        import multiprocessing as mp
+        import shutil
+        import tempfile
+        from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
+        base = "/dev/shm" if os.path.isdir("/dev/shm") else None
+        folder = tempfile.mkdtemp(prefix="csa2_oracle_", dir=base)
+        try:
+            for n, arr in arrays.items():
+                np.save(os.path.join(folder, n + ".npy"), np.ascontiguousarray(arr))
+            with ProcessPoolExecutor(max_workers=procs, mp_context=mp.get_context("spawn"),
+                                     initializer=_oracle_worker_init,
+                                     initargs=(kind, folder, sorted(_oracle_names(w)))) as pool:
+                # warm every worker (start-up and memory-mapping are not timed)
+                list(pool.map(_oracle_worker_rows, [[]] * procs))
+                t0 = time.perf_counter()
+                attended = reps = 0
+                nxt = 0
+                pending = set()
+                while len(pending) < procs:
+                    pending.add(pool.submit(_oracle_worker_rows, [rows[nxt % len(rows)]]))
+                    nxt += 1
+                while pending:
+                    done, pending = wait(pending, return_when=FIRST_COMPLETED)
+                    for f in done:
+                        attended += f.result()
+                    if time.perf_counter() - t0 < min_seconds:
+                        for _ in done:
+                            pending.add(pool.submit(_oracle_worker_rows, [rows[nxt % len(rows)]]))
+                            nxt += 1
+                dt = time.perf_counter() - t0
+                reps = nxt / len(rows)
+        finally:
+            shutil.rmtree(folder, ignore_errors=True)
+        how = f"in a pool of {procs} spawned processes (one numpy thread each), one row per task"
+    sample = ("the whole workload" if len(rows) == w.R else f"{len(rows)} of the {w.R} rows of the workload")
+    return {"value": attended / dt, "unit": "tokens/s/layer", "cores": procs, "kind": "oracle",
+            "sample": f"{sample} ({len(rows)} rows x {len(w.schedule)} layers) run {reps:g} times, "
+                      f"{attended} row-layers in {dt:.1f} s {how} (numpy elementwise float32 scores, "
+                      f"float64 attention); input generation not timed",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def _oracle_names(w):
+    names = {"P", "S", "K"}
+    if w.paged:
+        names.add("pt")
+    for li, m in enumerate(w.schedule):
+        names.update({f"q{li}", f"k{li}", f"v{li}", f"st{li}", f"ln{li}"})
+        if m in "FI":
+            names.add(f"qi{li}")
+    return names
 
 
 def data_desc(w):
@@ -205,6 +298,22 @@ def fp8_keys(inp):
     return dataclasses.replace(inp, k_idx=codes, k_scale=scale.contiguous())
 
 
+def replica(base):
+    """A copy of a workload's device inputs in separate memory, so that
+    cycling replicas step by step leaves no input in the 256 MB last-level
+    cache from the step before."""
+    import dataclasses
+    from fp4_kv_cache_02_amd import group
+
+    def cl(t):
+        return None if t is None else t.clone()
+    layers = [group.LayerInputs(q=cl(L.q), swa_k=cl(L.swa_k), swa_v=cl(L.swa_v), swa_start=cl(L.swa_start),
+                                swa_len=cl(L.swa_len), q_idx=cl(L.q_idx)) for L in base.layers]
+    return dataclasses.replace(base, kv_fp4=cl(base.kv_fp4), kv_scale=cl(base.kv_scale), k_idx=cl(base.k_idx),
+                               k_scale=cl(base.k_scale), seq_len=cl(base.seq_len), page_table=cl(base.page_table),
+                               row_seq=cl(base.row_seq), layers=layers)
+
+
 def measure(w, steps, warmup, n_replicas, fp8=False):
     """Times `steps` whole steps of workload w (every group once) and, apart,
     back-to-back launches of its dominant kernel (the Full layer's scan, with
@@ -218,12 +327,10 @@ def measure(w, steps, warmup, n_replicas, fp8=False):
     if fp8:
         base = fp8_keys(base)
     reps = [base]
-    # extra replicas of the per-position caches (the per-layer inputs are small)
+    # extra replicas: every input the step reads (caches, queries, windows)
+    # in memory of its own
     for _ in range(max(0, n_replicas - 1)):
-        reps.append(group.GroupInputs(kv_fp4=base.kv_fp4.clone(), kv_scale=base.kv_scale.clone(),
-                                      k_idx=base.k_idx.clone(), seq_len=base.seq_len, page_table=base.page_table,
-                                      seq_stride=base.seq_stride, row_seq=base.row_seq, layers=base.layers,
-                                      k_scale=None if base.k_scale is None else base.k_scale.clone()))
+        reps.append(replica(base))
     runners = [group.GroupRunner(w, inp) for inp in reps]
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
@@ -283,10 +390,7 @@ def measure_model(ws, steps, warmup, n_replicas):
     for i in range(max(1, n_replicas)):
         row = []
         for w, base in zip(ws, bases):
-            inp = base if i == 0 else group.GroupInputs(
-                kv_fp4=base.kv_fp4.clone(), kv_scale=base.kv_scale.clone(), k_idx=base.k_idx.clone(),
-                seq_len=base.seq_len, page_table=base.page_table, seq_stride=base.seq_stride,
-                row_seq=base.row_seq, layers=base.layers)
+            inp = base if i == 0 else replica(base)
             row.append(group.GroupRunner(w, inp))
         runners.append(row)
     torch.cuda.synchronize()
@@ -311,6 +415,31 @@ def measure_model(ws, steps, warmup, n_replicas):
     rows = ws[0].R
     return {"ms": ms, "value": rows * layers / (ms * 1e-3), "attn_layers": layers, "algo": algo,
             "replicas": len(runners), "setup_s": t_setup}
+
+
+def decode_summary(w, m):
+    """A decode workload's figures for the JSON line: step time, tokens/s/layer,
+    algorithmic bytes and their rate against the HBM peak, and the Full
+    layer's scan timed on its own."""
+    a = m["scan_algo"] / (m["kern_ms"] * 1e-3) / 1e9
+    gbps = m["algo"] / (m["ms"] * 1e-3) / 1e9
+    return {"workload": w.name, "value": m["value"], "unit": "tokens/s/layer", "ms_per_step": m["ms"],
+            "step_algorithmic_bytes": m["algo"], "step_gbps": gbps, "step_frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+            "scan_avg_launch_ms": m["kern_ms"], "scan_achieved_gbps": a, "scan_frac": a / HBM_PEAK_GBPS,
+            "replicas": m["replicas"], "batch": w.B, "context_max": w.n_max, "layers": w.schedule}
+
+
+def prefill_summary(w, m):
+    """A prefill workload's figures: the step's algorithmic flops (indexer
+    512 flop per visible (row, entry), counted once for the group; attention
+    2 x 2 x 16 x 512 x (512 + 128) flop per row-layer) against the dense bf16
+    MFMA peak."""
+    visible = sum(w.seq_lens) if w.shared_slots else w.R * w.n_max
+    flops = visible * 512 + m["attn_layers"] * w.R * 2 * 2 * 16 * 512 * (512 + 128)
+    tflops = flops / (m["ms"] * 1e-3) / 1e12
+    return {"workload": w.name, "value": m["value"], "unit": "tokens/s/layer", "ms_per_step": m["ms"],
+            "flops_per_step": flops, "achieved_tflops": tflops, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS, "rows": w.R, "entries": w.n_max, "layers": w.schedule}
 
 
 def copy_bandwidth_gbps(nbytes=1 << 30, reps=5):
@@ -375,13 +504,10 @@ def main():
     w = synth.workload(args.workload)
     m = measure(w, args.steps, args.warmup, args.replicas if not w.prefill_rows else 1)
     if w.prefill_rows:
-        # indexer 512 flop per (row, entry); attention 20.97 MFLOP per row-layer
-        visible = sum(w.seq_lens) if w.shared_slots else w.R * w.n_max
-        flops = visible * 512 + m["attn_layers"] * w.R * 2 * 2 * 16 * 512 * (512 + 128)
-        tflops = flops / (m["ms"] * 1e-3) / 1e12
+        pf = prefill_summary(w, m)
         roof = {"kernel": "whole prefill group step (MFMA indexer passes, selection, attention)", "bound": "mfma",
-                "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "flops_per_step": flops}
+                "achieved": pf["achieved_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": pf["mfma_frac"], "traffic": None, "flops_per_step": pf["flops_per_step"]}
     else:
         achieved = m["scan_algo"] / (m["kern_ms"] * 1e-3) / 1e9
         traffic = traffic_from_profiles(os.path.join(ROOT, "fp4_kv_cache_02_amd", "csrc", "index_score.hip"))
@@ -415,17 +541,23 @@ def main():
         "roofline": roof,
         "setup_s": m["setup_s"],
     }
-    if args.workload == "decode_128k" and not args.no_1m:
+    default = args.workload == "decode_128k" and not args.no_extras
+    if default and not args.no_1m:
         # the metric's second context: the 1M decode group (hierarchical Full
         # layer building 2048 candidate blocks, then Reindex + 3 Reuse)
         w2 = synth.workload("decode_1m")
-        m2 = measure(w2, args.steps, args.warmup, args.replicas)
-        a2 = m2["scan_algo"] / (m2["kern_ms"] * 1e-3) / 1e9
-        out["context_1m"] = {"workload": w2.name, "value": m2["value"], "unit": "tokens/s/layer",
-                             "ms_per_step": m2["ms"], "step_gbps": m2["algo"] / (m2["ms"] * 1e-3) / 1e9,
-                             "scan_avg_launch_ms": m2["kern_ms"], "scan_achieved_gbps": a2,
-                             "scan_frac": a2 / HBM_PEAK_GBPS, "replicas": m2["replicas"]}
-    if args.workload == "decode_128k" and not args.no_fp8:
+        out["context_1m"] = decode_summary(w2, measure(w2, args.steps, args.warmup, args.replicas))
+    if default:
+        # the other workloads, each timed the same way: one Full layer at 4096
+        # positions, the 4096-row prefill chunk (priced against the MFMA
+        # peak) and the mixed 20-layer serving batch
+        w0 = synth.workload("full_4k")
+        out["full_4k"] = decode_summary(w0, measure(w0, args.steps, args.warmup, args.replicas))
+        w3 = synth.workload("prefill")
+        out["prefill"] = prefill_summary(w3, measure(w3, args.steps, args.warmup, 1))
+        w4 = synth.workload("serving")
+        out["serving"] = decode_summary(w4, measure(w4, args.steps, args.warmup, args.replicas))
+    if default and not args.no_fp8:
         # the same 128K group with the indexer keys in the FP8 form (68 B per
         # position: 64 E4M3 codes and a float32 scale)
         m8 = measure(w, args.steps, args.warmup, args.replicas, fp8=True)
@@ -434,23 +566,26 @@ def main():
                                    "ms_per_step": m8["ms"], "scan_avg_launch_ms": m8["kern_ms"],
                                    "scan_algorithmic_bytes_per_launch": m8["scan_algo"],
                                    "scan_achieved_gbps": a8, "scan_frac": a8 / HBM_PEAK_GBPS,
+                                   "step_frac_of_hbm_peak": m8["algo"] / (m8["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                    "replicas": m8["replicas"]}
-    if args.workload == "decode_128k" and not args.no_model:
+    if default and not args.no_model:
         # the whole decode step's CSA2 layers: encoder (18, ratio 2) + decoder (20)
         ws = synth.model_step()
         m5 = measure_model(ws, args.steps, args.warmup, args.replicas)
         out["model_38_layers"] = {"workload": "+".join(w.name for w in ws), "layers": m5["attn_layers"],
                                   "value": m5["value"], "unit": "tokens/s/layer", "ms_per_step": m5["ms"],
                                   "step_gbps": m5["algo"] / (m5["ms"] * 1e-3) / 1e9,
+                                  "step_frac_of_hbm_peak": m5["algo"] / (m5["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                   "replicas": m5["replicas"]}
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-        # the same oracle with the rows spread over the host's cores (at most
-        # one thread per row; the GPU machine gives a process 16 cores)
-        n_cores = min(len(os.sched_getaffinity(0)), 16, w.R)
+        arrays = _oracle_inputs(w)
+        out["cpu_baseline"] = cpu_baseline(w, args.workload, args.cpu_seconds, arrays=arrays)
+        # the same oracle over every host core this process may use, one
+        # process per core
+        n_cores = len(os.sched_getaffinity(0))
         if n_cores > 1:
-            par = cpu_baseline(w, args.cpu_seconds, threads=n_cores)
-            out["cpu_baseline_all_cores"] = par
+            out["cpu_baseline_all_cores"] = cpu_baseline(w, args.workload, args.cpu_seconds, procs=n_cores,
+                                                         arrays=arrays)
     print(json.dumps(out), flush=True)
 
 

@@ -34,24 +34,36 @@ uint64_t* g_trace[3] = {nullptr, nullptr, nullptr};   // scan, top-k, attention
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Carves a workspace into aligned regions.  A sizing pass runs with a null
+// base; a real carve records an overrun of `end` in `over`, which the entry
+// points check before launching anything that uses the carved regions.
 struct Bump {
   char* base;
   size_t off;
+  size_t end = SIZE_MAX;
+  bool over = false;
   template <class T>
   T* take(size_t n) {
     T* p = base ? (T*)(base + off) : nullptr;
     off = align_up(off + n * sizeof(T));
+    if (off > end) over = true;
     return p;
   }
 };
 
-bool cache_ok(const csa2_cache* c, bool need_scale) {
-  if (!c || !c->data) return false;
-  if (need_scale && !c->scale) return false;
-  if (c->n_slots < 0) return false;
-  if (c->page_table && (c->page_size != CSA2_PAGE || c->max_pages <= 0)) return false;
-  if (!c->page_table && c->seq_stride < 0) return false;
-  return true;
+// Checks a cache descriptor: missing pointers give CSA2_ERR_NULL, negative
+// sizes CSA2_ERR_SHAPE, a page size other than CSA2_PAGE CSA2_ERR_UNSUPPORTED.
+csa2_status cache_status(const csa2_cache* c, bool need_scale) {
+  if (!c || !c->data) return CSA2_ERR_NULL;
+  if (need_scale && !c->scale) return CSA2_ERR_NULL;
+  if (c->n_slots < 0) return CSA2_ERR_SHAPE;
+  if (c->page_table) {
+    if (c->max_pages <= 0) return CSA2_ERR_SHAPE;
+    if (c->page_size != CSA2_PAGE) return CSA2_ERR_UNSUPPORTED;
+  } else if (c->seq_stride < 0) {
+    return CSA2_ERR_SHAPE;
+  }
+  return CSA2_OK;
 }
 
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
@@ -60,7 +72,7 @@ csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_E
 // keys (64 E4M3 codes per slot, 8-byte aligned rows, and a float32 scale per
 // slot, 4-byte aligned).
 csa2_status idx_cache_status(const csa2_cache* c) {
-  if (!cache_ok(c, false)) return CSA2_ERR_NULL;
+  if (const csa2_status cs = cache_status(c, false)) return cs;
   if (c->n_slots < 1 || c->n_slots > 0x7FFFFFFFll) return CSA2_ERR_SHAPE;
   if (c->scale && (((uintptr_t)c->scale & 3u) || ((uintptr_t)c->data & 7u))) return CSA2_ERR_SHAPE;
   if (!c->scale && ((uintptr_t)c->data & 15u)) return CSA2_ERR_SHAPE;
@@ -268,6 +280,15 @@ size_t attn_region(int R, int n_layers, int k) {
   return bp.off;
 }
 
+// The attention's partials depend on k only through its number of 128-key
+// main steps, and not monotonically (fewer steps can take more blocks per
+// row-layer): the largest region over k = 1 .. kmax.
+size_t attn_region_any_k(int R, int n_layers, int kmax) {
+  size_t m = 0;
+  for (int steps = 1; (steps - 1) * 128 < kmax; ++steps) m = std::max(m, attn_region(R, n_layers, std::min(kmax, 128 * steps)));
+  return m;
+}
+
 struct AttnLayerIn {
   const uint16_t *q, *swa_k, *swa_v;
   int32_t S;
@@ -390,6 +411,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       // prefill chunk: matrix-core indexer with exact selection; the rows it
       // lists (too many candidates) take the exact scan and Top-k below
       const PrefWs pw = carve_prefill(bp, R, n_max);
+      if (bp.over) return CSA2_ERR_WORKSPACE;
       PrefArgs p;
       p.q32 = (const uint32_t*)a->q_idx;
       p.head_w = a->head_w;
@@ -443,11 +465,14 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       t.row_list_count = pw.fb_count;
       return run_topk(t, TopkWs{}, st);
     }
+    TopkWs dw, tw;
+    carve_desc(bp, dw, R, n_max, CSA2_TOPK);
+    const int nb = (int)cdiv(n_max, 8);
+    if (mode == CSA2_FULL && sh->hier) carve_large(bp, tw, R, nb, CSA2_KEEP_BLOCKS);
+    if (bp.over) return CSA2_ERR_WORKSPACE;
     s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max, scores,
                        bmax, m64, st);
     if (s) return s;
-    TopkWs dw;
-    carve_desc(bp, dw, R, n_max, CSA2_TOPK);
     if (!blocks_only) {
       TopkArgs t = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
       t.lv[1] = bmax;
@@ -456,9 +481,6 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       if (s) return s;
     }
     if (mode == CSA2_FULL && sh->hier) {
-      const int nb = (int)cdiv(n_max, 8);
-      TopkWs tw;
-      carve_large(bp, tw, R, nb, CSA2_KEEP_BLOCKS);
       TopkArgs t = topk_args(bmax, nb, a->row_seq, sh->seq_len, 8, R, nb, CSA2_KEEP_BLOCKS, sh->cand_blocks);
       t.lv[1] = m64;     // maxima of 8 block maxima
       t.lv_stride[1] = cdiv(n_max, 64);
@@ -473,6 +495,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
   float* cmax = bp.take<float>((size_t)R * CSA2_KEEP_BLOCKS);     // maxima of the candidate blocks
   TopkWs dw;
   carve_desc(bp, dw, R, nc, CSA2_TOPK);
+  if (bp.over) return CSA2_ERR_WORKSPACE;
   s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, sh->cand_blocks, CSA2_KEEP_BLOCKS,
                      R, n_max, scores, cmax, nullptr, st);
   if (s) return s;
@@ -488,7 +511,7 @@ csa2_status check_shared(const csa2_shared* sh, int R) {
   if (R < 1 || R > CSA2_MAX_ROWS || sh->n_max < 0 || sh->B < 1) return CSA2_ERR_SHAPE;
   if (sh->n_max > kMaxTopkN) return CSA2_ERR_UNSUPPORTED;
   if (!sh->seq_len || !sh->topk_idx) return CSA2_ERR_NULL;
-  if (!cache_ok(&sh->kv, true)) return CSA2_ERR_NULL;
+  if (const csa2_status cs = cache_status(&sh->kv, true)) return cs;
   if (sh->kv.n_slots > 0x7FFFFFFFll) return CSA2_ERR_UNSUPPORTED;
   return CSA2_OK;
 }
@@ -533,7 +556,7 @@ size_t csa2_topk_workspace_bytes(int32_t R, int32_t n_max, int32_t k) {
 
 size_t csa2_attn_workspace_bytes(int32_t R) {
   if (R < 0) return 0;
-  return kCtrlBytes + attn_region(R, 1, CSA2_TOPK);
+  return kCtrlBytes + attn_region_any_k(R, 1, CSA2_TOPK);
 }
 
 csa2_status csa2_index_score(const uint16_t* q_idx, const float* head_w, const csa2_cache* k_idx,
@@ -564,8 +587,9 @@ csa2_status csa2_topk(const float* scores, int64_t row_stride, const int32_t* ro
   if (cand_blocks && n_max > 8 * CSA2_KEEP_BLOCKS) return CSA2_ERR_UNSUPPORTED;
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_topk_workspace_bytes(R, n_max, k)) return CSA2_ERR_WORKSPACE;
-  Bump bp{(char*)ws, kCtrlBytes};
+  Bump bp{(char*)ws, kCtrlBytes, ws_bytes};
   const TopkWs tw = carve_topk(bp, R, n_max, k);
+  if (bp.over) return CSA2_ERR_WORKSPACE;
   TopkArgs t = topk_args(scores, row_stride, row_seq, n_valid, 1, R, n_max, k, idx);
   t.cand_blocks = cand_blocks;
   t.cand_stride = n_max / 8;
@@ -581,8 +605,9 @@ csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq,
   const int nb = (int)cdiv(n_max, 8);
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_topk_workspace_bytes(R, nb, keep)) return CSA2_ERR_WORKSPACE;
-  Bump bp{(char*)ws, kCtrlBytes};
+  Bump bp{(char*)ws, kCtrlBytes, ws_bytes};
   const TopkWs tw = carve_topk(bp, R, nb, keep);
+  if (bp.over) return CSA2_ERR_WORKSPACE;
   return run_topk(topk_args(block_max, nb, row_seq, seq_len, 8, R, nb, keep, cand_blocks), tw, stream);
 }
 
@@ -593,13 +618,14 @@ csa2_status csa2_fp4_sparse_attn(const uint16_t* q, const csa2_cache* kv, const 
                                  void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!q || !kv || !seq_len || !idx || !swa_k || !swa_v || !swa_start || !swa_len || !out)
     return CSA2_ERR_NULL;
-  if (!cache_ok(kv, true)) return CSA2_ERR_NULL;
+  if (const csa2_status cs = cache_status(kv, true)) return cs;
   if (R < 1 || R > CSA2_MAX_ROWS || k < 1 || k > CSA2_TOPK || S < 0) return CSA2_ERR_SHAPE;
   if (kv->n_slots > 0x7FFFFFFFll) return CSA2_ERR_UNSUPPORTED;
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_attn_workspace_bytes(R)) return CSA2_ERR_WORKSPACE;
-  Bump bp{(char*)ws, kCtrlBytes};
+  Bump bp{(char*)ws, kCtrlBytes, ws_bytes};
   const AttnWs aw = carve_attn(bp, R, 1, k);
+  if (bp.over) return CSA2_ERR_WORKSPACE;
   const AttnLayerIn L{q, swa_k, swa_v, S, swa_start, swa_len, out, lse, sm_scale, 0};
   return do_attn(&L, 1, kv, row_seq, seq_len, idx, k, R, aw, (char*)ws, stream);
 }
@@ -617,7 +643,11 @@ size_t csa2_group_workspace_bytes(csa2_mode first_mode, int32_t n_layers, int32_
   if (R < 0 || n_max < 0 || n_layers < 1 || n_layers > CSA2_MAX_GROUP_LAYERS) return 0;
   size_t off = kCtrlBytes;
   off = align_up(off + index_region(first_mode, R, n_max, hier));
-  off = align_up(off + attn_region(R, n_layers, CSA2_TOPK));
+  // a hierarchical Full layer that only builds candidates leaves n_layers - 1
+  // attended layers, which can need more partials than n_layers
+  size_t attn = attn_region(R, n_layers, CSA2_TOPK);
+  if (first_mode == CSA2_FULL && hier && n_layers > 1) attn = std::max(attn, attn_region(R, n_layers - 1, CSA2_TOPK));
+  off = align_up(off + attn);
   return off;
 }
 
@@ -649,19 +679,25 @@ csa2_status csa2_group_step(csa2_mode first_mode, int32_t n_layers, const csa2_l
   if (!ws) return CSA2_ERR_WORKSPACE;
   if (ws_bytes < csa2_group_workspace_bytes(first_mode, n_layers, R, sh->n_max, sh->hier)) return CSA2_ERR_WORKSPACE;
 
+  // workspace: the indexer part's region, then the attention's partials;
+  // both carved (and checked against ws_bytes) before anything is launched
   char* w = (char*)ws;
-  Bump bp{w, kCtrlBytes};
-  if (first_mode != CSA2_REUSE) {
-    const size_t mark = bp.off;
-    s = run_index(first_mode, &layers[0], sh, bp, blocks_only, st);
-    if (s) return s;
-    bp.off = align_up(mark + index_region(first_mode, R, sh->n_max, sh->hier));
-  }
+  Bump bp{w, kCtrlBytes, ws_bytes};
+  const size_t index_off = bp.off;
+  if (first_mode != CSA2_REUSE) bp.off = align_up(bp.off + index_region(first_mode, R, sh->n_max, sh->hier));
+  const size_t index_end = bp.off;
+  if (index_end > ws_bytes) return CSA2_ERR_WORKSPACE;
   const int na = n_layers - a0;
+  const AttnWs aw = na > 0 ? carve_attn(bp, R, na, CSA2_TOPK) : AttnWs{nullptr, nullptr, 0, 0};
+  if (bp.over) return CSA2_ERR_WORKSPACE;
+  if (first_mode != CSA2_REUSE) {
+    Bump ib{w, index_off, index_end};
+    s = run_index(first_mode, &layers[0], sh, ib, blocks_only, st);
+    if (s) return s;
+  }
   if (na == 0) return CSA2_OK;
   AttnLayerIn L[CSA2_MAX_GROUP_LAYERS];
   for (int i = 0; i < na; ++i) L[i] = layer_in(&layers[a0 + i]);
-  const AttnWs aw = carve_attn(bp, R, na, CSA2_TOPK);
   return do_attn(L, na, &sh->kv, layers[0].row_seq, sh->seq_len, sh->topk_idx, CSA2_TOPK, R, aw, w, st);
 }
 

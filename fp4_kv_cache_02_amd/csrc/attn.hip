@@ -64,6 +64,7 @@ struct AttnSmem {
   uint32_t scale[kStepKeys * 8];         // their E4M3 scales
   float red_m[kAttnWaves][16];
   float red_l[kAttnWaves][16];
+  float qscale[16];            // main steps: sm_scale * 2^t_h, the query of head h held as q * 2^-t_h
 };
 
 // byte `sel` of `word` (two E2M1 codes, low nibble first) as fp16 at unit scale;
@@ -94,16 +95,6 @@ CSA2_DEV half8_t dequant8(uint32_t word, half2_t sv) {
   return r;
 }
 
-CSA2_DEV uint4 bf16x8_to_f16x8(uint4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const half2_t h = {(_Float16)bf16_lo(w[i]), (_Float16)bf16_hi(w[i])};
-    o[i] = h2u(h);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
 CSA2_DEV bf8_t as_bf8(uint4 v) { return __builtin_bit_cast(bf8_t, v); }
 CSA2_DEV half8_t as_h8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
 CSA2_DEV uint32_t f32_to_bf16_rne(float f) {
@@ -310,11 +301,13 @@ template <bool MAIN>
 CSA2_DEV void step_softmax(AttnSmem& sm, RowState& st, float (&s)[8], uint64_t vmask, float sm_scale, int w, int c,
                            int g) {
     float cmax = -__builtin_inff();
+    // main steps: the logits of head c carry the power of two its fp16 query was scaled by
+    const float f = MAIN ? sm.qscale[c] : sm_scale;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
       const bool ok = (vmask >> key) & 1ull;
-      s[e] = ok ? s[e] * sm_scale : -__builtin_inff();
+      s[e] = ok ? s[e] * f : -__builtin_inff();
       cmax = fmaxf(cmax, s[e]);
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
@@ -389,13 +382,47 @@ CSA2_DEV void step_softmax(AttnSmem& sm, RowState& st, float (&s)[8], uint64_t v
 // The query of the row into LDS from loads issued earlier: fp16 for main
 // steps, bf16 for the window step (per-word selects: a select of whole uint4s
 // becomes a branch per load, each waiting for its load).
-CSA2_DEV void store_q(AttnSmem& sm, const uint4 (&qv)[4], bool to_f16, int tid) {
+//
+// fp16 holds a narrower range than bf16, so for main steps each head's query
+// is first scaled by a power of two 2^-t_h (exact) that puts its largest
+// element in [2^14, 2^15); the logits of that head are multiplied by
+// sm_scale * 2^t_h instead of sm_scale.  Elements more than 2^28 below the
+// head's largest one become fp16 subnormals or zero (a relative change of the
+// head's logits below 2^-28 of sum |q| |k|).  Wave w holds heads w + 4i.
+CSA2_DEV uint32_t bf16_abs_max8(uint4 v) {
+  const uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  const uint32_t b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+  return max(a, b);
+}
+CSA2_DEV uint4 bf16x8_to_f16x8_scaled(uint4 v, float mul) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2_t h = {(_Float16)(bf16_lo(w[i]) * mul), (_Float16)(bf16_hi(w[i]) * mul)};
+    o[i] = h2u(h);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+CSA2_DEV void store_q(AttnSmem& sm, const uint4 (&qv)[4], bool to_f16, int tid, float sm_scale) {
+  if (!to_f16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      sm.q[(e >> 6) * kQRow + (e & 63)] = qv[i];
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid + 256 * i;
-    const uint4 h = bf16x8_to_f16x8(qv[i]);
-    sm.q[(e >> 6) * kQRow + (e & 63)] = make_uint4(to_f16 ? h.x : qv[i].x, to_f16 ? h.y : qv[i].y,
-                                                   to_f16 ? h.z : qv[i].z, to_f16 ? h.w : qv[i].w);
+    // bf16 exponent field of the head's largest |element|; t = exponent - 14,
+    // kept >= -126 so that 2^-t and sm_scale * 2^t stay normal floats
+    const uint32_t ex = wave_max_u32(bf16_abs_max8(qv[i])) >> 7;
+    const int t = max((int)ex - 127 - 14, -126);
+    const float down = __uint_as_float((uint32_t)(127 - t) << 23);
+    sm.q[(e >> 6) * kQRow + (e & 63)] = bf16x8_to_f16x8_scaled(qv[i], down);
+    if ((tid & 63) == 0) sm.qscale[e >> 6] = sm_scale * __uint_as_float((uint32_t)(127 + t) << 23);
   }
 }
 
@@ -492,7 +519,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       if (need_q) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];   // uint4 e: head e / 64, piece e % 64
-        if (!kEarly) store_q(sm, qv, true, tid);
+        if (!kEarly) store_q(sm, qv, true, tid, Ly.sm_scale);
       }
       if (tid < kStepKeys) sm.slot[tid] = (pos >= 0 && pos < L) ? (int32_t)a.map(b, pos) : -1;
       __syncthreads();
@@ -511,7 +538,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
         const int kk = (step + 1) * kStepKeys + tid;
         pos_next = kk < a.k ? idx_row[kk] : -1;
       }
-      if (kEarly && need_q) store_q(sm, qv, true, tid);
+      if (kEarly && need_q) store_q(sm, qv, true, tid, Ly.sm_scale);
       uint4* dst = (uint4*)&sm.code[key * kCodeRow + 32 * half];
 #pragma unroll
       for (int i = 0; i < 8; ++i) dst[i] = mask4(rv[i], rmask);
@@ -530,7 +557,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       uint4 qv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];
-      store_q(sm, qv, false, tid);
+      store_q(sm, qv, false, tid, Ly.sm_scale);
       const int e = 32 * w + (lane & 31);
       const uint64_t vmask = __ballot(e < nwk && koff + e < wl && wst >= 0 && (int64_t)wst + koff + e < Ly.S);
       __syncthreads();    // query visible
@@ -544,7 +571,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       uint4 qv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) qv[i] = qsrc[tid + 256 * i];
-      store_q(sm, qv, false, tid);
+      store_q(sm, qv, false, tid, Ly.sm_scale);
       const int e = 32 * w + (lane & 31);
       const uint64_t vmask = __ballot(e < nwk && koff + e < wl && wst >= 0 && (int64_t)wst + koff + e < Ly.S);
       __syncthreads();    // query visible

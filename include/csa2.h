@@ -92,7 +92,10 @@ typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
  *   page_table == NULL : b * seq_stride + p
  *   page_table != NULL : page_table[b * max_pages + p / page_size] * page_size
  *                        + p % page_size          (page_size must be 64)
- * A slot outside [0, n_slots) is treated as absent.
+ * A slot outside [0, n_slots) is treated as absent.  Every entry point
+ * returns CSA2_ERR_NULL for a missing data (or main-KV scale) pointer,
+ * CSA2_ERR_SHAPE for a negative n_slots, seq_stride or max_pages, and
+ * CSA2_ERR_UNSUPPORTED for a page table with page_size other than 64.
  */
 typedef struct {
   const void* data;
@@ -106,7 +109,16 @@ typedef struct {
 
 /*
  * Indexer scoring (the Full layer's scan, or the Reindex layer's scoring of
- * its candidate positions): for query row r of sequence b = row_seq[r]
+ * its candidate positions).  Defined by: conexaotc.com.br page "DeepSeek lança
+ * V4.1-Flash com contexto de um milhão de tokens...", paragraph on CSA2 (a Full
+ * layer scores the context with its own indexer query against the indexer
+ * keys; a Reindex layer re-scores, with its own indexer query, the candidate
+ * positions of the hierarchical indexer); e-cogni summary of
+ * "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression", section
+ * "Como funciona" (Reindex uses the shared indexer K of the preceding Full
+ * layer).  The pages do not give the head combination; the form below is
+ * the one this library fixes.
+ * For query row r of sequence b = row_seq[r]
  * (row_seq NULL: b = r), with L = seq_len[b] visible positions,
  *   score(p) = sum_h w_h * ReLU(q_idx[r][h] . k_idx(b, p)),  h = 0..3,
  * w = head_w[r] (head_w NULL: all ones), evaluated in float32 in a fixed order:
@@ -137,7 +149,12 @@ csa2_status csa2_index_score(const uint16_t* q_idx /* [R][4][64] */, const float
                              float* block_max, hipStream_t stream);
 
 /*
- * Top-k selection: for row r, among scores[r][0 .. n) with
+ * Top-k selection.  Defined by: conexaotc.com.br page, paragraph on CSA2 (each
+ * Full or Reindex layer keeps the Top-512 positions by indexer score);
+ * 7minutos.es page "DeepSeek AI lanzó DeepSeek-V4.1-Flash...", section
+ * "Atención escasa comprimida 2 (CSA2)".  Ties and output order are not given
+ * there: ties go to the lower index, indices come out ascending.
+ * For row r, among scores[r][0 .. n) with
  * n = n_valid[row_seq ? row_seq[r] : r] (n_valid NULL: n = n_max), entries equal
  * to -inf being absent, keep the first min(k, present) in the order (score
  * descending, index ascending; -0 below +0) and write their indices in
@@ -157,7 +174,12 @@ csa2_status csa2_topk(const float* scores, int64_t row_stride, const int32_t* ro
 size_t csa2_topk_workspace_bytes(int32_t R, int32_t n_max, int32_t k);
 
 /*
- * Hierarchical candidate build: for row r with L = seq_len[row_seq[r]], keep
+ * Hierarchical candidate build.  Defined by: conexaotc.com.br page, paragraph
+ * on CSA2 (in the decoder the Full layer builds a candidate set of up to 2048
+ * blocks of 8 positions, 16384 positions, that the Reindex layers score
+ * instead of the whole context); e-cogni summary, section "Como funciona".
+ * The block score is not given there: it is the largest score in the block.
+ * For row r with L = seq_len[row_seq[r]], keep
  * the `keep` best of the ceil(L/8) block scores block_max[r][..] (order:
  * score descending, block id ascending) and write their block ids ascending
  * to cand_blocks[r][0..keep), padding with -1.  Row stride of block_max is
@@ -171,8 +193,15 @@ csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq,
                                  hipStream_t stream);
 
 /*
- * Sparse FP4 attention with the sliding window, for query row r of sequence
- * b = row_seq[r] (row_seq NULL: b = r), L = seq_len[b]:
+ * Sparse FP4 attention with the sliding window.  Defined by: e-cogni summary
+ * of "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression",
+ * sections "O que os autores propõem" and "Como funciona" (every layer attends
+ * with its own query over the selected main-KV entries and its own 128-token
+ * sliding window); conexaotc.com.br page, paragraph on the KV quantisation
+ * (the main KV is E2M1 with one E4M3 scale per 16 channels and no global
+ * scale).  How the two branches combine is not given there: one softmax over
+ * their union.
+ * For query row r of sequence b = row_seq[r] (row_seq NULL: b = r), L = seq_len[b]:
  *   entries = { main-KV vector of position idx[r][i] : 0 <= idx < L }
  *           U { window entry w : swa_start[r] <= w < swa_start[r] + swa_len[r] }
  *   out[r][h] = sum_e softmax_e(sm_scale * q[r][h] . key_e) * value_e
@@ -183,9 +212,12 @@ csa2_status csa2_hier_candidates(const float* block_max, const int32_t* row_seq,
  * between the two branches).  A row with no entries gets out = 0, lse = -inf.
  * idx entries < 0 or >= L are skipped, and so are window entries outside
  * [0, S).  Requires 1 <= k <= CSA2_TOPK, swa_len <= 128 (longer windows are
- * cut to 128 entries), kv->n_slots < 2^31, queries with |q| < 65504.
- * Accumulation in float32; output float32.
- * Workspace: csa2_attn_workspace_bytes(R).
+ * cut to 128 entries), kv->n_slots < 2^31; any finite bf16 query (the main
+ * keys' products run on fp16 matrix cores with each head's query scaled by a
+ * power of two into fp16's range, elements more than 2^28 below the head's
+ * largest one dropping out).  A paged kv with page_size other than 64 returns
+ * CSA2_ERR_UNSUPPORTED.  Accumulation in float32; output float32.
+ * Workspace: csa2_attn_workspace_bytes(R), enough for every k.
  */
 csa2_status csa2_fp4_sparse_attn(const uint16_t* q /* [R][16][512] */, const csa2_cache* kv,
                                  const int32_t* row_seq, const int32_t* seq_len,
@@ -198,7 +230,11 @@ csa2_status csa2_fp4_sparse_attn(const uint16_t* q /* [R][16][512] */, const csa
 size_t csa2_attn_workspace_bytes(int32_t R);
 
 /*
- * FP4 quantisation of new main-KV vectors (the write side of the cache):
+ * FP4 quantisation of new main-KV vectors (the write side of the cache).
+ * Defined by: conexaotc.com.br page, paragraph on the KV quantisation (E2M1
+ * values with one E4M3 scale per 16 channels, the NVFP4 pattern without its
+ * global scale); 7minutos.es page, section "FP4 KV, repetición limitada y
+ * otras extensiones".  Rounding and saturation are not given there:
  * x[i] (512 float32) -> main-KV slot dst_slot[i] (dst_slot NULL: slot i).
  * Per 16-channel block: amax = max|x|; scale = E4M3 round-to-nearest-even of
  * amax/6 (float32 division), saturating at 448; codes = E2M1
@@ -263,7 +299,10 @@ size_t csa2_group_workspace_bytes(csa2_mode first_mode, int32_t n_layers, int32_
                                   int32_t hier);
 
 /*
- * One CSA2 layer:
+ * One CSA2 layer.  Defined by: conexaotc.com.br page, paragraph on CSA2 (the
+ * static Full / Reindex / Reuse modes); 7minutos.es page, section "Atención
+ * escasa comprimida 2 (CSA2)"; e-cogni summary, section "Como funciona" (each
+ * layer's own query and window).
  *   CSA2_FULL    : scan all L positions -> Top-512 into shared->topk_idx (and,
  *                  if shared->hier, candidate blocks into shared->cand_blocks)
  *                  -> attention.  With blocks_only: candidates only.

@@ -99,7 +99,13 @@ def test_host_validation_errors(C):
     cache.page_size = 32
     cache.max_pages = 4
     assert lib.csa2_index_score(fake, None, ctypes.byref(cache), None, fake, None, 0, 1, 16, fake, None,
-                                None) == 1
+                                None) == 3
+    cache.page_size = 64
+    cache.max_pages = 0
+    assert lib.csa2_index_score(fake, None, ctypes.byref(cache), None, fake, None, 0, 1, 16, fake, None,
+                                None) == 2
+    cache.page_table = None
+    cache.max_pages = 0
     # Top-k: k out of range, missing workspace, too small workspace
     assert C._topk(fake, 16, None, None, 1, 16, 0, None, fake, fake, 1 << 30, None) == 2
     assert C._topk(fake, 16, None, None, 1, 16, 4096, None, fake, fake, 1 << 30, None) == 2
@@ -160,3 +166,79 @@ def test_host_validation_errors(C):
     assert C._quant(fake, 32, None, fake, fake, 16, None) == 2
     assert C._ws_init(fake, 16, None) == 4
     assert C._ws_init(None, 1 << 20, None) == 1
+
+
+# Without a GPU every launch fails with CSA2_ERR_HIP (5); the entry points carve
+# their workspace and check it against ws_bytes before the first launch, so a
+# call that gets as far as status 5 was given enough workspace by the sizing
+# function, while CSA2_ERR_WORKSPACE (4) would mean the sizing fell short.
+ATTN_KS = (1, 100, 127, 128, 129, 200, 255, 256, 257, 300, 383, 384, 385, 450, 511, 512)
+
+
+def _kv_desc(C, paged=False, page_size=64):
+    kv = C.csa2_cache()
+    kv.data, kv.scale, kv.n_slots = 0x1000, 0x1000, 1 << 20
+    if paged:
+        kv.page_table, kv.page_size, kv.max_pages = 0x1000, page_size, 16
+    return kv
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="relies on launches failing without a GPU")
+def test_attention_workspace_covers_every_k(C):
+    """csa2_attn_workspace_bytes(R) suffices for every k of 1..512: the
+    partials depend on k through its number of 128-key steps, and fewer steps
+    can take more blocks per row (e.g. k = 300 at R = 90)."""
+    fake = ctypes.c_void_p(0x1000)
+    kv = _kv_desc(C)
+    for R in range(1, 601):
+        ws = C.csa2_attn_workspace_bytes(R)
+        for k in ATTN_KS:
+            st = C._attn(fake, ctypes.byref(kv), None, fake, fake, k, fake, fake, 128, fake, fake, 0.1, R, fake,
+                         None, fake, ws, None)
+            assert st == 5, (R, k, st)
+    # and a workspace one byte short of a case that needs partials is refused
+    ws = C.csa2_attn_workspace_bytes(90)
+    assert C._attn(fake, ctypes.byref(kv), None, fake, fake, 300, fake, fake, 128, fake, fake, 0.1, 90, fake, None,
+                   fake, 1024, None) == 4
+    assert ws > 1024
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="relies on launches failing without a GPU")
+def test_group_workspace_covers_every_layer_count(C):
+    """csa2_group_workspace_bytes suffices for groups of 1..8 layers at any R,
+    including a hierarchical Full layer that only builds candidates (its
+    group attends n_layers - 1 layers, which can need more partials)."""
+    fake = 0x1000
+    s = C.csa2_shared()
+    s.kv = _kv_desc(C)
+    s.k_idx.data, s.k_idx.n_slots = fake, 1 << 20
+    s.B, s.n_max = 1, 4096
+    s.seq_len = s.topk_idx = s.cand_blocks = fake
+    for hier, blocks_only, mode in ((0, 0, C.REUSE), (1, 1, C.FULL), (1, 0, C.FULL), (0, 0, C.FULL)):
+        s.hier = hier
+        for n in range(1, C.MAX_GROUP_LAYERS + 1):
+            for R in list(range(1, 200)) + list(range(200, 601, 7)):
+                a = C.csa2_layer_args()
+                a.R = R
+                a.q = a.swa_k = a.swa_v = a.swa_start = a.swa_len = a.out = a.q_idx = fake
+                a.blocks_only = blocks_only
+                arr = C.make_layer_array([a] * n)
+                ws = C.csa2_group_workspace_bytes(mode, n, R, s.n_max, bool(hier))
+                st = C._group(mode, n, ctypes.cast(arr, ctypes.c_void_p), ctypes.byref(s), ctypes.c_void_p(fake),
+                              ws, None)
+                assert st == 5, (mode, hier, blocks_only, n, R, st)
+
+
+def test_page_size_other_than_64_is_unsupported(C):
+    fake = ctypes.c_void_p(0x1000)
+    kv = _kv_desc(C, paged=True, page_size=32)
+    assert C._attn(fake, ctypes.byref(kv), None, fake, fake, 512, fake, fake, 128, fake, fake, 0.1, 1, fake, None,
+                   fake, 1 << 30, None) == 3
+    s = C.csa2_shared()
+    s.kv = kv
+    s.B, s.n_max = 1, 16
+    s.seq_len = s.topk_idx = 0x1000
+    a = C.csa2_layer_args()
+    a.R = 1
+    a.q = a.swa_k = a.swa_v = a.swa_start = a.swa_len = a.out = 0x1000
+    assert C._layer(C.REUSE, ctypes.byref(a), ctypes.byref(s), fake, 1 << 30, None) == 3
