@@ -73,6 +73,7 @@ _layer = _sig("csa2_layer_step", _st, [_i32, _P(csa2_layer_args), _P(csa2_shared
 _ws_bytes = _sig("csa2_workspace_bytes", _sz, [_i32, _i32, _i32, _i32])
 _group = _sig("csa2_group_step", _st, [_i32, _i32, ctypes.c_void_p, _P(csa2_shared), c_ptr, _sz, c_ptr])
 _group_ws = _sig("csa2_group_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32])
+_group_noalloc = _sig("csa2_group_step_noalloc", _st, [_i32, _i32, ctypes.c_void_p, _P(csa2_shared), c_ptr])
 _ws_init = _sig("csa2_workspace_init", _st, [c_ptr, _sz, c_ptr])
 _status_string = _sig("csa2_status_string", ctypes.c_char_p, [_st])
 _version = _sig("csa2_version", ctypes.c_char_p, [])
@@ -80,7 +81,8 @@ _version = _sig("csa2_version", ctypes.c_char_p, [])
 EXPORTED = ("csa2_index_score", "csa2_topk", "csa2_topk_workspace_bytes", "csa2_hier_candidates",
             "csa2_fp4_sparse_attn", "csa2_attn_workspace_bytes", "csa2_fp4_quantize", "csa2_layer_step",
             "csa2_workspace_bytes", "csa2_group_step", "csa2_group_workspace_bytes", "csa2_workspace_init",
-            "csa2_status_string", "csa2_version")
+            "csa2_status_string", "csa2_version", "csa2_group_step_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Csa2Error(RuntimeError):
@@ -253,3 +255,10 @@ def csa2_group_step(first_mode: int, layers, shared: csa2_shared, ws, stream=Non
     first_mode, the rest Reuse)."""
     _check(_group(first_mode, len(layers), ctypes.cast(layers, ctypes.c_void_p), ctypes.byref(shared), _p(ws),
                   ws.numel() * ws.element_size(), _stream(stream)), "csa2_group_step")
+
+
+def csa2_group_step_noalloc(first_mode: int, layers, shared: csa2_shared, stream=None):
+    """csa2_group_step on the library's static scratch (no workspace, no
+    allocation); layers as for csa2_group_step."""
+    _check(_group_noalloc(first_mode, len(layers), ctypes.cast(layers, ctypes.c_void_p), ctypes.byref(shared),
+                          _stream(stream)), "csa2_group_step_noalloc")

@@ -10,6 +10,7 @@
 // takes the most recent Top-K.  Every mode attends with the layer's own query
 // and window.
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -516,6 +517,32 @@ csa2_status check_shared(const csa2_shared* sh, int R) {
   return CSA2_OK;
 }
 
+// Scratch of csa2_group_step_noalloc: a static device array (zero when the
+// code object is loaded; each GPU holds its own copy until the process ends).
+// In host code `scratch` names a host-side stand-in: kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = CSA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+csa2_status device_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CSA2_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CSA2_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA2_ERR_HIP;
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -705,6 +732,20 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, const csa2
                             size_t ws_bytes, hipStream_t st) {
   if (!a || !sh) return CSA2_ERR_NULL;
   return csa2_group_step(mode, 1, a, sh, ws, ws_bytes, st);
+}
+
+csa2_status csa2_group_step_noalloc(csa2_mode first_mode, int32_t n_layers, const csa2_layer_args* layers,
+                                    const csa2_shared* sh, hipStream_t st) {
+  if (!layers || !sh) return CSA2_ERR_NULL;
+  if (n_layers < 1 || n_layers > CSA2_MAX_GROUP_LAYERS) return CSA2_ERR_SHAPE;
+  if (layers[0].R < 0 || sh->n_max < 0) return CSA2_ERR_SHAPE;
+  // the static scratch stands in for the caller's workspace: a call needing
+  // more is refused before anything touches the device
+  const size_t need = csa2_group_workspace_bytes(first_mode, n_layers, layers[0].R, sh->n_max, sh->hier);
+  if (need > kScratchBytes) return CSA2_ERR_WORKSPACE;
+  char* ptr = nullptr;
+  if (const csa2_status s = device_scratch(&ptr)) return s;
+  return csa2_group_step(first_mode, n_layers, layers, sh, ptr, kScratchBytes, st);
 }
 
 }  // extern "C"

@@ -299,6 +299,28 @@ size_t csa2_group_workspace_bytes(csa2_mode first_mode, int32_t n_layers, int32_
                                   int32_t hier);
 
 /*
+ * csa2_group_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The library's own scratch stands in for
+ * the workspace: a static device array of CSA2_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends (its device
+ * address is looked up once per device, on the device current at the call;
+ * `stream` must belong to that device).  Results equal csa2_group_step's with
+ * a workspace of its own.  A call whose csa2_group_workspace_bytes exceeds
+ * CSA2_NOALLOC_SCRATCH_BYTES returns CSA2_ERR_WORKSPACE before anything is
+ * enqueued (64 MiB covers, for instance, a Full + 3 Reuse group at batch 32 and
+ * 131072 positions, or the 1M-position hierarchical groups at batch 1; not a
+ * 32-row Full layer at 1M positions, nor a prefill chunk).  Every call on one
+ * GPU uses the same scratch, which keeps the last call's contents (nothing in
+ * it needs clearing: the kernels reset their own counters): calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  This entry point calls no allocator.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (64ull << 20)
+csa2_status csa2_group_step_noalloc(csa2_mode first_mode, int32_t n_layers, const csa2_layer_args* layers,
+                                    const csa2_shared* shared, hipStream_t stream);
+
+/*
  * One CSA2 layer.  Defined by: conexaotc.com.br page, paragraph on CSA2 (the
  * static Full / Reindex / Reuse modes); 7minutos.es page, section "Atención
  * escasa comprimida 2 (CSA2)"; e-cogni summary, section "Como funciona" (each
