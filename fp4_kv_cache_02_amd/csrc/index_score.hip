@@ -274,7 +274,193 @@ void index_scan_kernel(IdxArgs a) {
   }
 }
 
+// ---- FP8 indexer keys: 16-byte loads ----
+//
+// A 68-byte FP8 entry moves half the bytes of a bf16 one, so with the layout
+// above a wave step carries 4 KiB.  Here lane 4g + q (g = 0..15, q = 0..3)
+// loads 16 bytes -- the E4M3 codes of channels 16q .. 16q+15, i.e. chunks 2q
+// and 2q+1 -- of each of the eight positions of group g: a wave step is 128
+// positions and 8 KiB, as for bf16 keys.  The lane runs the two FMA chains of
+// its chunks and adds them (the first level of the canonical tree,
+// c_{2q} + c_{2q+1}); the two levels left are a reduce-scatter over the four
+// lanes of the group (partner q ^ 1, then q ^ 2), after which lane q holds
+// positions q and q + 4 of its group, each scaled, ReLU'd and summed over the
+// heads as in the kernel above.  Candidate mode: group g of step t is
+// candidate block 16 t + g.
+template <bool CAND, bool HAS_W, bool MAXIMA>
+__global__ __launch_bounds__(kScanWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void index_scan_fp8_kernel(IdxArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 2, q = lane & 3;
+  const bool b0 = q & 1, b1 = (q >> 1) & 1;
+  const uint32_t n_items = (uint32_t)a.R * (uint32_t)a.steps_per_row;
+  const uint32_t item = __builtin_amdgcn_readfirstlane(blockIdx.x * kScanWaves + (threadIdx.x >> 6));
+  if (item >= n_items) return;
+  const int r = __builtin_amdgcn_readfirstlane((int)(item / (uint32_t)a.steps_per_row));
+  const int t = __builtin_amdgcn_readfirstlane((int)(item - (uint32_t)r * (uint32_t)a.steps_per_row));
+  const int b = a.row_seq ? a.row_seq[r] : r;
+  const int L = __builtin_amdgcn_readfirstlane(min(a.seq_len[b], a.n_max));
+  if (!CAND && t * 128 >= L) return;      // past the row's visible positions: nothing to write
+  int64_t pos0;
+  int ci = 0;
+  if (CAND) {
+    ci = t * 16 + g;
+    const int blk = ci < a.n_cand ? a.cand[(int64_t)r * a.n_cand + ci] : -1;
+    pos0 = blk >= 0 ? (int64_t)blk * 8 : (int64_t)1 << 40;
+  } else {
+    pos0 = (int64_t)t * 128 + g * 8;
+  }
+  int64_t s0 = 0;
+  int nv = 0;
+  if (pos0 < L) {
+    const int64_t sl = a.map(b, pos0);    // a group of 8 never straddles a page
+    if (sl >= 0) {
+      nv = (int)min(min((int64_t)L - pos0, a.map.n_slots - sl), (int64_t)8);
+      s0 = sl;
+    }
+  }
+  // the eight 16-byte loads at once (slot 0 for absent positions)
+  const u32x4_t* kd = (const u32x4_t*)a.kdata;
+  u32x4_t kr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kr[i] = __builtin_nontemporal_load(kd + ((i < nv) ? s0 + i : 0) * 4 + q);
+  // scales of the two positions this lane finishes: q and q + 4
+  const float sc0 = a.kscale[(q < nv) ? s0 + q : 0];
+  const float sc1 = a.kscale[(q + 4 < nv) ? s0 + q + 4 : 0];
+  // query channels 16q .. 16q+15 of each head
+  float qf[4][16];
+  {
+    const uint4* qp = (const uint4*)(a.q32 + (int64_t)r * 128);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint4 v = qp[h * 8 + 2 * q + u];
+        qf[h][8 * u + 0] = bf16_lo(v.x); qf[h][8 * u + 1] = bf16_hi(v.x);
+        qf[h][8 * u + 2] = bf16_lo(v.y); qf[h][8 * u + 3] = bf16_hi(v.y);
+        qf[h][8 * u + 4] = bf16_lo(v.z); qf[h][8 * u + 5] = bf16_hi(v.z);
+        qf[h][8 * u + 6] = bf16_lo(v.w); qf[h][8 * u + 7] = bf16_hi(v.w);
+      }
+    }
+  }
+  float w[4] = {1.f, 1.f, 1.f, 1.f};
+  if (HAS_W) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w[h] = a.head_w[(int64_t)r * 4 + h];
+  }
+  // level 1 in the lane: (c_{2q} + c_{2q+1}) of the eight positions, four heads
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  float P[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float kf[16];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)kr[i][d], false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)kr[i][d], true);
+      kf[4 * d + 0] = lo[0]; kf[4 * d + 1] = lo[1]; kf[4 * d + 2] = hi[0]; kf[4 * d + 3] = hi[1];
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float c0 = 0.0f, c1 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        c0 = __builtin_fmaf(kf[e], qf[h][e], c0);
+        c1 = __builtin_fmaf(kf[8 + e], qf[h][8 + e], c1);
+      }
+      P[i][h] = c0 + c1;
+    }
+  }
+  // level 2 (partner q ^ 1): lane keeps positions i with (i & 1) == b0
+  float Q[4][4], d[2][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float keep = b0 ? P[2 * m + 1][h] : P[2 * m][h];
+      const float send = b0 ? P[2 * m][h] : P[2 * m + 1][h];
+      Q[m][h] = keep + CSA2_DPP(send, 0xB1);          // quad_perm 1,0,3,2
+    }
+  // level 3 (partner q ^ 2): of positions b0 + 2m (m = 0..3) keep m with (m & 1) == b1
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float keep = b1 ? Q[2 * u + 1][h] : Q[2 * u][h];
+      const float send = b1 ? Q[2 * u][h] : Q[2 * u + 1][h];
+      d[u][h] = keep + CSA2_DPP(send, 0x4E);          // quad_perm 2,3,0,1
+    }
+  // lane q now holds positions b0 + 2 b1 + 4u = q + 4u, u = 0, 1
+  float sc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float scale = u ? sc1 : sc0;
+    float rr[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float dh = d[u][h] * scale;
+      rr[h] = (dh > 0.0f) ? dh : 0.0f;
+    }
+    if (HAS_W) {
+      const float p0 = w[0] * rr[0], p1 = w[1] * rr[1], p2 = w[2] * rr[2], p3 = w[3] * rr[3];
+      sc[u] = (p0 + p1) + (p2 + p3);
+    } else {
+      sc[u] = (rr[0] + rr[1]) + (rr[2] + rr[3]);
+    }
+  }
+  const bool pres0 = q < nv, pres1 = q + 4 < nv;
+  uint32_t k = max(pres0 ? order_key(sc[0]) : 0u, pres1 ? order_key(sc[1]) : 0u);
+  if (CAND) {
+    const int64_t base = (int64_t)r * a.score_stride + (int64_t)ci * 8;
+    if (ci < a.n_cand) {
+      a.scores[base + q] = pres0 ? sc[0] : -__builtin_inff();
+      a.scores[base + q + 4] = pres1 ? sc[1] : -__builtin_inff();
+    }
+    if (MAXIMA) {
+      k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));
+      k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));
+      if (q == 0 && ci < a.n_cand)
+        a.block_max[(int64_t)r * a.bmax_stride + ci] = k ? key_to_float(k) : -__builtin_inff();
+    }
+  } else {
+    float* srow = a.scores + (int64_t)r * a.score_stride;
+    if (pos0 + q < L) srow[pos0 + q] = pres0 ? sc[0] : -__builtin_inff();
+    if (pos0 + q + 4 < L) srow[pos0 + q + 4] = pres1 ? sc[1] : -__builtin_inff();
+    if (MAXIMA) {
+      k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));
+      k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));
+      if (q == 0 && pos0 < L)
+        a.block_max[(int64_t)r * a.bmax_stride + (pos0 >> 3)] = k ? key_to_float(k) : -__builtin_inff();
+      if (a.max64) {
+        // 64-position maxima: lanes 0-31 and 32-63 each cover 64 positions
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x124, 0xF, 0xF, false));   // row_ror:4
+        k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x128, 0xF, 0xF, false));   // row_ror:8
+        k = max(k, (uint32_t)__shfl_xor((int)k, 16, 64));
+        const int64_t p64 = (int64_t)t * 128 + (lane >> 5) * 64;
+        if ((lane & 31) == 0 && p64 < L)
+          a.max64[(int64_t)r * a.max64_stride + (p64 >> 6)] = k ? key_to_float(k) : -__builtin_inff();
+      }
+    }
+  }
+}
+
 hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxima, hipStream_t st) {
+  if (a.kscale && !a.row_list && ((uintptr_t)a.kdata & 15u) == 0) {
+    // FP8 keys in 16-byte loads: 128 positions (16 candidate blocks) per wave step
+    IdxArgs f = a;
+    f.steps_per_row = cand ? (a.n_cand + 15) / 16 : (a.n_max + 127) / 128;
+    const int64_t items = (int64_t)f.R * f.steps_per_row;
+    if (items == 0) return hipSuccess;
+    if (items > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((items + kScanWaves - 1) / kScanWaves)), blk(kScanWaves * 64);
+#define CSA2_FP8_LAUNCH(C, Wt, M) hipLaunchKernelGGL((index_scan_fp8_kernel<C, Wt, M>), grid, blk, 0, st, f)
+    if (cand && maxima) { if (has_w) CSA2_FP8_LAUNCH(true, true, true); else CSA2_FP8_LAUNCH(true, false, true); }
+    else if (cand) { if (has_w) CSA2_FP8_LAUNCH(true, true, false); else CSA2_FP8_LAUNCH(true, false, false); }
+    else if (maxima) { if (has_w) CSA2_FP8_LAUNCH(false, true, true); else CSA2_FP8_LAUNCH(false, false, true); }
+    else { if (has_w) CSA2_FP8_LAUNCH(false, true, false); else CSA2_FP8_LAUNCH(false, false, false); }
+#undef CSA2_FP8_LAUNCH
+    return hipGetLastError();
+  }
   const int64_t items = (int64_t)a.R * a.steps_per_row;
   if (items == 0) return hipSuccess;
   if (items > 0x7FFFFFFFll) return hipErrorInvalidValue;

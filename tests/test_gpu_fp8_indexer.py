@@ -155,3 +155,62 @@ def test_fp8_layers_parity(C, paged):
                 assert np.array_equal(host(cand)[r], state.cand[r]), (li, r)
             assert np.all(rel_err(go[r], res[r][0]) <= ATTN_TOL), (li, r)
             assert lse_ok(gl[r], res[r][1]), (li, r)
+
+
+@pytest.mark.parametrize("n_cand", [1, 7, 100, 2047])
+def test_index_score_fp8_few_candidates(C, n_cand):
+    """Reindex scoring over FP8 keys (raw codes with subnormals and zero
+    scales) for candidate counts that leave the last 16-block step partly
+    empty."""
+    rng = np.random.default_rng(820 + n_cand)
+    lens = [20000, 3000, 100, 9]
+    B = len(lens)
+    n_max = max(lens)
+    seqs = [fp8_keys(rng, L, "raw" if b % 2 else "normal") for b, L in enumerate(lens)]
+    codes, sc = place_fp8(seqs, lens, B * n_max, None, n_max)
+    cand = np.full((B, n_cand), -1, np.int32)
+    for b, L in enumerate(lens):
+        nb = (L + 7) // 8
+        m = min(nb, n_cand)
+        cand[b, :m] = np.sort(rng.choice(nb, size=m, replace=False))
+    q = bf16(rng, (B, 4, 64))
+    say("fp8 index_score n_cand", n_cand)
+    kc = C.make_cache(dev(codes), scale=dev(sc), seq_stride=n_max)
+    scores = torch.full((B, n_cand * 8), float("nan"), device="cuda")
+    C.csa2_index_score(dev(q), kc, dev(np.array(lens, np.int32)), scores, cand_blocks=dev(cand), n_max=n_max)
+    torch.cuda.synchronize()
+    g = host(scores)
+    for b, L in enumerate(lens):
+        pos = (cand[b][:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+        ok = (np.repeat(cand[b], 8) >= 0) & (pos < L)
+        ref = np.full(n_cand * 8, -np.inf, np.float32)
+        ref[ok] = O.index_scores_fp8(q[b], seqs[b][0][pos[ok]], seqs[b][1][pos[ok]])
+        assert np.array_equal(g[b].view(np.uint32), ref.view(np.uint32)), b
+
+
+def test_index_score_fp8_unaligned_codes(C):
+    """FP8 codes whose array starts 8 bytes off a 16-byte boundary (allowed:
+    8-byte alignment) take the 8-byte-load scan; scores and block maxima equal
+    the oracle's as on aligned codes."""
+    rng = np.random.default_rng(830)
+    lens = [5000, 777]
+    B = len(lens)
+    n_max = max(lens) + 3
+    seqs = [fp8_keys(rng, L) for L in lens]
+    codes, sc = place_fp8(seqs, lens, B * n_max, None, n_max)
+    raw = torch.zeros(codes.size + 8, dtype=torch.uint8, device="cuda")
+    view = raw[8:].view(B * n_max, 64)
+    view.copy_(dev(codes))
+    assert view.data_ptr() % 16 == 8
+    q = bf16(rng, (B, 4, 64))
+    say("fp8 index_score unaligned codes")
+    kc = C.make_cache(view, scale=dev(sc), seq_stride=n_max)
+    scores = torch.full((B, n_max), float("nan"), device="cuda")
+    bmax = torch.full((B, (n_max + 7) // 8), float("nan"), device="cuda")
+    C.csa2_index_score(dev(q), kc, dev(np.array(lens, np.int32)), scores, block_max=bmax)
+    torch.cuda.synchronize()
+    g, gb = host(scores), host(bmax)
+    for b, L in enumerate(lens):
+        ref = O.index_scores_fp8(q[b], seqs[b][0], seqs[b][1])
+        assert np.array_equal(g[b, :L].view(np.uint32), ref.view(np.uint32)), b
+        assert np.array_equal(gb[b, :(L + 7) // 8].view(np.uint32), O.block_max(ref, L).view(np.uint32)), b
