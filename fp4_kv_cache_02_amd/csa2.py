@@ -69,6 +69,7 @@ _attn = _sig("csa2_fp4_sparse_attn", _st, [c_ptr, _P(csa2_cache), c_ptr, c_ptr, 
                                            c_ptr, c_ptr, _f32, _i32, c_ptr, c_ptr, c_ptr, _sz, c_ptr])
 _attn_ws = _sig("csa2_attn_workspace_bytes", _sz, [_i32])
 _quant = _sig("csa2_fp4_quantize", _st, [c_ptr, _i64, c_ptr, c_ptr, c_ptr, _i64, c_ptr])
+_fp8q = _sig("csa2_fp8_key_quantize", _st, [c_ptr, _i64, c_ptr, c_ptr, c_ptr, _i64, c_ptr])
 _layer = _sig("csa2_layer_step", _st, [_i32, _P(csa2_layer_args), _P(csa2_shared), c_ptr, _sz, c_ptr])
 _ws_bytes = _sig("csa2_workspace_bytes", _sz, [_i32, _i32, _i32, _i32])
 _group = _sig("csa2_group_step", _st, [_i32, _i32, ctypes.c_void_p, _P(csa2_shared), c_ptr, _sz, c_ptr])
@@ -81,7 +82,8 @@ _version = _sig("csa2_version", ctypes.c_char_p, [])
 EXPORTED = ("csa2_index_score", "csa2_topk", "csa2_topk_workspace_bytes", "csa2_hier_candidates",
             "csa2_fp4_sparse_attn", "csa2_attn_workspace_bytes", "csa2_fp4_quantize", "csa2_layer_step",
             "csa2_workspace_bytes", "csa2_group_step", "csa2_group_workspace_bytes", "csa2_workspace_init",
-            "csa2_status_string", "csa2_version", "csa2_group_step_noalloc")
+            "csa2_status_string", "csa2_version", "csa2_group_step_noalloc",
+            "csa2_fp8_key_quantize")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -186,6 +188,13 @@ def csa2_fp4_quantize(x, fp4, scale, dst_slot=None, stream=None):
     n = int(x.shape[0])
     _check(_quant(_p(x), n, _p(dst_slot), _p(fp4), _p(scale), int(fp4.shape[0]), _stream(stream)),
            "csa2_fp4_quantize")
+
+
+def csa2_fp8_key_quantize(k, codes, scale, dst_slot=None, stream=None):
+    """k: [n, 64] bf16 bits (int16/bf16); codes: [n_slots, 64] uint8; scale: [n_slots] float32."""
+    n = int(k.shape[0])
+    _check(_fp8q(_p(k), n, _p(dst_slot), _p(codes), _p(scale), int(codes.shape[0]), _stream(stream)),
+           "csa2_fp8_key_quantize")
 
 
 def csa2_workspace_bytes(mode: int, R: int, n_max: int, hier: bool) -> int:

@@ -666,6 +666,15 @@ csa2_status csa2_fp4_quantize(const float* x, int64_t n, const int64_t* dst_slot
   return hip_status(launch_quant(x, n, dst_slot, fp4, scale, n_slots, stream));
 }
 
+csa2_status csa2_fp8_key_quantize(const uint16_t* k, int64_t n, const int64_t* dst_slot, uint8_t* codes,
+                                  float* scale, int64_t n_slots, hipStream_t stream) {
+  if (n > 0 && (!k || !codes || !scale)) return CSA2_ERR_NULL;
+  if (n < 0 || n_slots < 0) return CSA2_ERR_SHAPE;
+  if (!dst_slot && n > n_slots) return CSA2_ERR_SHAPE;
+  if (n / 4 >= (int64_t)0x7FFFFFFF) return CSA2_ERR_SHAPE;
+  return hip_status(launch_fp8_key_quant(k, n, dst_slot, codes, scale, n_slots, stream));
+}
+
 size_t csa2_group_workspace_bytes(csa2_mode first_mode, int32_t n_layers, int32_t R, int32_t n_max, int32_t hier) {
   if (R < 0 || n_max < 0 || n_layers < 1 || n_layers > CSA2_MAX_GROUP_LAYERS) return 0;
   size_t off = kCtrlBytes;

@@ -148,6 +148,8 @@ hipError_t launch_maxima(const MaximaArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,
                         int64_t n_slots, hipStream_t st);
+hipError_t launch_fp8_key_quant(const uint16_t* k, int64_t n, const int64_t* dst, uint8_t* codes, float* scale,
+                                int64_t n_slots, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
 hipError_t launch_prefill_index(const PrefArgs& a, bool has_w, hipStream_t st);
 constexpr int kPrefMinRows = 256;        // rows from which the MFMA prefill indexer is used

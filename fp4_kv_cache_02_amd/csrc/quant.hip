@@ -62,6 +62,38 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(const float* __restrict_
   if ((lane & 1) == 0) scale[slot * 32 + (lane >> 1)] = (uint8_t)sc;
 }
 
+// FP8 indexer keys (64 E4M3 codes and a float32 scale per position): one
+// wave per key, lane l owns channel l.  s = amax / 448 (float32 division),
+// code_l = E4M3(|k_l| / s) nearest-even with the sign of k_l; s == 0 gives
+// all codes 0.
+__global__ __launch_bounds__(256) void fp8_key_quant_kernel(const uint16_t* __restrict__ k, int64_t n,
+                                                            const int64_t* __restrict__ dst,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scale, int64_t n_slots) {
+  const int lane = threadIdx.x & 63;
+  const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (v >= n) return;
+  const int64_t slot = dst ? dst[v] : v;
+  const uint32_t bits = (uint32_t)k[v * 64 + lane] << 16;
+  // |k| as float bits orders like |k| (non-negative floats)
+  const float amax = __uint_as_float(wave_max_u32(bits & 0x7FFFFFFFu));
+  const float s = amax / 448.0f;
+  uint32_t code = 0u;
+  if (s != 0.0f) code = e4m3_rne(__uint_as_float(bits & 0x7FFFFFFFu) / s) | ((bits >> 31) << 7);
+  if (slot < 0 || slot >= n_slots) return;
+  codes[slot * 64 + lane] = (uint8_t)code;
+  if (lane == 0) scale[slot] = s;
+}
+
+hipError_t launch_fp8_key_quant(const uint16_t* k, int64_t n, const int64_t* dst, uint8_t* codes, float* scale,
+                                int64_t n_slots, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 3) / 4;
+  hipLaunchKernelGGL(fp8_key_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, k, n, dst, codes, scale,
+                     n_slots);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,
                         int64_t n_slots, hipStream_t st) {
   if (n == 0) return hipSuccess;

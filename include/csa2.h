@@ -247,6 +247,22 @@ csa2_status csa2_fp4_quantize(const float* x, int64_t n, const int64_t* dst_slot
                               uint8_t* scale /* [n_slots][32] */, int64_t n_slots,
                               hipStream_t stream);
 
+/*
+ * FP8 quantisation of new indexer keys (the write side of the FP8 indexer-key
+ * cache).  The pages give only the entry size -- 890 B of global KV cache per
+ * token, which adds up with a 68-B indexer entry beside the 288-B FP4 main-KV
+ * entry (conexaotc.com.br page, opening paragraph; 7minutos.es page, opening
+ * section); the encoding is this library's reading: k[i] (64 bf16 channels)
+ * -> slot dst_slot[i] (dst_slot NULL: slot i) of codes ([n_slots][64] uint8,
+ * OCP E4M3FN) and scale ([n_slots] float32): s = amax / 448 (amax = max |k|,
+ * float32 division), code = E4M3 round-to-nearest-even of |k| / s (float32
+ * division, saturating at 448) with the sign of k; s == 0 gives all codes 0.
+ * The largest element of a key maps to +-448.  Slots outside [0, n_slots) are
+ * skipped.
+ */
+csa2_status csa2_fp8_key_quantize(const uint16_t* k, int64_t n, const int64_t* dst_slot, uint8_t* codes,
+                                  float* scale, int64_t n_slots, hipStream_t stream);
+
 /* State handed from layer to layer within a group (Full -> Reindex/Reuse). */
 typedef struct {
   csa2_cache kv;           /* main KV shared by the group                          */

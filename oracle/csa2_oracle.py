@@ -157,6 +157,27 @@ def quantize_fp4(x) -> Tuple[np.ndarray, np.ndarray]:
     return packed, scale_code.astype(np.uint8)
 
 
+def quantize_fp8_keys(k_bits) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantise bf16 indexer keys [N, 64] to FP8 entries: (codes [N, 64] u8
+    OCP E4M3FN, scale [N] float32) -- the 68-B entry of index_scores_fp8.
+
+    The pages give only the entry size (890 B per token, conexaotc.com.br
+    page, opening paragraph); the reading taken here: one scale per position,
+    s = float32(amax / 448) with amax = max |k| (so the largest element maps
+    to the largest E4M3 value), codes = E4M3(|k| / s) rounded to nearest-even
+    (the division in float32), saturating at 448, with the sign of k; a key
+    whose s is 0 gets s = 0 and all codes 0.
+    """
+    k = bf16_to_f64(k_bits).astype(np.float32)
+    amax = np.max(np.abs(k), axis=1)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1.0), s)
+    y = (np.abs(k) / safe[:, None]).astype(np.float32)
+    codes = e4m3_encode(y) | np.where(np.signbit(k), 0x80, 0).astype(np.uint8)
+    codes = np.where((s == 0)[:, None], np.uint8(0), codes).astype(np.uint8)
+    return codes, s
+
+
 def dequantize_fp4(packed, scale) -> np.ndarray:
     """Decode (packed [N, 256], scale [N, 32]) to float64 [N, 512] exactly."""
     packed = np.asarray(packed, dtype=np.uint8)

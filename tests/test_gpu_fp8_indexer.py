@@ -214,3 +214,35 @@ def test_index_score_fp8_unaligned_codes(C):
         ref = O.index_scores_fp8(q[b], seqs[b][0], seqs[b][1])
         assert np.array_equal(g[b, :L].view(np.uint32), ref.view(np.uint32)), b
         assert np.array_equal(gb[b, :(L + 7) // 8].view(np.uint32), O.block_max(ref, L).view(np.uint32)), b
+
+
+def test_fp8_key_quantize_bitexact(C):
+    """The library's FP8 key quantiser against the oracle's: codes and scales
+    bit-exact (zero and -0 keys, single-element keys, magnitudes 2^-120 ..
+    2^40), contiguous and into scattered slots."""
+    rng = np.random.default_rng(840)
+    N = 5000
+    k = rng.standard_normal((N, 64)).astype(np.float32)
+    k *= np.exp2(rng.uniform(-120, 40, size=(N, 1))).astype(np.float32)
+    k[0] = 0.0
+    k[1] = -0.0
+    k[2, :] = 0.0
+    k[2, 7] = -5.5
+    k[3, ::2] = -0.0
+    from fp4_kv_cache_02_amd import synth
+    kb = synth.f32_to_bf16_bits(k)
+    ref_c, ref_s = O.quantize_fp8_keys(kb)
+    say("fp8 key quantize N", N)
+    codes = torch.zeros((N, 64), dtype=torch.uint8, device="cuda")
+    sc = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    C.csa2_fp8_key_quantize(dev(kb), codes, sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sc).view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(host(codes), ref_c)
+    perm = rng.permutation(N + 77)[:N].astype(np.int64)
+    codes2 = torch.zeros((N + 77, 64), dtype=torch.uint8, device="cuda")
+    sc2 = torch.zeros((N + 77,), dtype=torch.float32, device="cuda")
+    C.csa2_fp8_key_quantize(dev(kb), codes2, sc2, dst_slot=dev(perm))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(codes2)[perm], ref_c)
+    assert np.array_equal(host(sc2)[perm].view(np.uint32), ref_s.view(np.uint32))

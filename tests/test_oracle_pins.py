@@ -517,3 +517,64 @@ def test_fp8_cache_unit_scale_equals_bf16_cache_layers():
     for r in range(B):
         assert np.array_equal(f1[r], f2[r]) and np.array_equal(s1.cand[r], s2.cand[r])
         assert np.array_equal(s1.topk[r], s2.topk[r])
+
+
+def _fp8_key_cases(rng):
+    k = rng.standard_normal((300, 64)).astype(np.float32)
+    k *= np.exp2(rng.uniform(-20, 20, size=(300, 1))).astype(np.float32)
+    k[0] = 0.0                                   # zero key: scale 0, codes 0
+    k[1] = -0.0
+    k[2, :] = 0.0
+    k[2, 5] = -3.0                               # one element: it alone is +-448
+    k[3] = np.float32(2.0) ** -125               # tiny keys
+    return synth.f32_to_bf16_bits(k)
+
+
+def test_fp8_key_quantiser_against_torch_float8_cast():
+    """The FP8 key quantiser's codes equal torch's float8_e4m3fn cast (an
+    independent round-to-nearest-even implementation) of k / s, s = amax / 448
+    in float32."""
+    rng = np.random.default_rng(61)
+    kb = _fp8_key_cases(rng)
+    codes, s = O.quantize_fp8_keys(kb)
+    k = synth.bf16_bits_to_f32(kb)
+    ref_s = (np.abs(k).max(axis=1) / np.float32(448.0)).astype(np.float32)
+    assert np.array_equal(s.view(np.uint32), ref_s.view(np.uint32))
+    nz = s > 0
+    y = torch.from_numpy((k[nz] / s[nz, None]).astype(np.float32))
+    tc = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes[nz], tc)
+    assert np.all(codes[~nz] == 0)
+    # no NaN codes; the largest element of every nonzero key is +-448
+    assert not np.any((codes & 0x7F) == 0x7F)
+    big = np.abs(k[nz]).argmax(axis=1)
+    assert np.all((codes[nz][np.arange(nz.sum()), big] & 0x7F) == 0x7E)
+    assert codes[2, 5] == 0xFE
+
+
+def test_fp8_key_quantiser_round_trip_and_bound():
+    """Keys that are E4M3 values times a power-of-two scale with 448 among
+    them come back unchanged (codes and scale); any key is reproduced within
+    half an E4M3 step (relative 2^-4, or 2^-10 s absolute in the subnormal
+    range)."""
+    rng = np.random.default_rng(62)
+    N = 200
+    codes0 = rng.integers(0, 0x7F, size=(N, 64)).astype(np.uint8) | (rng.integers(0, 2, size=(N, 64)) * 0x80).astype(np.uint8)
+    codes0[:, 0] = 0x7E
+    e = rng.integers(-20, 20, size=N)
+    s0 = np.exp2(e).astype(np.float32)
+    k = (O.e4m3_value(codes0) * s0[:, None].astype(np.float64)).astype(np.float32)
+    kb = synth.f32_to_bf16_bits(k)
+    assert np.array_equal(synth.bf16_bits_to_f32(kb), k)        # exact in bf16 (4 significant bits)
+    codes, s = O.quantize_fp8_keys(kb)
+    assert np.array_equal(s, s0)
+    same = codes == codes0
+    # -0 and +0 codes both decode to 0 (the sign of a zero element is kept as given)
+    assert np.all(same | ((codes0 & 0x7F) == 0))
+    kb2 = _fp8_key_cases(np.random.default_rng(63))
+    c2, s2 = O.quantize_fp8_keys(kb2)
+    k2 = synth.bf16_bits_to_f32(kb2).astype(np.float64)
+    dq = O.e4m3_value(c2) * s2[:, None].astype(np.float64)
+    err = np.abs(dq - k2)
+    bound = np.maximum(np.abs(k2) * 2.0 ** -4, s2[:, None].astype(np.float64) * 2.0 ** -10) * (1 + 2.0 ** -20)
+    assert np.all(err <= bound)
