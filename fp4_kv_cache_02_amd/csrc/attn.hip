@@ -49,6 +49,7 @@ constexpr int kQRow = 65;                       // uint4 per head row of Q in LD
 constexpr int kPRow = kStepKeys + 8;            // halves per head row of P in LDS
 
 constexpr int kCodeRow = 68;                   // dwords per staged key row (256 B of codes + 16 B pad)
+constexpr int kSh2Row = 34;                    // dwords per staged scale row (32 fp16 pairs + 2 pad)
 
 struct AttnSmem {
   uint4 q[16 * kQRow];         // query of the step kind: fp16 (main steps) or bf16 (window step)
@@ -56,7 +57,7 @@ struct AttnSmem {
   uint16_t p_lo[16 * kPRow];
   int32_t slot[kStepKeys];     // slot of each main key of the step (-1: absent)
   uint32_t code[kStepKeys * kCodeRow];   // FP4 codes of the step's main keys (zeros when absent)
-  uint32_t scale[kStepKeys * 8];         // their E4M3 scales
+  uint32_t sh2[kStepKeys * kSh2Row];     // their scales as fp16 pairs {s, s}, one per 16 channels (0: absent)
   float red_m[kAttnWaves][16];
   float red_l[kAttnWaves][16];
   float qscale[16];            // main steps: sm_scale * 2^t_h, the query of head h held as q * 2^-t_h
@@ -81,13 +82,20 @@ CSA2_DEV void qk_main(const AttnSmem& sm, int w, int c, int g, float (&s)[8]) {
     uint4 raw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) raw[i] = src[i];
-    const uint2 sc = *(const uint2*)&sm.scale[key * 8 + 2 * g];
+    // the fp16 scale pairs of channel blocks 8g .. 8g+7
+    const uint2* sp = (const uint2*)&sm.sh2[key * kSh2Row + 8 * g];
+    uint32_t sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 x = sp[i];
+      sv[2 * i] = x.x;
+      sv[2 * i + 1] = x.y;
+    }
     const uint32_t rw[16] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w,
                              raw[2].x, raw[2].y, raw[2].z, raw[2].w, raw[3].x, raw[3].y, raw[3].z, raw[3].w};
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint32_t sbyte = ((t < 8 ? sc.x : sc.y) >> (8 * ((t >> 1) & 3))) & 0xFFu;
-      const half8_t kf = dequant8(rw[t], scale_h2(sbyte));
+      const half8_t kf = dequant8(rw[t], u2h(sv[t >> 1]));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, as_h8(qrow[t]), acc, 0, 0, 0);
     }
 #pragma unroll
@@ -96,12 +104,12 @@ CSA2_DEV void qk_main(const AttnSmem& sm, int w, int c, int g, float (&s)[8]) {
 }
 
 // Window keys of this wave's two 16-key groups: lane (c, g) holds key
-// 32w + 16u + c of the step (window entry koff + that), dims 128g .. 128g+127 (entry 0 of the buffer stands in for
-// an absent key; its words are zeroed at use).  Loaded at the head of the
-// window step, with the query, so that one round trip brings both.
+// 32w + 16u + c of the step (window entry koff + that), dims 128g .. 128g+127
+// (entry 0 of the buffer stands in for an absent key: its logits are replaced
+// by -inf, whatever the entry holds).  Loaded at the head of the window step,
+// with the query, so that one round trip brings both.
 struct WinK {
   uint4 k[2][16];
-  uint32_t ok[2];     // all-ones when the key is present
 };
 CSA2_DEV void win_k_load(const AttnLayer& Ly, int b, int wst, int wl, int koff, int nkeys, int w, int c, int g,
                          WinK& wk) {
@@ -112,7 +120,6 @@ CSA2_DEV void win_k_load(const AttnLayer& Ly, int b, int wst, int wl, int koff, 
     const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
 #pragma unroll
     for (int t = 0; t < 16; ++t) wk.k[u][t] = src[t];
-    wk.ok[u] = ok ? 0xFFFFFFFFu : 0u;
   }
 }
 
@@ -122,10 +129,8 @@ CSA2_DEV void qk_win(const AttnSmem& sm, const WinK& wk, int c, int g, float (&s
   for (int u = 0; u < 2; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint4 kz = mask4(wk.k[u][t], wk.ok[u]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kz), as_bf8(qrow[t]), acc, 0, 0, 0);
-    }
+    for (int t = 0; t < 16; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(wk.k[u][t]), as_bf8(qrow[t]), acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
   }
@@ -142,8 +147,7 @@ CSA2_DEV void pv_main(const AttnSmem& sm, RowState& st, int w, int c, int g) {
     for (int i = 0; i < 8; ++i) {
       const int key = key0 + i;
       dw[i] = sm.code[key * kCodeRow + 16 * w + c];
-      const uint32_t sw = sm.scale[key * 8 + 2 * w + (c >> 3)];
-      sv[i] = scale_h2((sw >> (8 * ((c >> 1) & 3))) & 0xFFu);
+      sv[i] = u2h(sm.sh2[key * kSh2Row + 8 * w + (c >> 1)]);
     }
     const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
     const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
@@ -162,25 +166,32 @@ CSA2_DEV void pv_main(const AttnSmem& sm, RowState& st, int w, int c, int g) {
   }
 }
 
+// The window keys of a step: entries koff .. koff + nkeys - 1 of the row's
+// window (b: the window buffer's sequence).
+struct WinGeo {
+  int b, wst, wl, koff;
+};
+CSA2_DEV bool win_key_ok(const AttnLayer& Ly, const WinGeo& wg, int kk) {
+  return kk < wg.wl && wg.wst >= 0 && (int64_t)wg.wst + kk < Ly.S;
+}
+
 // Window V words of keys 32 ks + 8g + i (i < 8) of the step (window entries
-// koff + those), dims 128w + 8c .. 128w + 8c + 7 (zero for an absent key).
-CSA2_DEV void win_v_load(const AttnLayer& Ly, int b, int wst, int wl, int koff, int ks, int w, int c, int g,
-                         uint4 (&vr)[8]) {
-  const int key0 = koff + 32 * ks + 8 * g;
-  uint4 v[8];
-  bool okv[8];
+// koff + those), dims 128w + 8c .. 128w + 8c + 7; an absent key reads entry 0
+// and is zeroed (P is 0 there, but the entry may hold any bits).
+CSA2_DEV void win_v_load(const AttnLayer& Ly, const WinGeo& wg, int ks, int w, int c, int g, uint4 (&vr)[8]) {
+  const int key0 = wg.koff + 32 * ks + 8 * g;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int kk = key0 + i;
-    okv[i] = kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
-    v[i] = Ly.swa_v[((int64_t)b * Ly.S + (okv[i] ? wst + kk : 0)) * 64 + 16 * w + c];
+    const bool ok = win_key_ok(Ly, wg, kk);
+    vr[i] = Ly.swa_v[((int64_t)wg.b * Ly.S + (ok ? wg.wst + kk : 0)) * 64 + 16 * w + c];
+    vr[i] = mask4(vr[i], ok ? 0xFFFFFFFFu : 0u);
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) vr[i] = mask4(v[i], okv[i] ? 0xFFFFFFFFu : 0u);
 }
 
 // O += P V over keys 32 ks .. 32 ks + 31 of the window step.
-CSA2_DEV void pv_win_part(const AttnSmem& sm, RowState& st, int ks, int c, int g, const uint4 (&vr)[8]) {
+CSA2_DEV void pv_win_part(const AttnLayer& Ly, const WinGeo& wg, const AttnSmem& sm, RowState& st, int ks, int c,
+                          int g, const uint4 (&v)[8]) {
   const int key0 = 32 * ks + 8 * g;
   const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
   const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
@@ -188,7 +199,7 @@ CSA2_DEV void pv_win_part(const AttnSmem& sm, RowState& st, int ks, int c, int g
   for (int m = 0; m < 4; ++m) {
     uint32_t x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (m == 0) ? vr[i].x : (m == 1) ? vr[i].y : (m == 2) ? vr[i].z : vr[i].w;
+    for (int i = 0; i < 8; ++i) x[i] = (m == 0) ? v[i].x : (m == 1) ? v[i].y : (m == 2) ? v[i].z : v[i].w;
     const uint4 b0 = make_uint4(pack_lo(x[0], x[1]), pack_lo(x[2], x[3]), pack_lo(x[4], x[5]), pack_lo(x[6], x[7]));
     const uint4 b1 = make_uint4(pack_hi(x[0], x[1]), pack_hi(x[2], x[3]), pack_hi(x[4], x[5]), pack_hi(x[6], x[7]));
     st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b0), st.o[2 * m], 0, 0, 0);
@@ -201,20 +212,20 @@ CSA2_DEV void pv_win_part(const AttnSmem& sm, RowState& st, int ks, int c, int g
 // The window step's P V over its 32-key parts (4, or 2 for half a window):
 // the first two were loaded before the softmax statistics; the later ones are
 // loaded ahead of the MFMAs that precede their use.
-CSA2_DEV void pv_win(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int koff,
-                     int nparts, int w, int c, int g, const uint4 (&v0)[8], const uint4 (&v1)[8]) {
+CSA2_DEV void pv_win(const AttnLayer& Ly, const WinGeo& wg, const AttnSmem& sm, RowState& st, int nparts, int w,
+                     int c, int g, const uint4 (&v0)[8], const uint4 (&v1)[8]) {
   if (nparts <= 2) {
-    pv_win_part(sm, st, 0, c, g, v0);
-    pv_win_part(sm, st, 1, c, g, v1);
+    pv_win_part(Ly, wg, sm, st, 0, c, g, v0);
+    pv_win_part(Ly, wg, sm, st, 1, c, g, v1);
     return;
   }
   uint4 v2[8], v3[8];
-  win_v_load(Ly, b, wst, wl, koff, 2, w, c, g, v2);
-  pv_win_part(sm, st, 0, c, g, v0);
-  win_v_load(Ly, b, wst, wl, koff, 3, w, c, g, v3);
-  pv_win_part(sm, st, 1, c, g, v1);
-  pv_win_part(sm, st, 2, c, g, v2);
-  pv_win_part(sm, st, 3, c, g, v3);
+  win_v_load(Ly, wg, 2, w, c, g, v2);
+  pv_win_part(Ly, wg, sm, st, 0, c, g, v0);
+  win_v_load(Ly, wg, 3, w, c, g, v3);
+  pv_win_part(Ly, wg, sm, st, 1, c, g, v1);
+  pv_win_part(Ly, wg, sm, st, 2, c, g, v2);
+  pv_win_part(Ly, wg, sm, st, 3, c, g, v3);
 }
 
 // Window step with loads issued part by part (the variant with two blocks
@@ -232,21 +243,19 @@ CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst
 #pragma unroll
     for (int t = 0; t < 16; ++t) kr[t] = src[t];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint4 kz = mask4(kr[t], ok ? 0xFFFFFFFFu : 0u);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kz), as_bf8(qrow[t]), acc, 0, 0, 0);
-    }
+    for (int t = 0; t < 16; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr[t]), as_bf8(qrow[t]), acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
   }
 }
-CSA2_DEV void pv_win_seq(const AttnLayer& Ly, const AttnSmem& sm, RowState& st, int b, int wst, int wl, int koff,
-                         int nparts, int w, int c, int g) {
+CSA2_DEV void pv_win_seq(const AttnLayer& Ly, const WinGeo& wg, const AttnSmem& sm, RowState& st, int nparts, int w,
+                         int c, int g) {
 #pragma unroll 1
   for (int ks = 0; ks < nparts; ++ks) {
     uint4 vr[8];
-    win_v_load(Ly, b, wst, wl, koff, ks, w, c, g, vr);
-    pv_win_part(sm, st, ks, c, g, vr);
+    win_v_load(Ly, wg, ks, w, c, g, vr);
+    pv_win_part(Ly, wg, sm, st, ks, c, g, vr);
   }
 }
 
@@ -479,10 +488,23 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
         pos_next = kk < a.k ? idx_row[kk] : -1;
       }
       if (kEarly && need_q) store_q(sm, qv, true, tid, Ly.sm_scale);
+      // codes as loaded; an absent key's scales are zero, so its values are
+      // zero whatever slot 0 holds (its logits are masked as well)
       uint4* dst = (uint4*)&sm.code[key * kCodeRow + 32 * half];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = mask4(rv[i], rmask);
-      *(uint4*)&sm.scale[key * 8 + 4 * half] = mask4(rsc, rmask);
+      for (int i = 0; i < 8; ++i) dst[i] = rv[i];
+      {
+        const uint4 scz = mask4(rsc, rmask);
+        const uint32_t sw[4] = {scz.x, scz.y, scz.z, scz.w};
+        uint2* sd = (uint2*)&sm.sh2[key * kSh2Row + 16 * half];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t o[4];
+          scale_pairs4(sw[i], o);
+          sd[2 * i] = make_uint2(o[0], o[1]);
+          sd[2 * i + 1] = make_uint2(o[2], o[3]);
+        }
+      }
       const uint64_t vmask = __ballot(sm.slot[32 * w + (lane & 31)] >= 0);
       __syncthreads();    // query, codes and scales visible
       CSA2_MARK(a, 1);
@@ -504,7 +526,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       float s[8];
       qk_win_seq(Ly, sm, wb, wst, wl, koff, nwk, w, c, g, s);
       step_softmax<false>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
-      pv_win_seq(Ly, sm, st, wb, wst, wl, koff, nwp, w, c, g);
+      const WinGeo wg{wb, wst, wl, koff};
+      pv_win_seq(Ly, wg, sm, st, nwp, w, c, g);
     } else {
       WinK wk;
       win_k_load(Ly, wb, wst, wl, koff, nwk, w, c, g, wk);
@@ -518,11 +541,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       float s[8];
       qk_win(sm, wk, c, g, s);
       // the first two 32-key parts of the values, in flight during the statistics
+      const WinGeo wg{wb, wst, wl, koff};
       uint4 v0[8], v1[8];
-      win_v_load(Ly, wb, wst, wl, koff, 0, w, c, g, v0);
-      win_v_load(Ly, wb, wst, wl, koff, 1, w, c, g, v1);
+      win_v_load(Ly, wg, 0, w, c, g, v0);
+      win_v_load(Ly, wg, 1, w, c, g, v1);
       step_softmax<false>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
-      pv_win(Ly, sm, st, wb, wst, wl, koff, nwp, w, c, g, v0, v1);
+      pv_win(Ly, wg, sm, st, nwp, w, c, g, v0, v1);
     }
     __syncthreads();    // P, slots and statistics may be overwritten by the next step
   }

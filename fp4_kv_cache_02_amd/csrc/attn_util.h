@@ -22,14 +22,26 @@ CSA2_DEV half2_t fp4x2(uint32_t word, int sel) {
   }
 }
 CSA2_DEV uint32_t h2u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
-CSA2_DEV uint32_t pack_lo(uint32_t x, uint32_t y) { return (x & 0xFFFFu) | (y << 16); }
-CSA2_DEV uint32_t pack_hi(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xFFFF0000u); }
-CSA2_DEV half2_t scale_h2(uint32_t code) {
-  const _Float16 s = (_Float16)e4m3_to_float(code);
-  return half2_t{s, s};
+CSA2_DEV half2_t u2h(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+// low halves of x and y as (x, y); high halves as (x, y): one byte permute each
+CSA2_DEV uint32_t pack_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
+CSA2_DEV uint32_t pack_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
+
+// Four E4M3 scales (the bytes of `w`) as fp16 pairs {s_i, s_i}: the hardware
+// OCP E4M3 -> fp16 conversion at unit scale (exact: every E4M3 value,
+// subnormals included, is an fp16 normal number), then each half doubled.
+CSA2_DEV void scale_pairs4(uint32_t w, uint32_t (&o)[4]) {
+  const uint32_t a = h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  const uint32_t b = h2u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  o[0] = pack_lo(a, a);
+  o[1] = pack_hi(a, a);
+  o[2] = pack_lo(b, b);
+  o[3] = pack_hi(b, b);
 }
 
-// 8 consecutive FP4 codes (one dword) times one E4M3 scale, as fp16 (exact).
+// 8 consecutive FP4 codes (one dword) times one E4M3 scale held as the fp16
+// pair {s, s}, as fp16 (exact: an E2M1 value times an E4M3 value has at most
+// six significant bits and lies within fp16's normal range).
 CSA2_DEV half8_t dequant8(uint32_t word, half2_t sv) {
   const half2_t h0 = fp4x2(word, 0) * sv, h1 = fp4x2(word, 1) * sv;
   const half2_t h2 = fp4x2(word, 2) * sv, h3 = fp4x2(word, 3) * sv;

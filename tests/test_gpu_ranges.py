@@ -152,3 +152,39 @@ def test_hier_candidates_keep_below_2048(C, keep):
     g = host(out)
     for r, L in enumerate(lens):
         assert np.array_equal(g[r], O.topk(bm[r, :(L + 7) // 8], keep)), (r, keep)
+
+
+def test_attention_every_scale_code(C):
+    """Each row attends one main key and no window, so its output is that
+    key's dequantised vector times a softmax weight of exactly 1: the FP4
+    values times their E4M3 scales, which the kernel converts to fp16 with the
+    hardware conversion.  Eight rows cover the 254 scale codes that are
+    numbers (zero, subnormals, 448, negative scales; the two NaN codes are
+    left out, padded with 1.0); the outputs must equal the float64 decode
+    exactly."""
+    rng = np.random.default_rng(1500)
+    R = 8
+    L = 40
+    packed = rng.integers(0, 256, size=(L, 256), dtype=np.uint8)
+    scale = rng.integers(0x28, 0x40, size=(L, 32), dtype=np.uint8)
+    keys = rng.choice(L, size=R, replace=False)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] + [0x38, 0x38], np.uint8)
+    for r in range(R):
+        scale[keys[r]] = codes[32 * r:32 * r + 32]
+    idx = keys.astype(np.int32).reshape(R, 1)
+    q = bf16(rng, (R, 16, 512))
+    swk, swv = bf16(rng, (1, 8, 512)), bf16(rng, (1, 8, 512))
+    say("attention every scale code")
+    kv = C.make_cache(dev(packed), dev(scale), seq_stride=L)
+    out = torch.full((R, 16, 512), float("nan"), device="cuda")
+    lse = torch.full((R, 16), float("nan"), device="cuda")
+    ws = workspace(C.csa2_attn_workspace_bytes(R))
+    C.csa2_fp4_sparse_attn(dev(q), kv, dev(np.array([L], np.int32)), dev(idx), dev(swk), dev(swv),
+                           dev(np.zeros(R, np.int32)), dev(np.zeros(R, np.int32)), 1.0 / math.sqrt(512), out, lse, ws,
+                           row_seq=dev(np.zeros(R, np.int32)))
+    torch.cuda.synchronize()
+    g = host(out)
+    ref = O.dequantize_fp4(packed[keys], scale[keys])
+    for r in range(R):
+        for h in range(16):
+            assert np.array_equal(g[r, h].astype(np.float64), ref[r]), (r, h)
