@@ -153,3 +153,19 @@ def test_group_many_decode_rows(R):
     lens[0], lens[1] = 0, 5000
     w = synth.Workload(f"decode_many_rows_b{R}", 1300 + R, lens, "FRRR", planted=0.01, raw_fp4=True)
     run_and_compare(w, by_group=True, check_rows=[0, 1, 2, 57, 101, 159, R - 1])
+
+
+@pytest.mark.parametrize("lens,paged", [
+    ([1048576, 131073, 32767, 32768, 32769, 500001, 65, 0], True),
+    ([262144, 131073, 200000, 163840], False),
+])
+@pytest.mark.parametrize("kind", ["planted", "equal_keys"])
+def test_group_long_full_rows(lens, paged, kind):
+    """Full-layer Top-512 on rows past 131072 positions (one block per row
+    descending the scan's maxima): a row of 2^20 positions, rows just past
+    131072 and around multiples of 32768, short and empty rows in the same
+    batch, paged and contiguous caches.  With every indexer key equal, every
+    score of a row ties and the selection takes its general path."""
+    w = synth.Workload(f"long_full_rows_{'paged' if paged else 'contig'}", 1600 + len(lens), lens, "FR",
+                       paged=paged, planted=0.02, raw_fp4=True)
+    run_and_compare(w, by_group=True, equal_keys=kind == "equal_keys")
