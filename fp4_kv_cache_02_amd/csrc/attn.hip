@@ -200,8 +200,8 @@ CSA2_DEV void pv_win_part(const AttnLayer& Ly, const WinGeo& wg, const AttnSmem&
     uint32_t x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (m == 0) ? v[i].x : (m == 1) ? v[i].y : (m == 2) ? v[i].z : v[i].w;
-    const uint4 b0 = make_uint4(pack_lo(x[0], x[1]), pack_lo(x[2], x[3]), pack_lo(x[4], x[5]), pack_lo(x[6], x[7]));
-    const uint4 b1 = make_uint4(pack_hi(x[0], x[1]), pack_hi(x[2], x[3]), pack_hi(x[4], x[5]), pack_hi(x[6], x[7]));
+    const uint4 b0 = make_uint4(pack_lo_w(x[0], x[1]), pack_lo_w(x[2], x[3]), pack_lo_w(x[4], x[5]), pack_lo_w(x[6], x[7]));
+    const uint4 b1 = make_uint4(pack_hi_w(x[0], x[1]), pack_hi_w(x[2], x[3]), pack_hi_w(x[4], x[5]), pack_hi_w(x[6], x[7]));
     st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b0), st.o[2 * m], 0, 0, 0);
     st.o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), as_bf8(b0), st.o[2 * m], 0, 0, 0);
     st.o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(ph), as_bf8(b1), st.o[2 * m + 1], 0, 0, 0);

@@ -23,9 +23,14 @@ CSA2_DEV half2_t fp4x2(uint32_t word, int sel) {
 }
 CSA2_DEV uint32_t h2u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 CSA2_DEV half2_t u2h(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
-// low halves of x and y as (x, y); high halves as (x, y): one byte permute each
+// low halves of x and y as (x, y); high halves as (x, y): one byte permute
+// each (the FP4 values of a main step), or a mask and a shift each (the
+// window's bf16 words: with the permute there, a launch of whole window
+// steps -- eight rows x six layers -- measured ~2.5 us slower)
 CSA2_DEV uint32_t pack_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
 CSA2_DEV uint32_t pack_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
+CSA2_DEV uint32_t pack_lo_w(uint32_t x, uint32_t y) { return (x & 0xFFFFu) | (y << 16); }
+CSA2_DEV uint32_t pack_hi_w(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xFFFF0000u); }
 
 // Four E4M3 scales (the bytes of `w`) as fp16 pairs {s_i, s_i}: the hardware
 // OCP E4M3 -> fp16 conversion at unit scale (exact: every E4M3 value,
