@@ -169,3 +169,21 @@ def test_group_long_full_rows(lens, paged, kind):
     w = synth.Workload(f"long_full_rows_{'paged' if paged else 'contig'}", 1600 + len(lens), lens, "FR",
                        paged=paged, planted=0.02, raw_fp4=True)
     run_and_compare(w, by_group=True, equal_keys=kind == "equal_keys")
+
+
+@pytest.mark.parametrize("R", [24, 150])
+def test_group_blocks_only_full_then_reuse(R):
+    """A hierarchical Full layer that only builds the candidate blocks, with
+    three Reuse layers in its group (they attend over the Top-K the Reindex
+    layer of the group before left): the group's attention covers one layer
+    fewer than the group holds, and at these batch sizes three layers take
+    more attention partials than four would (24 rows: 6 blocks per
+    row-layer for three layers against 4 for four, 432 partials against
+    384; 150 rows: partials and a merge for three layers, one block per
+    row-layer and no partials for four), so the group workspace must be
+    sized for both counts."""
+    r = np.random.default_rng(1700 + R)
+    lens = [int(x) for x in r.integers(600, 5001, size=R)]
+    w = synth.Workload(f"blocks_only_FIRRR_FRRR_b{R}", 1700 + R, lens, "FIRRRFRRR", hier=True,
+                       full_blocks_only=True, planted=0.01, raw_fp4=True)
+    run_and_compare(w, by_group=True, check_rows=sorted(set([0, 1, R // 2, R - 1])))
