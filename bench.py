@@ -46,6 +46,8 @@ def parse():
                    help="skip the 38-layer decode step (reported beside the default)")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the 128K group on FP8 indexer keys (reported beside the default)")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the full_4k, prefill and serving sub-objects (the default line keeps the rest)")
     p.add_argument("--no-extras", action="store_true",
                    help="report the default workload alone (no 1M, 4K, prefill, serving, FP8-key or 38-layer "
                         "sub-objects)")
@@ -547,7 +549,7 @@ def main():
         # layer building 2048 candidate blocks, then Reindex + 3 Reuse)
         w2 = synth.workload("decode_1m")
         out["context_1m"] = decode_summary(w2, measure(w2, args.steps, args.warmup, args.replicas))
-    if default:
+    if default and not args.no_others:
         # the other workloads, each timed the same way: one Full layer at 4096
         # positions, the 4096-row prefill chunk (priced against the MFMA
         # peak) and the mixed 20-layer serving batch
