@@ -107,7 +107,7 @@ struct MaximaArgs {
 };
 
 constexpr int kMaxAttnLayers = CSA2_MAX_GROUP_LAYERS;
-constexpr int kMaxAttnBlocks = 6;   // 4 main steps + the window step in two halves
+constexpr int kMaxAttnBlocks = 8;   // 4 main steps + the window step in four quarters
 
 struct AttnLayer {
   const uint4* q;               // [R][16][64] uint4 (8 bf16 each)
