@@ -30,8 +30,9 @@
 //      in that layout.
 // A block that covers every step of its row (many rows) keeps an online
 // softmax over the steps and writes the output; otherwise (few rows: decode)
-// each block takes one step (the window step split over two blocks of 64
-// keys, halving the window K/V one CU fetches) and writes a partial (O, max, sum), and
+// each block takes one or two steps (the window step split over two or four
+// blocks, so that one CU fetches a half or a quarter of the window K/V) and
+// writes a partial (O, max, sum), and
 // attn_merge_kernel combines the partials of each row as one softmax.  (A
 // cross-block hand-off inside one kernel would need a device-scope release,
 // which on this chip writes back the whole L2 of the issuing XCD.)  Several
@@ -265,29 +266,8 @@ CSA2_DEV void pv_win_part(const AttnSmem& sm, RowState<Shape<NW>::NT>& st, int k
   }
 }
 
-// The window step's P V over its 32-key parts (4, or 2 for half a window):
-// the first two were loaded before the softmax statistics; the later ones are
-// loaded ahead of the MFMAs that precede their use.
-template <int NW>
-CSA2_DEV void pv_win(const AttnLayer& Ly, const WinGeo& wg, const AttnSmem& sm, RowState<Shape<NW>::NT>& st,
-                     int nparts, int w, int c, int g, const VWord<Shape<NW>::NT> (&v0)[8],
-                     const VWord<Shape<NW>::NT> (&v1)[8]) {
-  if (nparts <= 2) {
-    pv_win_part<NW>(sm, st, 0, c, g, v0);
-    pv_win_part<NW>(sm, st, 1, c, g, v1);
-    return;
-  }
-  VWord<Shape<NW>::NT> v2[8], v3[8];
-  win_v_load<NW>(Ly, wg, 2, w, c, g, v2);
-  pv_win_part<NW>(sm, st, 0, c, g, v0);
-  win_v_load<NW>(Ly, wg, 3, w, c, g, v3);
-  pv_win_part<NW>(sm, st, 1, c, g, v1);
-  pv_win_part<NW>(sm, st, 2, c, g, v2);
-  pv_win_part<NW>(sm, st, 3, c, g, v3);
-}
-
-// Window step with loads issued part by part (the variant with two blocks
-// per CU, whose register budget does not hold the batched loads).
+// Window keys loaded one 16-key group at a time (two blocks per CU: their
+// register budget does not hold a wave's keys at once).
 template <int NW>
 CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int koff, int nkeys, int w,
                          int c, int g, float (&s)[4 * Shape<NW>::NU]) {
@@ -309,6 +289,9 @@ CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst
     for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
   }
 }
+// The window step's P V over its 32-key parts (4, 2 or 1), each part's values
+// loaded just ahead of its MFMAs (a wave's registers do not hold the values
+// of several parts beside its output tiles at two waves per SIMD).
 template <int NW>
 CSA2_DEV void pv_win_seq(const AttnLayer& Ly, const WinGeo& wg, const AttnSmem& sm, RowState<Shape<NW>::NT>& st,
                          int nparts, int w, int c, int g) {
@@ -444,10 +427,10 @@ CSA2_DEV void store_q(AttnSmem& sm, const uint4 (&qv)[Shape<NW>::NQ], bool to_f1
 
 // BPC: blocks per CU; NW: waves per block.  BPC = 1 (a launch whose blocks
 // all fit on the CUs at once, as in decode) runs NW = 8 waves (two per SIMD,
-// each with half a step's work), and the window step issues its keys with the
-// query and its values ahead of use, and a main step its indices with the
-// query.  BPC = 2 (many blocks, prefill) runs NW = 4 waves and loads them
-// part by part.
+// each with half a step's work): the window step issues all of its keys with
+// the query, a main step its indices with the query.  BPC = 2 (many blocks:
+// prefill, large decode batches) runs NW = 4 waves and loads the window keys
+// one 16-key group at a time.
 template <int BPC, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BPC * NW / 4, BPC * NW / 4)))
 void fp4_attn_kernel(AttnArgs a) {
@@ -621,19 +604,8 @@ void fp4_attn_kernel(AttnArgs a) {
       float s[4 * S::NU];
       qk_win<NW>(sm, wk, c, g, s);
       const WinGeo wg{wb, wst, wl, koff};
-      if constexpr (NW == 4) {
-        // the first two 32-key parts of the values, in flight during the statistics
-        VWord<NT> v0[8], v1[8];
-        win_v_load<NW>(Ly, wg, 0, w, c, g, v0);
-        win_v_load<NW>(Ly, wg, 1, w, c, g, v1);
-        step_softmax<false, NW>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
-        pv_win<NW>(Ly, wg, sm, st, nwp, w, c, g, v0, v1);
-      } else {
-        // (eight waves: two per SIMD, whose registers hold the keys but not
-        // the values as well) the values part by part after the statistics
-        step_softmax<false, NW>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
-        pv_win_seq<NW>(Ly, wg, sm, st, nwp, w, c, g);
-      }
+      step_softmax<false, NW>(sm, st, s, vmask, Ly.sm_scale, w, c, g);
+      pv_win_seq<NW>(Ly, wg, sm, st, nwp, w, c, g);
     }
     __syncthreads();    // P, slots and statistics may be overwritten by the next step
   }
