@@ -213,7 +213,11 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
 }
 
 // Builds the missing levels of maxima into the workspace, then selects.
-csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
+// defer (optional): when the split path is taken, only its segment lists are
+// built here and *defer receives the arguments of its final selection, which
+// the attention launch that follows takes over (defer->out stays null
+// otherwise).
+csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st, TopkArgs* defer = nullptr) {
   const int need = topk_levels_built(a.R, a.n_max, a.k);
   for (int l = 1; l <= need; ++l) {
     if (a.lv[l]) continue;
@@ -250,6 +254,10 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st) {
     a.seg_cnt = tw.desc_cnt;
     a.seg_key = tw.desc_key;
     a.seg_pos = tw.desc_pos;
+    if (defer) {
+      *defer = a;
+      return hip_status(launch_desc_seg(a, st));
+    }
     return hip_status(launch_topk_desc(a, st));
   }
   return hip_status(launch_topk(a, st));
@@ -299,10 +307,14 @@ struct AttnLayerIn {
   int32_t swa_shared;
 };
 
+// fin (optional): the split Top-k's final selection, still to run (it
+// writes idx); the attention launch takes it over or launches it first.
 csa2_status do_attn(const AttnLayerIn* L, int n_layers, const csa2_cache* kv, const int32_t* row_seq,
                     const int32_t* seq_len, const int32_t* idx, int32_t k, int32_t R,
-                    const AttnWs& aw, char* ws, hipStream_t st) {
+                    const AttnWs& aw, char* ws, hipStream_t st, const TopkArgs* fin = nullptr) {
   AttnArgs a;
+  a.sel = fin ? *fin : TopkArgs{};
+  if (!fin) a.sel.out = nullptr;
   for (int i = 0; i < n_layers; ++i) {
     a.layer[i].q = (const uint4*)L[i].q;
     a.layer[i].swa_k = (const uint4*)L[i].swa_k;
@@ -396,7 +408,7 @@ size_t index_region(csa2_mode mode, int R, int n_max, int hier) {
 // shared->topk_idx (and the candidate blocks of a hierarchical Full layer in
 // shared->cand_blocks).
 csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_shared* sh, Bump& bp, bool blocks_only,
-                      hipStream_t st) {
+                      hipStream_t st, TopkArgs* defer) {
   const int R = a->R, n_max = sh->n_max;
   csa2_status s;
   if (mode == CSA2_FULL || (mode == CSA2_REINDEX && !sh->hier)) {
@@ -478,7 +490,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       TopkArgs t = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
       t.lv[1] = bmax;
       t.lv[2] = m64;
-      s = run_topk(t, dw, st);
+      s = run_topk(t, dw, st, defer);
       if (s) return s;
     }
     if (mode == CSA2_FULL && sh->hier) {
@@ -504,7 +516,7 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
   t.lv[1] = cmax;
   t.cand_blocks = sh->cand_blocks;
   t.cand_stride = CSA2_KEEP_BLOCKS;
-  return run_topk(t, dw, st);
+  return run_topk(t, dw, st, defer);
 }
 
 csa2_status check_shared(const csa2_shared* sh, int R) {
@@ -726,15 +738,19 @@ csa2_status csa2_group_step(csa2_mode first_mode, int32_t n_layers, const csa2_l
   const int na = n_layers - a0;
   const AttnWs aw = na > 0 ? carve_attn(bp, R, na, CSA2_TOPK) : AttnWs{nullptr, nullptr, 0, 0};
   if (bp.over) return CSA2_ERR_WORKSPACE;
+  // the split Top-512's final selection may be left to the attention launch
+  TopkArgs fin{};
+  fin.out = nullptr;
   if (first_mode != CSA2_REUSE) {
     Bump ib{w, index_off, index_end};
-    s = run_index(first_mode, &layers[0], sh, ib, blocks_only, st);
+    s = run_index(first_mode, &layers[0], sh, ib, blocks_only, st, na > 0 ? &fin : nullptr);
     if (s) return s;
   }
   if (na == 0) return CSA2_OK;
   AttnLayerIn L[CSA2_MAX_GROUP_LAYERS];
   for (int i = 0; i < na; ++i) L[i] = layer_in(&layers[a0 + i]);
-  return do_attn(L, na, &sh->kv, layers[0].row_seq, sh->seq_len, sh->topk_idx, CSA2_TOPK, R, aw, w, st);
+  return do_attn(L, na, &sh->kv, layers[0].row_seq, sh->seq_len, sh->topk_idx, CSA2_TOPK, R, aw, w, st,
+                 fin.out ? &fin : nullptr);
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, const csa2_shared* sh, void* ws,

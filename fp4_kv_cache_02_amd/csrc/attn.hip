@@ -44,6 +44,7 @@
 // multiply by the E4M3 scale (products have <= 6 significant bits within
 // fp16's normal range).  Window steps use bf16 throughout.
 #include "attn_util.h"
+#include "topk_row.h"
 
 
 namespace csa2 {
@@ -431,13 +432,35 @@ CSA2_DEV void store_q(AttnSmem& sm, const uint4 (&qv)[Shape<NW>::NQ], bool to_f1
 // the query, a main step its indices with the query.  BPC = 2 (many blocks:
 // prefill, large decode batches) runs NW = 4 waves and loads the window keys
 // one 16-key group at a time.
-template <int BPC, int NW>
+// LDS of a block: the attention's; with SEL also the final Top-k selection's
+// (used first, then given over to the attention) and the selected positions.
+template <bool SEL>
+struct AttnShared {
+  AttnSmem at;
+};
+template <>
+struct AttnShared<true> {
+  union {
+    AttnSmem at;
+    DescFinalSmem topk;
+  };
+  int32_t sel_pos[CSA2_TOPK];
+};
+
+// SEL: the split Top-k's final selection runs at the head of every block of
+// main steps (each repeats its row's selection from the segment lists and
+// keeps the row's k positions in LDS; one block per row also writes them to
+// idx), instead of in a launch of its own whose end the attention would wait
+// for.  Window blocks need no indices and start at once.
+template <int BPC, int NW, bool SEL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BPC * NW / 4, BPC * NW / 4)))
 void fp4_attn_kernel(AttnArgs a) {
   using S = Shape<NW>;
   constexpr bool kEarly = BPC == 1;
   constexpr int NT = S::NT;
-  __shared__ AttnSmem sm;
+  static_assert(!SEL || NW * 64 == kSelThreads, "the selection runs on blocks of kSelThreads threads");
+  __shared__ AttnShared<SEL> shm;
+  AttnSmem& sm = shm.at;
   // flat grid: block id = (li * R + r) * n_blocks + blk
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so
   // within each run of 8 rows, row 8q + x takes every id = x (mod 8): all
@@ -467,6 +490,7 @@ void fp4_attn_kernel(AttnArgs a) {
   // window step in one block, or split over nwb = 2 or 4 blocks of 128 / nwb
   // keys (the blocks of the row-layer past its main-step blocks).
   int st0, st1, nwb = 1, wpart = 0;
+  bool main_block = true;
   if (a.n_blocks == 1) {
     st0 = 0;
     st1 = n_main + 1;
@@ -481,12 +505,26 @@ void fp4_attn_kernel(AttnArgs a) {
       st1 = n_main + 1;
       nwb = a.n_blocks - nmb;
       wpart = blk - nmb;
+      main_block = false;
     }
   }
   const int nwk = kStepKeys / nwb;                                  // the window step's keys in this block
   const int koff = nwk * wpart;                                     // its first window entry
   const int nwp = nwk / 32;                                         // 32-key parts
   const int32_t* idx_row = a.idx + (int64_t)r * a.k;
+  if constexpr (SEL) {
+    if (main_block) {     // uniform over the block
+      desc_final_row(a.sel, r, shm.topk, shm.sel_pos);
+      __syncthreads();    // positions visible; the selection's LDS is free
+      if (li == 0 && blk == 0)
+        for (int i = threadIdx.x; i < a.k; i += NW * 64) a.sel.out[(int64_t)r * a.sel.out_stride + i] = shm.sel_pos[i];
+    }
+  }
+  // position of rank kk of the row's Top-k (kk < k)
+  auto rank_pos = [&](int kk) -> int {
+    if constexpr (SEL) return shm.sel_pos[kk];
+    else return idx_row[kk];
+  };
   const int wst = Ly.swa_start[r];
   const int wl = min(Ly.swa_len[r], CSA2_MAX_WINDOW);
   CSA2_MARK(a, 0);
@@ -523,7 +561,7 @@ void fp4_attn_kernel(AttnArgs a) {
       // each thread finds the slot of the key it stages (its index, then the
       // slot: no hand-off through LDS ahead of the row loads)
       const int kk = step * kStepKeys + skey;
-      const int pos = (step > st0) ? pos_next : (kk < a.k ? idx_row[kk] : -1);
+      const int pos = (step > st0) ? pos_next : (kk < a.k ? rank_pos(kk) : -1);
       uint4 qv[S::NQ];
       if (need_q) {
 #pragma unroll
@@ -550,7 +588,7 @@ void fp4_attn_kernel(AttnArgs a) {
       const uint32_t rmask = sl >= 0 ? 0xFFFFFFFFu : 0u;
       if (step + 1 < min(st1, n_main)) {
         const int kn = (step + 1) * kStepKeys + skey;
-        pos_next = kn < a.k ? idx_row[kn] : -1;
+        pos_next = kn < a.k ? rank_pos(kn) : -1;
       }
       if (kEarly && need_q) store_q<NW>(sm, qv, true, tid, Ly.sm_scale);
       // codes as loaded; an absent key's scales are zero, so its values are
@@ -739,10 +777,19 @@ int attn_blocks(int k, int rows_x_layers, int* steps_per_block) {
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.R == 0 || a.n_layers == 0) return hipSuccess;
   const int64_t blocks = (int64_t)a.n_blocks * a.R * a.n_layers;
-  if (blocks <= 256)   // one block of eight waves per CU
-    hipLaunchKernelGGL((fp4_attn_kernel<1, 8>), dim3((unsigned)blocks), dim3(8 * 64), 0, st, a);
-  else                 // two blocks of four waves per CU
-    hipLaunchKernelGGL((fp4_attn_kernel<2, 4>), dim3((unsigned)blocks), dim3(4 * 64), 0, st, a);
+  const bool sel = a.sel.out != nullptr;    // the split Top-k's final selection is still to run
+  if (blocks <= 256) {   // one block of eight waves per CU
+    if (sel)
+      hipLaunchKernelGGL((fp4_attn_kernel<1, 8, true>), dim3((unsigned)blocks), dim3(8 * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((fp4_attn_kernel<1, 8, false>), dim3((unsigned)blocks), dim3(8 * 64), 0, st, a);
+  } else {               // two blocks of four waves per CU, after the selection's own launch
+    if (sel) {
+      const hipError_t e = launch_desc_final(a.sel, st);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((fp4_attn_kernel<2, 4, false>), dim3((unsigned)blocks), dim3(4 * 64), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_blocks == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(4 * a.n_layers * a.R), dim3(256), 0, st, a);

@@ -137,6 +137,10 @@ struct AttnArgs {
   int32_t steps_per_block;    // 128-key steps per block
   float* part_o;                // [n_layers][R][n_blocks][16][512]
   float* part_ml;               // [n_layers][R][n_blocks][16][2]
+  // the final selection of the split Top-k, when it is left to this launch
+  // (sel.out non-null: the segment lists are ready, idx = sel.out is still to
+  // be written)
+  TopkArgs sel;
   CSA2_TRACE_ARG
 };
 
@@ -144,6 +148,8 @@ hipError_t launch_index_score(const IdxArgs& a, bool cand, bool has_w, bool maxi
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_desc(const TopkArgs& a, hipStream_t st);
+hipError_t launch_desc_seg(const TopkArgs& a, hipStream_t st);
+hipError_t launch_desc_final(const TopkArgs& a, hipStream_t st);
 hipError_t launch_maxima(const MaximaArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,
