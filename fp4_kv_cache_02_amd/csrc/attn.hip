@@ -512,10 +512,13 @@ void fp4_attn_kernel(AttnArgs a) {
   const int koff = nwk * wpart;                                     // its first window entry
   const int nwp = nwk / 32;                                         // 32-key parts
   const int32_t* idx_row = a.idx + (int64_t)r * a.k;
+  CSA2_MARK(a, 0);
+  CSA2_SPAN(a, 256, 0);
   if constexpr (SEL) {
     if (main_block) {     // uniform over the block
       desc_final_row(a.sel, r, shm.topk, shm.sel_pos);
       __syncthreads();    // positions visible; the selection's LDS is free
+      CSA2_MARK(a, 6);
       if (li == 0 && blk == 0)
         for (int i = threadIdx.x; i < a.k; i += NW * 64) a.sel.out[(int64_t)r * a.sel.out_stride + i] = shm.sel_pos[i];
     }
@@ -527,8 +530,6 @@ void fp4_attn_kernel(AttnArgs a) {
   };
   const int wst = Ly.swa_start[r];
   const int wl = min(Ly.swa_len[r], CSA2_MAX_WINDOW);
-  CSA2_MARK(a, 0);
-  CSA2_SPAN(a, 256, 0);
 
   RowState<NT> st;
 #pragma unroll

@@ -351,15 +351,11 @@ CSA2_DEV void desc_final_row(const TopkArgs& a, int r, DescFinalSmem& u, int32_t
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const uint32_t K = (uint32_t)a.k;
-  const int64_t n0 = row_count(a, r);
-  if (n0 == 0) {
-    for (int i = tid; i < a.k; i += kSelThreads) out[i] = -1;
-    return;
-  }
-  CSA2_MARK(a, 3);
   // list lengths (one segment per lane; every wave alike) and, in the same
   // round of loads, the fixed register slots of the fast path below: segment
-  // s owns slots [spp s, spp (s+1)), thread t slots 4t .. 4t+3
+  // s owns slots [spp s, spp (s+1)), thread t slots 4t .. 4t+3.  Issued
+  // beside the row's length (every segment of an empty row has length 0, and
+  // the slots are read only below a list's length).
   const uint32_t c = lane < a.nseg ? a.seg_cnt[(int64_t)r * a.nseg + lane] : 0u;
   const int64_t rb = (int64_t)r * a.nseg * kDescCap;
   const int spp = min(kRegCap / a.nseg, kDescCap) & ~(kRegPer - 1);
@@ -367,6 +363,12 @@ CSA2_DEV void desc_final_row(const TopkArgs& a, int r, DescFinalSmem& u, int32_t
   const int64_t g0 = sg < a.nseg ? rb + (int64_t)sg * kDescCap + sl0 : rb;
   const uint4 kk = *(const uint4*)(a.seg_key + g0);
   const int4 pp = *(const int4*)(a.seg_pos + g0);
+  const int64_t n0 = row_count(a, r);
+  if (n0 == 0) {
+    for (int i = tid; i < a.k; i += kSelThreads) out[i] = -1;
+    return;
+  }
+  CSA2_MARK(a, 3);
   const bool marked = __ballot(c > (uint32_t)kDescCap) != 0ull;
   const uint32_t inc = wave_incl_scan_u32(c);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
