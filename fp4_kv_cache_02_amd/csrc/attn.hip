@@ -123,10 +123,14 @@ CSA2_DEV void qk_main(const AttnSmem& sm, int w, int c, int g, float (&s)[4 * Sh
 }
 
 // Window keys of this wave's 16-key groups: lane (c, g) holds key
-// KPW w + 16u + c of the step (window entry koff + that), dims 128g ..
-// 128g+127 (entry 0 of the buffer stands in for an absent key: its logits are
-// replaced by -inf, whatever the entry holds).  Loaded at the head of the
-// window step, with the query, so that one round trip brings both.
+// KPW w + 16u + c of the step (window entry koff + that), dims 32t + 8g ..
+// 32t + 8g + 7 in its t-th word, so that the four lanes of a key read one
+// 64-byte piece of its row per load (a lane reading a contiguous quarter of
+// the row touched four times as many cache lines per load; the MFMA's t-th
+// step then sums dims 32t .. 32t + 31).  Entry 0 of the buffer stands in for
+// an absent key: its logits are replaced by -inf, whatever the entry holds.
+// Loaded at the head of the window step, with the query, so that one round
+// trip brings both.
 template <int NW>
 struct WinK {
   uint4 k[Shape<NW>::NU][16];
@@ -139,21 +143,21 @@ CSA2_DEV void win_k_load(const AttnLayer& Ly, int b, int wst, int wl, int koff, 
   for (int u = 0; u < S::NU; ++u) {
     const int e = S::KPW * w + 16 * u + c, kk = koff + e;
     const bool ok = e < nkeys && kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
-    const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
+    const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) wk.k[u][t] = src[t];
+    for (int t = 0; t < 16; ++t) wk.k[u][t] = src[4 * t];
   }
 }
 
 template <int NW>
 CSA2_DEV void qk_win(const AttnSmem& sm, const WinK<NW>& wk, int c, int g, float (&s)[4 * Shape<NW>::NU]) {
-  const uint4* qrow = sm.q + c * kQRow + 16 * g;
+  const uint4* qrow = sm.q + c * kQRow + g;
 #pragma unroll
   for (int u = 0; u < Shape<NW>::NU; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 16; ++t)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(wk.k[u][t]), as_bf8(qrow[t]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(wk.k[u][t]), as_bf8(qrow[4 * t]), acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
   }
@@ -273,19 +277,19 @@ template <int NW>
 CSA2_DEV void qk_win_seq(const AttnLayer& Ly, const AttnSmem& sm, int b, int wst, int wl, int koff, int nkeys, int w,
                          int c, int g, float (&s)[4 * Shape<NW>::NU]) {
   using S = Shape<NW>;
-  const uint4* qrow = sm.q + c * kQRow + 16 * g;
+  const uint4* qrow = sm.q + c * kQRow + g;
 #pragma unroll 1
   for (int u = 0; u < S::NU; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int e = S::KPW * w + 16 * u + c, kk = koff + e;
     const bool ok = e < nkeys && kk < wl && wst >= 0 && (int64_t)wst + kk < Ly.S;
-    const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g * 16;
+    const uint4* src = Ly.swa_k + ((int64_t)b * Ly.S + (ok ? wst + kk : 0)) * 64 + g;   // as in win_k_load
     uint4 kr[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) kr[t] = src[t];
+    for (int t = 0; t < 16; ++t) kr[t] = src[4 * t];
 #pragma unroll
     for (int t = 0; t < 16; ++t)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr[t]), as_bf8(qrow[t]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr[t]), as_bf8(qrow[4 * t]), acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * u + i] = acc[i];
   }
@@ -543,7 +547,9 @@ void fp4_attn_kernel(AttnArgs a) {
   const uint4* qsrc = Ly.q + (int64_t)r * 16 * 64;
   const int wb = Ly.swa_shared ? 0 : b;
   // staging of a main step's rows: thread t loads part t % (NW / 2) of key
-  // t / (NW / 2) -- 256 / (NW / 2) bytes of codes and 32 / (NW / 2) of scales
+  // t / (NW / 2) -- 256 / (NW / 2) bytes of codes and 32 / (NW / 2) of scales;
+  // the codes as the 16-byte pieces p + i NW / 2 of the row (i = 0, 1, ...),
+  // so that the threads of a key read adjacent pieces with each load
   constexpr int TPK = NW / 2;                 // threads per key (2, 4)
   constexpr int CPT = 16 / TPK;               // uint4 of codes per thread (8, 4)
   constexpr int SPT = 32 / TPK;               // scale bytes per thread (16, 8)
@@ -574,10 +580,10 @@ void fp4_attn_kernel(AttnArgs a) {
       // the step's FP4 rows (unconditional loads from slot 0 for absent keys;
       // their scales are zeroed below, so their values are zero)
       const int64_t ss = sl >= 0 ? sl : 0;
-      const uint4* src = (const uint4*)(a.kv + ss * 256) + CPT * spart;
+      const uint4* src = (const uint4*)(a.kv + ss * 256) + spart;
       uint4 rv[CPT];
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) rv[i] = src[i];
+      for (int i = 0; i < CPT; ++i) rv[i] = src[TPK * i];
       uint32_t rs[SPT / 4];
       if constexpr (SPT == 16) {
         const uint4 x = *(const uint4*)(a.kv_scale + ss * 32 + 16 * spart);
@@ -594,9 +600,9 @@ void fp4_attn_kernel(AttnArgs a) {
       if (kEarly && need_q) store_q<NW>(sm, qv, true, tid, Ly.sm_scale);
       // codes as loaded; an absent key's scales are zero, so its values are
       // zero whatever slot 0 holds (its logits are masked as well)
-      uint4* dst = (uint4*)&sm.code[skey * kCodeRow + 4 * CPT * spart];
+      uint4* dst = (uint4*)&sm.code[skey * kCodeRow] + spart;
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) dst[i] = rv[i];
+      for (int i = 0; i < CPT; ++i) dst[TPK * i] = rv[i];
       {
         uint2* sd = (uint2*)&sm.sh2[skey * kSh2Row + SPT * spart];
 #pragma unroll
