@@ -187,3 +187,16 @@ def test_group_blocks_only_full_then_reuse(R):
     w = synth.Workload(f"blocks_only_FIRRR_FRRR_b{R}", 1700 + R, lens, "FIRRRFRRR", hier=True,
                        full_blocks_only=True, planted=0.01, raw_fp4=True)
     run_and_compare(w, by_group=True, check_rows=sorted(set([0, 1, R // 2, R - 1])))
+
+
+@pytest.mark.parametrize("kind", ["planted", "equal_keys"])
+def test_group_paged_ragged_small_batch(kind):
+    """A small paged batch whose attention launches fit on the CUs (8 rows x
+    4 layers), so the Top-512's final selection runs inside the attention
+    launch: ragged lengths with an empty row, rows shorter than the Top-512
+    and rows of several segments, a Full and a Reindex group over the
+    candidate blocks; with every indexer key equal the selection takes its
+    general path there."""
+    w = synth.Workload(f"paged_ragged_small_{kind}", 1701, [0, 1, 700, 2049, 5000, 12000, 3000, 64], "FRRRIRRR",
+                       hier=True, paged=True, planted=0.02, raw_fp4=True)
+    run_and_compare(w, by_group=True, equal_keys=kind == "equal_keys")
