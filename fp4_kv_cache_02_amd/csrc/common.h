@@ -106,6 +106,8 @@ CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
     }                                                                                            \
   } while (0)
 #define CSA2_TRACE_PTR(a) (a).trace
+// slot `off` of the trace buffer, or null when none is set
+#define CSA2_TRACE_AT(a, off) ((a).trace ? (a).trace + (off) : (uint64_t*)nullptr)
 // per-block start (i = 0) and end (i = 1) times of a 1-D grid at slots
 // base + 2 * block + i of a 2048-slot trace buffer
 #define CSA2_SPAN(a, base, i)                                                                     \
@@ -125,6 +127,7 @@ CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
   do {                    \
   } while (0)
 #define CSA2_TRACE_PTR(a) ((uint64_t*)nullptr)
+#define CSA2_TRACE_AT(a, off) ((uint64_t*)nullptr)
 #endif
 
 }  // namespace csa2

@@ -193,7 +193,7 @@ CSA2_DEV SelResult block_select(Sm& sm, const Keys& ks, uint32_t kth, uint32_t c
   uint32_t lo, hi, count;
   block_range(sm, ks, lo, hi, count);
   CSA2_MARKP(tr, 0);
-  int pass = 0;
+  [[maybe_unused]] int pass = 0;     // (numbers the trace marks)
   SelResult res;
   if (count <= kth) {
     res.T = 0u;

@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
   __syncthreads();
   CSA2_MARK(a, 21);
   const LdsKeysT<SelSmemT<kTauKeyWords>> ks{&sm.sel, n_pad};
-  const SelResult res = block_select(sm.sel, ks, K, 0u, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 24 : nullptr);
+  const SelResult res = block_select(sm.sel, ks, K, 0u, CSA2_TRACE_AT(a, 24));
   CSA2_MARK(a, 22);
   const uint32_t m = block_compact(sm.sel, ks, res, K, [&](uint32_t o, int e) { out[o] = sm.pos[e]; });
   for (int i = (int)m + tid; i < a.k; i += kSelThreads) out[i] = -1;

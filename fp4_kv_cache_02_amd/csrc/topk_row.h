@@ -103,7 +103,7 @@ CSA2_DEV bool topk_threshold(const TopkArgs& a, int r, int64_t n0, SelSmem& sm, 
   // (the descent keeps every child >= it), so the search may stop at the
   // first bin edge with at most 1.5 k values above it (usually one pass).
   const uint32_t cap = (T == 0) ? 0u : K + K / 2;
-  const SelResult s = block_select(sm, top, K, cap, CSA2_TRACE_PTR(a) ? CSA2_TRACE_PTR(a) + 10 : nullptr);
+  const SelResult s = block_select(sm, top, K, cap, CSA2_TRACE_AT(a, 10));
   CSA2_MARK(a, 1);
   if (T == 0) {
     const uint32_t m = block_compact(sm, top, s, K, [&](uint32_t pos, int e) {
