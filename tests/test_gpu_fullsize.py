@@ -14,9 +14,10 @@ from tests.gpu_util import ATTN_TOL, host, lse_ok, rel_err, say
 pytestmark = pytest.mark.gpu
 
 
-def oracle_caches(w, K):
+def oracle_caches(w, K, K_scale=None):
     """The oracle's own main KV (quantised by the oracle from the seeded source
-    values) and the indexer keys at their slots."""
+    values) and the indexer keys at their slots (FP8 codes with K_scale when
+    given)."""
     n_slots, pt, _ = synth.slots_layout(w)
     if w.raw_fp4:
         P, S = synth.gen_fp4_raw(w, n_slots)
@@ -33,17 +34,30 @@ def oracle_caches(w, K):
                 P[sl], S[sl] = pp[m], ps[m]
             else:
                 P[sl], S[sl] = O.quantize_fp4(synth.gen_kv_values(w, b, 0, L))
-    return O.Cache(P, S, K, w.seq_lens, pt, 64, w.slot_stride), P, S, pt
+    return O.Cache(P, S, K, w.seq_lens, pt, 64, w.slot_stride, k_idx_scale=K_scale), P, S, pt
 
 
-def run_fullsize(w, rows):
-    from fp4_kv_cache_02_amd import group
+def run_fullsize(w, rows, fp8_keys=False):
+    """fp8_keys: the indexer keys in the FP8 form bench.py times, made from the
+    workload's bf16 keys by the library's FP8 key quantiser; its bytes must
+    equal the oracle's quantisation at every slot, and the oracle scores its
+    own FP8 entries."""
+    import dataclasses
+    from fp4_kv_cache_02_amd import csa2, group
     n_slots, pt, _ = synth.slots_layout(w)
-    say(w.name, "building inputs, rows checked", rows)
+    say(w.name, "building inputs, rows checked", rows, "fp8 keys" if fp8_keys else "")
     K = group.k_idx_slots_from_synth(w, n_slots, pt)
     inp = group.build_inputs(w, k_idx=K)
+    K_scale = None
+    if fp8_keys:
+        codes = torch.zeros((inp.k_idx.shape[0], 64), dtype=torch.uint8, device="cuda")
+        scale = torch.zeros((inp.k_idx.shape[0],), dtype=torch.float32, device="cuda")
+        csa2.csa2_fp8_key_quantize(inp.k_idx, codes, scale)
+        inp = dataclasses.replace(inp, k_idx=codes, k_scale=scale)
+        K, K_scale = O.quantize_fp8_keys(K)
+        assert np.array_equal(host(codes), K) and np.array_equal(host(scale).view(np.uint32), K_scale.view(np.uint32))
     run = group.GroupRunner(w, inp)
-    cache, P, S, _ = oracle_caches(w, K)
+    cache, P, S, _ = oracle_caches(w, K, K_scale)
     gP, gS = host(inp.kv_fp4), host(inp.kv_scale)
     row_seq = w.row_seq()
     state = O.GroupState(w.R)
@@ -81,6 +95,13 @@ def run_fullsize(w, rows):
 def test_fullsize_decode_128k():
     w = synth.workload("decode_128k")
     run_fullsize(w, list(range(w.R)))
+
+
+def test_fullsize_decode_128k_fp8_keys():
+    """The 128K decode group on FP8 indexer keys (64 E4M3 codes + a float32
+    scale per position), every row."""
+    w = synth.workload("decode_128k")
+    run_fullsize(w, list(range(w.R)), fp8_keys=True)
 
 
 def test_fullsize_decode_1m():
