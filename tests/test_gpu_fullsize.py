@@ -109,6 +109,13 @@ def test_fullsize_decode_1m():
     run_fullsize(w, [0])
 
 
+def test_fullsize_decode_1m_fp8_keys():
+    """The 1M hierarchical group on FP8 indexer keys: the Full layer's scan and
+    candidate blocks, then the Reindex scoring of the candidates."""
+    w = synth.workload("decode_1m")
+    run_fullsize(w, [0], fp8_keys=True)
+
+
 def test_fullsize_prefill():
     w = synth.workload("prefill")
     rng = np.random.default_rng(7)
