@@ -130,6 +130,15 @@ def test_fullsize_mixed_serving():
     run_fullsize(w, rows)
 
 
+def test_fullsize_mixed_serving_fp8_keys():
+    """The mixed paged serving batch on FP8 indexer keys (paged FP8 scan, the
+    Top-512 of rows past 131072 positions, Reindex scoring of candidates)."""
+    w = synth.workload("serving")
+    lens = np.array(w.seq_lens)
+    rows = sorted(set([int(lens.argmax()), int(lens.argmin()), 9]))
+    run_fullsize(w, rows, fp8_keys=True)
+
+
 def test_fullsize_causal_prefill():
     """Config 3 with the chunk's own 2048 entries under the completion mask
     (matrix-core indexer with per-row lengths)."""
