@@ -175,7 +175,7 @@ def test_topk_bitexact(C, k):
     assert np.array_equal(host(out), g)
 
 
-@pytest.mark.parametrize("k", [7, 512])
+@pytest.mark.parametrize("k", [7, 512, 1024])
 def test_topk_bitexact_long_rows(C, k):
     """Rows of 131073 .. 1048576 values (one block per row descending three
     levels of maxima), every distribution, beside a short row in the same
