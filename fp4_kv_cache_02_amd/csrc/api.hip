@@ -445,6 +445,10 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
       p.fb_list = pw.fb_list;
       p.fb_count = pw.fb_count;
       p.out = sh->topk_idx;
+      // the approximate scores in bf16 share the memory of the exact scores,
+      // which only the listed rows' exact scan writes, after the selection
+      p.sb = (uint16_t*)scores;
+      p.sb_stride = cdiv(n_max, 64) * 64;     // whole groups of 64 per row (<= 2 n_max: fits)
       hipError_t e = launch_prefill_index(p, a->head_w != nullptr, st);
       if (e != hipSuccess) return CSA2_ERR_HIP;
       IdxArgs ia;

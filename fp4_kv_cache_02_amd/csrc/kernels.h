@@ -84,6 +84,8 @@ struct PrefArgs {
   int64_t gmax_stride = 0;
   float* kmax_part = nullptr;           // [ceil(n_max/2048)] largest |key element| per chunk of 2048 positions
   float* theta = nullptr;               // [R] candidate threshold
+  uint16_t* sb = nullptr;               // [R][sb_stride] approximate scores rounded to bf16 (NaN: not visible)
+  int64_t sb_stride = 0;                // a multiple of 64, >= n_max
   uint32_t* cand_count = nullptr;       // [R]
   int32_t* cand = nullptr;              // [R][cap] candidate positions
   int32_t cap = 0;

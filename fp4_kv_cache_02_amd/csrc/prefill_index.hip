@@ -10,16 +10,18 @@
 // therefore only used to find, for each row, a small superset of the Top-k,
 // with a proven error band, and the superset is then rescored exactly:
 //
-//   1. pass 0 (MFMA): s~ for every (row, position); per row and group of 64
-//      positions the maximum of s~ (gmax); the largest |key| element (kmax).
+//   1. pass 0 (MFMA): s~ for every (row, position), stored rounded to bf16;
+//      per row and group of 64 positions the maximum of s~ (gmax); the
+//      largest |key| element (kmax).
 //   2. threshold: tau = (a lower bound of) the k-th largest gmax of the row.
 //      At least k groups hold a position with s~ >= tau, so at least k
 //      positions have a canonical score >= tau - D, where D bounds |s~ - s|;
 //      hence every position of the exact Top-k has s >= tau - D and
 //      s~ >= theta = tau - 2D.
-//   3. pass 1 (MFMA): the positions with s~ >= theta are the candidates
-//      (groups whose gmax is below theta are skipped: the same arithmetic
-//      produced gmax).
+//   3. pass 1 (filter): the positions whose stored bf16 score is >=
+//      bf16(theta) are the candidates, read only in the groups whose gmax
+//      is >= theta (the same arithmetic produced gmax).  Rounding to nearest
+//      even is monotone, so every position with s~ >= theta passes.
 //   4. select: the candidates are put in position order, rescored with the
 //      canonical arithmetic and the exact Top-k (ties to the lower position)
 //      is written in ascending position order.
@@ -46,13 +48,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 CSA2_DEV bf16x8_t to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+// float -> bf16 bits, rounded to nearest even (monotone: x <= y gives bf16(x) <= bf16(y))
+CSA2_DEV uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+constexpr uint16_t kBf16NaN = 0x7FC0u;
 
 constexpr int kPWaves = 4;                  // waves per workgroup of the MFMA passes
 constexpr int kPRows = 16 * kPWaves;        // query rows per workgroup (16 per wave)
 constexpr int kPChunk = 2048;               // positions per workgroup
 constexpr int kPStage = 128;                // positions per LDS stage
 constexpr int kPGroup = 64;                 // positions per gmax group
-constexpr int kPGroupsWG = kPChunk / kPGroup;
 
 // DPP lane patterns inside a row of 16 lanes
 #define PF_DPP(v, ctrl) \
@@ -81,14 +85,10 @@ CSA2_DEV float row16_sum(float v) {
 struct PassSmem {
   uint4 keys[kPStage * 8];            // chunk c of stage position p at p*8 + (c ^ (p & 7))
   uint32_t present[kPStage + kPWaves * 64];   // [kPStage, ...): sink of the non-writing lanes
-  uint32_t bm[kPRows][kPChunk / 32];  // pass 1: candidate bitmap (row, position in the chunk)
-  uint32_t qcnt[kPWaves * 64];        // pass 1 flush: candidates per (row, quarter of the chunk)
-  uint32_t rowbase[kPRows];
   uint32_t kmax[kPWaves];
-  uint64_t act[kPWaves][kPGroupsWG / 4];
 };
 
-// Pass 0 (PASS = 0) and pass 1 (PASS = 1).  Workgroup (x, y): positions
+// Pass 0.  Workgroup (x, y): positions
 // [2048x, 2048x + 2048) of rows [64y, 64y + 64); wave w owns rows 64y + 16w
 // .. +15 as four MFMA row tiles of 4 rows x 4 heads.
 //
@@ -104,7 +104,7 @@ CSA2_DEV int pref_row_len(const PrefArgs& a, int r) {
   return min(a.seq_len[a.row_seq ? a.row_seq[r] : 0], a.n_max);
 }
 
-template <int PASS, bool HAS_W>
+template <bool HAS_W>
 __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   __shared__ PassSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -131,7 +131,6 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   int orow[4];
   int olen[4];
   float w[4][4];
-  float th[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     orow[mt] = rw0 + 4 * mt + g;
@@ -139,28 +138,8 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
     const int rr = min(orow[mt], a.R - 1);
 #pragma unroll
     for (int h = 0; h < 4; ++h) w[mt][h] = HAS_W ? a.head_w[(int64_t)rr * 4 + h] : 1.0f;
-    th[mt] = (PASS == 1 && orow[mt] < a.R) ? a.theta[orow[mt]] : __builtin_inff();
   }
-  // pass 1: which (4-row tile, group) pairs can hold a candidate.  Lane l
-  // tests row rw0 + (l & 15) at groups (l >> 4) + 4i; ballot i then holds the
-  // 16 row bits of group 4i + q in bits [16q, 16q + 16).
-  if (PASS == 1) {
-    const int row = rw0 + c;
-    const float t = row < a.R ? a.theta[row] : __builtin_inff();
-    const int rr = min(row, a.R - 1);
-    const int lrow = pref_row_len(a, row);
-#pragma unroll
-    for (int i = 0; i < kPGroupsWG / 4; ++i) {
-      const int64_t grp = x0 / kPGroup + g + 4 * i;
-      const bool ok = grp * kPGroup < lrow;
-      const float gm = ok ? a.gmax[(int64_t)rr * a.gmax_stride + (ok ? grp : 0)] : -__builtin_inff();
-      const uint64_t bits = __ballot(gm >= t);
-      if (lane == 0) sm.act[wave][i] = bits;
-    }
-    for (int i = tid; i < kPRows * kPChunk / 32; i += kPWaves * 64) (&sm.bm[0][0])[i] = 0u;
-  }
-
-  const bool want_kmax = PASS == 0 && blockIdx.y == 0;
+  const bool want_kmax = blockIdx.y == 0;
   uint32_t kmx = 0u;
 
   // stage loads: thread t loads chunk (t & 7) of stage positions (t >> 3) + 32i
@@ -207,14 +186,6 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 #pragma unroll 2
     for (int nt = 0; nt < kPStage / 16; ++nt) {
       const int pl = 16 * nt + c;
-      const int grp_wg = (s * kPStage + 16 * nt) / kPGroup;     // group within the workgroup
-      if (PASS == 1) {
-        // skip the 16 positions when none of the wave's 16 rows can hold a
-        // candidate in this group (all four tiles are computed otherwise: the
-        // eight MFMAs issue back to back)
-        const uint32_t bits = (uint32_t)(sm.act[wave][grp_wg >> 2] >> (16 * (grp_wg & 3))) & 0xFFFFu;
-        if (!__builtin_amdgcn_readfirstlane(bits)) continue;
-      }
       const uint4 b0 = sm.keys[pl * 8 + (g ^ (pl & 7))];
       const uint4 b1 = sm.keys[pl * 8 + ((4 + g) ^ (pl & 7))];
       const bool pres = sm.present[pl] != 0u;
@@ -226,7 +197,6 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][0], to_bf16x8(b0), acc[mt], 0, 0, 0);
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][1], to_bf16x8(b1), acc[mt], 0, 0, 0);
       }
-      bool hit[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const float r0 = fmaxf(acc[mt][0], 0.0f), r1 = fmaxf(acc[mt][1], 0.0f);
@@ -237,26 +207,11 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
         else
           sc = (r0 + r1) + (r2 + r3);
         const bool vis = pres && pos < olen[mt];
-        if (PASS == 0) gm[mt] = fmaxf(gm[mt], vis ? sc : -__builtin_inff());
-        hit[mt] = PASS == 1 && vis && orow[mt] < a.R && sc >= th[mt];
+        gm[mt] = fmaxf(gm[mt], vis ? sc : -__builtin_inff());
+        // the score for pass 1 (NaN where not visible: no comparison passes)
+        if (pos < L && orow[mt] < a.R) a.sb[(int64_t)orow[mt] * a.sb_stride + pos] = vis ? bf16_bits(sc) : kBf16NaN;
       }
-      if (PASS == 1) {
-        // hits as bits: lane (c, g) of tile mt is position 16 nt + c of row
-        // 16 wave + 4 mt + g; one LDS OR (no return value, no wait) per row
-        uint64_t mm[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) mm[mt] = __ballot(hit[mt]);
-        if ((mm[0] | mm[1] | mm[2] | mm[3]) != 0ull && c == 0) {
-          const int word = (s * kPStage + 16 * nt) >> 5;
-          const uint32_t sh = 16u * (uint32_t)(nt & 1);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const uint32_t bits = (uint32_t)(mm[mt] >> (16 * g)) & 0xFFFFu;
-            if (bits) atomicOr(&sm.bm[16 * wave + 4 * mt + g][word], bits << sh);
-          }
-        }
-      }
-      if (PASS == 0 && (nt & 3) == 3) {      // end of a group of 64 positions
+      if ((nt & 3) == 3) {      // end of a group of 64 positions
         const int64_t grp = (x0 + (int64_t)s * kPStage) / kPGroup + (nt >> 2);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -280,37 +235,104 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   }
 #undef PF_LOAD_STAGE
 #undef PF_LOAD1
-  if (PASS == 1) {
-    // flush the bitmap: thread t takes row t / 4, words 16 (t % 4) .. +15;
-    // one global reservation per row, positions written in increasing order
-    __syncthreads();
-    const int rl = tid >> 2, q = tid & 3;
-    const int row = blockIdx.y * kPRows + rl;
+}
+
+// Pass 1: the candidates of row r are the positions, inside the groups whose
+// maximum is >= theta, whose stored score is >= theta once both are rounded
+// to bf16.  Rounding to nearest even never reverses an order, so every
+// position with s~ >= theta passes; the few others that pass (less than one
+// bf16 step below theta) are rescored exactly like every candidate.  One
+// block per row: the row's groups at or above theta listed in LDS (ballot
+// compaction, one LDS reservation per wave), then eight lanes per group,
+// 16 bytes (8 scores) each, kFUnroll groups in flight per lane; the hits of
+// a wave take one reservation (a wave prefix sum of the lanes' counts).  The
+// list is in no particular order: the selection sorts it.
+constexpr int kFWaves = 4;
+constexpr int kFUnroll = 8;
+__global__ __launch_bounds__(kFWaves * 64) void pref_filter_kernel(PrefArgs a) {
+  constexpr int kMaxG = kPrefMaxN / kPGroup;
+  constexpr int kGPer = kMaxG / (kFWaves * 64);
+  __shared__ int32_t grp[kMaxG];
+  __shared__ uint32_t ng, nc;
+  const int r = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int L = pref_row_len(a, r);
+  const int G = (L + kPGroup - 1) / kPGroup;
+  const float th = a.theta[r];
+  const float thb = __uint_as_float((uint32_t)bf16_bits(th) << 16);
+  if (tid == 0) {
+    ng = 0u;
+    nc = 0u;
+  }
+  float gv[kGPer];
+#pragma unroll
+  for (int i = 0; i < kGPer; ++i) {
+    const int gi = tid + kFWaves * 64 * i;
+    gv[i] = gi < G ? a.gmax[(int64_t)r * a.gmax_stride + gi] : -__builtin_inff();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kGPer; ++i) {
+    const int gi = tid + kFWaves * 64 * i;
+    const bool q = gi < G && gv[i] >= th;
+    const uint64_t bq = __ballot(q);
+    if (bq) {                                      // uniform
+      uint32_t base = 0u;
+      if (lane == 0) base = atomicAdd(&ng, (uint32_t)__popcll(bq));
+      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+      if (q) grp[base + (uint32_t)__popcll(bq & lt)] = gi;
+    }
+  }
+  __syncthreads();
+  const uint32_t n_g = ng;
+  const uint4* row = (const uint4*)(a.sb + (int64_t)r * a.sb_stride);
+  int32_t* cl = a.cand + (int64_t)r * a.cap;
+  const int part = lane & 7;
+  for (uint32_t j0 = 0; j0 < n_g; j0 += kFUnroll * kFWaves * 8) {
+    int gg[kFUnroll];
+    uint4 v[kFUnroll];
+#pragma unroll
+    for (int u = 0; u < kFUnroll; ++u) {
+      const uint32_t j = j0 + (uint32_t)((u * kFWaves + wave) * 8 + (lane >> 3));
+      gg[u] = j < n_g ? grp[j] : -1;
+      v[u] = row[(int64_t)(gg[u] >= 0 ? gg[u] : 0) * 8 + part];
+    }
+    uint32_t hits[kFUnroll];
     uint32_t cnt = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) cnt += (uint32_t)__popc(sm.bm[rl][16 * q + i]);
-    sm.qcnt[tid] = cnt;
-    __syncthreads();
-    uint32_t pre = 0u, tot = 0u;
+    for (int u = 0; u < kFUnroll; ++u) {
+      const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const int p0 = gg[u] * kPGroup + 8 * part;
+      uint32_t h = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t v = sm.qcnt[4 * rl + i];
-      pre += i < q ? v : 0u;
-      tot += v;
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16);
+        h |= (gg[u] >= 0 && p0 + e < L && __uint_as_float(bits) >= thb) ? (1u << e) : 0u;
+      }
+      hits[u] = h;
+      cnt += (uint32_t)__popc(h);
     }
-    if (q == 0) sm.rowbase[rl] = (tot && row < a.R) ? atomicAdd(&a.cand_count[row], tot) : 0u;
-    __syncthreads();
-    uint32_t dst = sm.rowbase[rl] + pre;
-    for (int i = 0; i < 16 && cnt; ++i) {
-      uint32_t wbits = sm.bm[rl][16 * q + i];
-      while (wbits) {
-        const int bit = __ffs(wbits) - 1;
-        wbits &= wbits - 1u;
-        if (dst < (uint32_t)a.cap) a.cand[(int64_t)row * a.cap + dst] = (int32_t)(x0 + 32 * (16 * q + i) + bit);
-        ++dst;
+    const uint32_t inc = wave_incl_scan_u32(cnt);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    if (tot) {                                     // uniform
+      uint32_t base = 0u;
+      if (lane == 0) base = atomicAdd(&nc, tot);
+      uint32_t o = (uint32_t)__builtin_amdgcn_readfirstlane((int)base) + inc - cnt;
+#pragma unroll
+      for (int u = 0; u < kFUnroll; ++u) {
+        uint32_t h = hits[u];
+        const int p0 = gg[u] * kPGroup + 8 * part;
+        while (h) {
+          const int e = __ffs(h) - 1;
+          h &= h - 1u;
+          if (o < (uint32_t)a.cap) cl[o] = p0 + e;
+          ++o;
+        }
       }
     }
   }
+  __syncthreads();
+  if (tid == 0) a.cand_count[r] = nc;
 }
 
 // Threshold theta per row (one wave per row): tau = the largest key T with
@@ -500,21 +522,23 @@ __global__ __launch_bounds__(kSelThreads) void pref_select_kernel(PrefArgs a) {
 
 hipError_t launch_prefill_index(const PrefArgs& a, bool has_w, hipStream_t st) {
   if (a.R <= 0) return hipSuccess;
-  if (a.n_max > kPrefMaxN || a.cap != kPrefCap || a.k > kPrefCap) return hipErrorInvalidValue;
+  if (a.n_max > kPrefMaxN || a.cap != kPrefCap || a.k > kPrefCap || !a.sb || a.sb_stride < a.n_max ||
+      (a.sb_stride & 63) != 0 || ((uintptr_t)a.sb & 15u) != 0)
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)((a.n_max + kPChunk - 1) / kPChunk), (unsigned)((a.R + kPRows - 1) / kPRows));
   const dim3 tgrid((unsigned)((a.R + 3) / 4));
   const int G = (a.n_max + kPGroup - 1) / kPGroup;
   if (has_w) {
-    hipLaunchKernelGGL((pref_pass_kernel<0, true>), grid, dim3(kPWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((pref_pass_kernel<true>), grid, dim3(kPWaves * 64), 0, st, a);
     if (G <= 2048) hipLaunchKernelGGL((pref_threshold_kernel<32, true>), tgrid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((pref_threshold_kernel<64, true>), tgrid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((pref_pass_kernel<1, true>), grid, dim3(kPWaves * 64), 0, st, a);
+    hipLaunchKernelGGL(pref_filter_kernel, dim3(a.R), dim3(kFWaves * 64), 0, st, a);
     hipLaunchKernelGGL((pref_select_kernel<true>), dim3(a.R), dim3(kSelThreads), 0, st, a);
   } else {
-    hipLaunchKernelGGL((pref_pass_kernel<0, false>), grid, dim3(kPWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((pref_pass_kernel<false>), grid, dim3(kPWaves * 64), 0, st, a);
     if (G <= 2048) hipLaunchKernelGGL((pref_threshold_kernel<32, false>), tgrid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((pref_threshold_kernel<64, false>), tgrid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((pref_pass_kernel<1, false>), grid, dim3(kPWaves * 64), 0, st, a);
+    hipLaunchKernelGGL(pref_filter_kernel, dim3(a.R), dim3(kFWaves * 64), 0, st, a);
     hipLaunchKernelGGL((pref_select_kernel<false>), dim3(a.R), dim3(kSelThreads), 0, st, a);
   }
   return hipGetLastError();
