@@ -141,3 +141,43 @@ def test_prefill_indexer_causal_rows(C):
         ref = O.topk(O.index_scores_chunked(q_idx[r], keys[:lens[r]]), 512)
         assert np.array_equal(g[r], ref), (r, np.setdiff1d(g[r], ref)[:8], np.setdiff1d(ref, g[r])[:8])
     assert np.all(np.isfinite(host(out)))
+
+
+def test_prefill_indexer_short_and_ragged_rows(C):
+    """Rows of their own lengths in one chunk: empty rows, rows of a few
+    positions, rows below 512 groups of 64 (no threshold: every visible
+    position is a candidate, within the 4096 the selection holds), rows past
+    that (the exact-scan fallback) and rows ending on and beside group
+    boundaries, among long rows."""
+    rng = np.random.default_rng(506)
+    R = 256
+    special = [0, 1, 7, 63, 64, 65, 511, 513, 2047, 4000, 4096, 4097, 20000, 32767, 32768, 32769, 65535, 65536]
+    lens = special + list(rng.integers(60000, 70001, size=R - len(special)))
+    n_max = 70001
+    lens[-1] = n_max
+    keys = _keys(rng, n_max, "random")
+    q_idx = bf16(rng, (R, 4, 64))
+    P, S = rand_fp4(rng, n_max)
+    q = bf16(rng, (R, 16, 512))
+    Sw = R + 127
+    swk, swv = bf16(rng, (1, Sw, 512)), bf16(rng, (1, Sw, 512))
+    say("prefill indexer, short and ragged rows R", R, "n_max", n_max)
+    kv = C.make_cache(dev(P), dev(S), seq_stride=0)
+    kc = C.make_cache(dev(keys), seq_stride=0)
+    seq_len = dev(np.array(lens, np.int32))
+    topk = torch.full((R, 512), -7, dtype=torch.int32, device="cuda")
+    sh = C.make_shared(kv, kc, seq_len, n_max, topk)
+    out = torch.zeros((R, 16, 512), device="cuda")
+    args = C.make_layer_args(dev(q), dev(swk), dev(swv), dev(np.arange(R, dtype=np.int32)),
+                             dev(np.full(R, 128, np.int32)), 512 ** -0.5, out, q_idx=dev(q_idx),
+                             row_seq=dev(np.arange(R, dtype=np.int32)), swa_shared=True)
+    ws = workspace(C.csa2_workspace_bytes(FULL, R, n_max, False))
+    C.csa2_layer_step(FULL, args, sh, ws)
+    torch.cuda.synchronize()
+    g = host(topk)
+    rows = list(range(len(special))) + sorted(set([R - 1] + list(rng.choice(np.arange(len(special), R), size=8,
+                                                                              replace=False))))
+    for r in rows:
+        ref = O.topk(O.index_scores_chunked(q_idx[r], keys[:lens[r]]), 512)
+        assert np.array_equal(g[r], ref), (r, lens[r], np.setdiff1d(g[r], ref)[:8], np.setdiff1d(ref, g[r])[:8])
+    assert np.all(np.isfinite(host(out)))
