@@ -51,6 +51,10 @@ CSA2_DEV bf16x8_t to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 // float -> bf16 bits, rounded to nearest even (monotone: x <= y gives bf16(x) <= bf16(y))
 CSA2_DEV uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 constexpr uint16_t kBf16NaN = 0x7FC0u;
+// ReLU as a signed integer maximum of the bits: a negative float (-0 too) is a
+// negative integer and becomes +0; one instruction, with none of the NaN
+// canonicalisation a float maximum adds in IEEE mode
+CSA2_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 constexpr int kPWaves = 4;                  // waves per workgroup of the MFMA passes
 constexpr int kPRows = 16 * kPWaves;        // query rows per workgroup (16 per wave)
@@ -131,11 +135,15 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   int orow[4];
   int olen[4];
   float w[4][4];
+  uint16_t* srow[4];        // the rows' stored scores (a row past R stores nothing)
+  bool sw[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     orow[mt] = rw0 + 4 * mt + g;
     olen[mt] = pref_row_len(a, orow[mt]);
     const int rr = min(orow[mt], a.R - 1);
+    srow[mt] = a.sb + (int64_t)rr * a.sb_stride;
+    sw[mt] = orow[mt] < a.R;
 #pragma unroll
     for (int h = 0; h < 4; ++h) w[mt][h] = HAS_W ? a.head_w[(int64_t)rr * 4 + h] : 1.0f;
   }
@@ -189,7 +197,8 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
       const uint4 b0 = sm.keys[pl * 8 + (g ^ (pl & 7))];
       const uint4 b1 = sm.keys[pl * 8 + ((4 + g) ^ (pl & 7))];
       const bool pres = sm.present[pl] != 0u;
-      const int64_t pos = x0 + (int64_t)s * kPStage + pl;
+      const int pos = (int)x0 + s * kPStage + pl;          // < kPrefMaxN
+      const bool in_l = pos < L;
       f32x4_t acc[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -199,8 +208,8 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const float r0 = fmaxf(acc[mt][0], 0.0f), r1 = fmaxf(acc[mt][1], 0.0f);
-        const float r2 = fmaxf(acc[mt][2], 0.0f), r3 = fmaxf(acc[mt][3], 0.0f);
+        const float r0 = relu_bits(acc[mt][0]), r1 = relu_bits(acc[mt][1]);
+        const float r2 = relu_bits(acc[mt][2]), r3 = relu_bits(acc[mt][3]);
         float sc;
         if (HAS_W)
           sc = (w[mt][0] * r0 + w[mt][1] * r1) + (w[mt][2] * r2 + w[mt][3] * r3);
@@ -209,14 +218,14 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
         const bool vis = pres && pos < olen[mt];
         gm[mt] = fmaxf(gm[mt], vis ? sc : -__builtin_inff());
         // the score for pass 1 (NaN where not visible: no comparison passes)
-        if (pos < L && orow[mt] < a.R) a.sb[(int64_t)orow[mt] * a.sb_stride + pos] = vis ? bf16_bits(sc) : kBf16NaN;
+        if (in_l && sw[mt]) srow[mt][pos] = vis ? bf16_bits(sc) : kBf16NaN;
       }
       if ((nt & 3) == 3) {      // end of a group of 64 positions
-        const int64_t grp = (x0 + (int64_t)s * kPStage) / kPGroup + (nt >> 2);
+        const int grp = ((int)x0 + s * kPStage) / kPGroup + (nt >> 2);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const float v = row16_max(gm[mt]);
-          if (c == 0 && orow[mt] < a.R && grp * kPGroup < olen[mt]) a.gmax[(int64_t)orow[mt] * a.gmax_stride + grp] = v;
+          if (c == 0 && sw[mt] && grp * kPGroup < olen[mt]) a.gmax[(int64_t)orow[mt] * a.gmax_stride + grp] = v;
           gm[mt] = -__builtin_inff();
         }
       }
