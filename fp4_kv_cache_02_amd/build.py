@@ -20,6 +20,10 @@ FLAGS = [
     "-ffp-contract=off",
     # packed fp32 arithmetic is not generated
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs, not accumulation registers: the
+    # prefill indexer's epilogue then reads them without a copy per value
+    # (the other kernels already keep them there)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result",
 ]
 
