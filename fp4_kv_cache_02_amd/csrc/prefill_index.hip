@@ -13,7 +13,8 @@
 //   1. pass 0 (MFMA): s~ for every (row, position), stored rounded to bf16;
 //      per row and group of 64 positions the maximum of s~ (gmax); the
 //      largest |key| element (kmax).
-//   2. threshold: tau = (a lower bound of) the k-th largest gmax of the row.
+//   2. threshold (wave 0 of the row's pass-1 block): tau = (a lower bound
+//      of) the k-th largest gmax of the row.
 //      At least k groups hold a position with s~ >= tau, so at least k
 //      positions have a canonical score >= tau - D, where D bounds |s~ - s|;
 //      hence every position of the exact Top-k has s >= tau - D and
@@ -246,6 +247,54 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 #undef PF_LOAD1
 }
 
+// Threshold theta of row r (one wave; lane is its lane): tau = the largest
+// key T with its low 12 bits zero such that at least k group maxima have
+// keys >= T (a lower bound of the k-th largest group maximum), theta =
+// tau - 2D; -inf when fewer than k groups are present.  Valid in every lane.
+template <int NREG, bool HAS_W>
+CSA2_DEV float pref_theta(const PrefArgs& a, int r, int lane) {
+  const int L = pref_row_len(a, r);
+  const int G = (L + kPGroup - 1) / kPGroup;
+  uint32_t key[NREG];
+#pragma unroll
+  for (int i = 0; i < NREG; ++i) {
+    const int gi = lane + 64 * i;
+    key[i] = gi < G ? order_key(a.gmax[(int64_t)r * a.gmax_stride + gi]) : 0u;
+  }
+  uint32_t T = 0u;
+  for (int b = 31; b >= 12; --b) {
+    const uint32_t cand = T | (1u << b);
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) cnt += (uint32_t)__popcll(__ballot(key[i] >= cand));
+    if (cnt >= (uint32_t)a.k) T = cand;
+  }
+  // kmax over the chunks of the sequence
+  const int nchunk = (L + kPChunk - 1) / kPChunk;
+  float km = 0.0f;
+  for (int i = lane; i < nchunk; i += 64) km = fmaxf(km, a.kmax_part[i]);
+  km = __uint_as_float(wave_max_u32(__float_as_uint(km)));
+  // sum_h |w_h| |q_h|_1: lane l holds elements 4l .. 4l+3, head l / 16
+  const uint2 qv = ((const uint2*)(a.q32 + (int64_t)r * 128))[lane];
+  float s1 = (fabsf(bf16_lo(qv.x)) + fabsf(bf16_hi(qv.x))) + (fabsf(bf16_lo(qv.y)) + fabsf(bf16_hi(qv.y)));
+  s1 = row16_sum(s1);
+  if (HAS_W) s1 *= fabsf(a.head_w[(int64_t)r * 4 + (lane >> 4)]);
+  const float aq = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 0)) +
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 16))) +
+                   (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 32)) +
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 48)));
+  float theta = -__builtin_inff();
+  if (T != 0u) {
+    const double tau = (double)key_to_float(T);
+    const double u = 0x1p-24, u2 = 0x1p-20;
+    const double D = (double)aq * (double)km * (17.0 * u + 73.0 * u2) * (1.0 + 0x1p-10) + 0x1p-120;
+    float t = (float)(tau - 2.0 * D);
+    t = t - fabsf(t) * 0x1p-20f;
+    theta = t;
+  }
+  return theta;
+}
+
 // Pass 1: the candidates of row r are the positions, inside the groups whose
 // maximum is >= theta, whose stored score is >= theta once both are rounded
 // to bf16.  Rounding to nearest even never reverses an order, so every
@@ -255,23 +304,25 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 // compaction, one LDS reservation per wave), then eight lanes per group,
 // 16 bytes (8 scores) each, kFUnroll groups in flight per lane; the hits of
 // a wave take one reservation (a wave prefix sum of the lanes' counts).  The
-// list is in no particular order: the selection sorts it.
+// list is in no particular order: the selection sorts it.  Wave 0 first
+// finds the row's theta (pref_theta) while the group maxima come in.
 constexpr int kFWaves = 4;
 constexpr int kFUnroll = 8;
+template <int NREG, bool HAS_W>
 __global__ __launch_bounds__(kFWaves * 64) void pref_filter_kernel(PrefArgs a) {
   constexpr int kMaxG = kPrefMaxN / kPGroup;
   constexpr int kGPer = kMaxG / (kFWaves * 64);
   __shared__ int32_t grp[kMaxG];
   __shared__ uint32_t ng, nc;
+  __shared__ float s_th;
   const int r = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t lt = (1ull << lane) - 1ull;
   const int L = pref_row_len(a, r);
   const int G = (L + kPGroup - 1) / kPGroup;
-  const float th = a.theta[r];
-  const float thb = __uint_as_float((uint32_t)bf16_bits(th) << 16);
   if (tid == 0) {
     ng = 0u;
     nc = 0u;
+    if (r == 0) *a.fb_count = 0u;      // the selection lists its overflowing rows there
   }
   float gv[kGPer];
 #pragma unroll
@@ -279,7 +330,16 @@ __global__ __launch_bounds__(kFWaves * 64) void pref_filter_kernel(PrefArgs a) {
     const int gi = tid + kFWaves * 64 * i;
     gv[i] = gi < G ? a.gmax[(int64_t)r * a.gmax_stride + gi] : -__builtin_inff();
   }
+  if (wave == 0) {
+    const float t = pref_theta<NREG, HAS_W>(a, r, lane);
+    if (lane == 0) {
+      s_th = t;
+      a.theta[r] = t;
+    }
+  }
   __syncthreads();
+  const float th = s_th;
+  const float thb = __uint_as_float((uint32_t)bf16_bits(th) << 16);
 #pragma unroll
   for (int i = 0; i < kGPer; ++i) {
     const int gi = tid + kFWaves * 64 * i;
@@ -342,60 +402,6 @@ __global__ __launch_bounds__(kFWaves * 64) void pref_filter_kernel(PrefArgs a) {
   }
   __syncthreads();
   if (tid == 0) a.cand_count[r] = nc;
-}
-
-// Threshold theta per row (one wave per row): tau = the largest key T with
-// its low 12 bits zero such that at least k group maxima have keys >= T
-// (a lower bound of the k-th largest group maximum), theta = tau - 2D.
-template <int NREG, bool HAS_W>
-__global__ __launch_bounds__(256) void pref_threshold_kernel(PrefArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.fb_count = 0u;
-  if (r >= a.R) return;
-  const int L = pref_row_len(a, r);
-  const int G = (L + kPGroup - 1) / kPGroup;
-  uint32_t key[NREG];
-#pragma unroll
-  for (int i = 0; i < NREG; ++i) {
-    const int gi = lane + 64 * i;
-    key[i] = gi < G ? order_key(a.gmax[(int64_t)r * a.gmax_stride + gi]) : 0u;
-  }
-  uint32_t T = 0u;
-  for (int b = 31; b >= 12; --b) {
-    const uint32_t cand = T | (1u << b);
-    uint32_t cnt = 0u;
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) cnt += (uint32_t)__popcll(__ballot(key[i] >= cand));
-    if (cnt >= (uint32_t)a.k) T = cand;
-  }
-  // kmax over the chunks of the sequence
-  const int nchunk = (L + kPChunk - 1) / kPChunk;
-  float km = 0.0f;
-  for (int i = lane; i < nchunk; i += 64) km = fmaxf(km, a.kmax_part[i]);
-  km = __uint_as_float(wave_max_u32(__float_as_uint(km)));
-  // sum_h |w_h| |q_h|_1: lane l holds elements 4l .. 4l+3, head l / 16
-  const uint2 qv = ((const uint2*)(a.q32 + (int64_t)r * 128))[lane];
-  float s1 = (fabsf(bf16_lo(qv.x)) + fabsf(bf16_hi(qv.x))) + (fabsf(bf16_lo(qv.y)) + fabsf(bf16_hi(qv.y)));
-  s1 = row16_sum(s1);
-  if (HAS_W) s1 *= fabsf(a.head_w[(int64_t)r * 4 + (lane >> 4)]);
-  const float aq = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 0)) +
-                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 16))) +
-                   (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 32)) +
-                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 48)));
-  if (lane == 0) {
-    float theta = -__builtin_inff();
-    if (T != 0u) {
-      const double tau = (double)key_to_float(T);
-      const double u = 0x1p-24, u2 = 0x1p-20;
-      const double D = (double)aq * (double)km * (17.0 * u + 73.0 * u2) * (1.0 + 0x1p-10) + 0x1p-120;
-      float t = (float)(tau - 2.0 * D);
-      t = t - fabsf(t) * 0x1p-20f;
-      theta = t;
-    }
-    a.theta[r] = theta;
-    a.cand_count[r] = 0u;
-  }
 }
 
 // Exact selection among the candidates of a row (one block per row).
@@ -535,19 +541,16 @@ hipError_t launch_prefill_index(const PrefArgs& a, bool has_w, hipStream_t st) {
       (a.sb_stride & 63) != 0 || ((uintptr_t)a.sb & 15u) != 0)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((a.n_max + kPChunk - 1) / kPChunk), (unsigned)((a.R + kPRows - 1) / kPRows));
-  const dim3 tgrid((unsigned)((a.R + 3) / 4));
   const int G = (a.n_max + kPGroup - 1) / kPGroup;
   if (has_w) {
     hipLaunchKernelGGL((pref_pass_kernel<true>), grid, dim3(kPWaves * 64), 0, st, a);
-    if (G <= 2048) hipLaunchKernelGGL((pref_threshold_kernel<32, true>), tgrid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((pref_threshold_kernel<64, true>), tgrid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(pref_filter_kernel, dim3(a.R), dim3(kFWaves * 64), 0, st, a);
+    if (G <= 2048) hipLaunchKernelGGL((pref_filter_kernel<32, true>), dim3(a.R), dim3(kFWaves * 64), 0, st, a);
+    else hipLaunchKernelGGL((pref_filter_kernel<64, true>), dim3(a.R), dim3(kFWaves * 64), 0, st, a);
     hipLaunchKernelGGL((pref_select_kernel<true>), dim3(a.R), dim3(kSelThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL((pref_pass_kernel<false>), grid, dim3(kPWaves * 64), 0, st, a);
-    if (G <= 2048) hipLaunchKernelGGL((pref_threshold_kernel<32, false>), tgrid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((pref_threshold_kernel<64, false>), tgrid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(pref_filter_kernel, dim3(a.R), dim3(kFWaves * 64), 0, st, a);
+    if (G <= 2048) hipLaunchKernelGGL((pref_filter_kernel<32, false>), dim3(a.R), dim3(kFWaves * 64), 0, st, a);
+    else hipLaunchKernelGGL((pref_filter_kernel<64, false>), dim3(a.R), dim3(kFWaves * 64), 0, st, a);
     hipLaunchKernelGGL((pref_select_kernel<false>), dim3(a.R), dim3(kSelThreads), 0, st, a);
   }
   return hipGetLastError();
