@@ -507,7 +507,7 @@ def main():
     m = measure(w, args.steps, args.warmup, args.replicas if not w.prefill_rows else 1)
     if w.prefill_rows:
         pf = prefill_summary(w, m)
-        roof = {"kernel": "whole prefill group step (MFMA indexer passes, selection, attention)", "bound": "mfma",
+        roof = {"kernel": "whole prefill group step (MFMA indexer pass, candidate filter, selection, attention)", "bound": "mfma",
                 "achieved": pf["achieved_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": pf["mfma_frac"], "traffic": None, "flops_per_step": pf["flops_per_step"]}
     else:
