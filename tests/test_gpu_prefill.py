@@ -181,3 +181,9 @@ def test_prefill_indexer_short_and_ragged_rows(C):
         ref = O.topk(O.index_scores_chunked(q_idx[r], keys[:lens[r]]), 512)
         assert np.array_equal(g[r], ref), (r, lens[r], np.setdiff1d(g[r], ref)[:8], np.setdiff1d(ref, g[r])[:8])
     assert np.all(np.isfinite(host(out)))
+
+
+def test_prefill_indexer_max_positions(C):
+    """The largest chunk the matrix-core indexer takes: 262144 positions per
+    row (its stored bf16 scores, positions and group indices at their limits)."""
+    _run(C, R=256, L=262144, n_max=262144, kind="random", paged=False, weighted=True, seed=507, n_check=8)
