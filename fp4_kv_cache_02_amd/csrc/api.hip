@@ -217,7 +217,11 @@ TopkArgs topk_args(const float* lv0, int64_t stride, const int32_t* row_seq, con
 // built here and *defer receives the arguments of its final selection, which
 // the attention launch that follows takes over (defer->out stays null
 // otherwise).
-csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st, TopkArgs* defer = nullptr) {
+// The path a Top-k takes, chosen (and its arguments completed, building
+// missing levels of maxima first) by plan_topk, launched by launch_planned.
+enum TopkPath { kPathOneBlock, kPathDesc, kPathLarge, kPathError };
+
+TopkPath plan_topk(TopkArgs& a, const TopkWs& tw, hipStream_t st) {
   const int need = topk_levels_built(a.R, a.n_max, a.k);
   for (int l = 1; l <= need; ++l) {
     if (a.lv[l]) continue;
@@ -236,7 +240,7 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st, TopkArgs* def
     m.n_max = a.n_max;
     m.R = a.R;
     hipError_t e = launch_maxima(m, st);
-    if (e != hipSuccess) return CSA2_ERR_HIP;
+    if (e != hipSuccess) return kPathError;
     a.lv[l] = dst;
   }
   CSA2_SET_TRACE(a, 1);
@@ -246,7 +250,7 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st, TopkArgs* def
     a.seg_cnt = tw.seg_cnt;
     a.seg_key = tw.seg_key;
     a.seg_pos = tw.seg_pos;
-    return hip_status(launch_topk_large(a, st));
+    return kPathLarge;
   }
   if (tw.desc_cnt && !a.row_list && topk_desc_shape(a.R, a.n_max, a.k) && a.lv[1] &&
       (desc_top_level(a.n_max) < 2 || a.lv[2])) {
@@ -254,13 +258,29 @@ csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st, TopkArgs* def
     a.seg_cnt = tw.desc_cnt;
     a.seg_key = tw.desc_key;
     a.seg_pos = tw.desc_pos;
-    if (defer) {
-      *defer = a;
-      return hip_status(launch_desc_seg(a, st));
-    }
-    return hip_status(launch_topk_desc(a, st));
+    return kPathDesc;
   }
-  return hip_status(launch_topk(a, st));
+  return kPathOneBlock;
+}
+
+// defer: the split path's final selection is left to the caller (*defer).
+csa2_status launch_planned(const TopkArgs& a, TopkPath p, hipStream_t st, TopkArgs* defer = nullptr) {
+  switch (p) {
+    case kPathLarge: return hip_status(launch_topk_large(a, st));
+    case kPathDesc:
+      if (defer) {
+        *defer = a;
+        return hip_status(launch_desc_seg(a, st));
+      }
+      return hip_status(launch_topk_desc(a, st));
+    case kPathOneBlock: return hip_status(launch_topk(a, st));
+    default: return CSA2_ERR_HIP;
+  }
+}
+
+csa2_status run_topk(TopkArgs a, const TopkWs& tw, hipStream_t st, TopkArgs* defer = nullptr) {
+  const TopkPath p = plan_topk(a, tw, st);
+  return launch_planned(a, p, st, defer);
 }
 
 // -------------------------------------------------------------- attention --
@@ -311,7 +331,8 @@ struct AttnLayerIn {
 // writes idx); the attention launch takes it over or launches it first.
 csa2_status do_attn(const AttnLayerIn* L, int n_layers, const csa2_cache* kv, const int32_t* row_seq,
                     const int32_t* seq_len, const int32_t* idx, int32_t k, int32_t R,
-                    const AttnWs& aw, char* ws, hipStream_t st, const TopkArgs* fin = nullptr) {
+                    const AttnWs& aw, char* ws, hipStream_t st, const TopkArgs* fin = nullptr,
+                    const TopkArgs* cand = nullptr) {
   AttnArgs a;
   a.sel = fin ? *fin : TopkArgs{};
   if (!fin) a.sel.out = nullptr;
@@ -341,7 +362,7 @@ csa2_status do_attn(const AttnLayerIn* L, int n_layers, const csa2_cache* kv, co
   a.part_o = aw.part_o;
   a.part_ml = aw.part_ml;
   CSA2_SET_TRACE(a, 2);
-  return hip_status(launch_attn(a, st));
+  return hip_status(launch_attn(a, st, cand));
 }
 
 bool attn_layer_ok(const csa2_layer_args* a) {
@@ -407,8 +428,11 @@ size_t index_region(csa2_mode mode, int R, int n_max, int hier) {
 // Scoring + selection of a Full or Reindex layer; leaves the Top-512 in
 // shared->topk_idx (and the candidate blocks of a hierarchical Full layer in
 // shared->cand_blocks).
+// cand_defer: when given, a hierarchical Full layer's candidate build may
+// leave its final selection to the caller (*cand_defer, out non-null), its
+// first launch paired with the Top-512's.
 csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_shared* sh, Bump& bp, bool blocks_only,
-                      hipStream_t st, TopkArgs* defer) {
+                      hipStream_t st, TopkArgs* defer, TopkArgs* cand_defer = nullptr) {
   const int R = a->R, n_max = sh->n_max;
   csa2_status s;
   if (mode == CSA2_FULL || (mode == CSA2_REINDEX && !sh->hier)) {
@@ -490,18 +514,43 @@ csa2_status run_index(csa2_mode mode, const csa2_layer_args* a, const csa2_share
     s = do_index_score(a->q_idx, a->head_w, &sh->k_idx, a->row_seq, sh->seq_len, nullptr, 0, R, n_max, scores,
                        bmax, m64, st);
     if (s) return s;
+    TopkArgs t512{}, tc{};
+    TopkPath p512 = kPathError, pc = kPathError;
+    const bool cands = mode == CSA2_FULL && sh->hier;
     if (!blocks_only) {
-      TopkArgs t = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
-      t.lv[1] = bmax;
-      t.lv[2] = m64;
-      s = run_topk(t, dw, st, defer);
+      t512 = topk_args(scores, n_max, a->row_seq, sh->seq_len, 1, R, n_max, CSA2_TOPK, sh->topk_idx);
+      t512.lv[1] = bmax;
+      t512.lv[2] = m64;
+      p512 = plan_topk(t512, dw, st);
+      if (p512 == kPathError) return CSA2_ERR_HIP;
+    }
+    if (cands) {
+      tc = topk_args(bmax, nb, a->row_seq, sh->seq_len, 8, R, nb, CSA2_KEEP_BLOCKS, sh->cand_blocks);
+      tc.lv[1] = m64;     // maxima of 8 block maxima
+      tc.lv_stride[1] = cdiv(n_max, 64);
+      pc = plan_topk(tc, tw, st);
+      if (pc == kPathError) return CSA2_ERR_HIP;
+    }
+    // the Top-512 and the candidate build read only the scan's outputs: their
+    // first launches share one, and the candidates' final selection joins the
+    // merge after the attention (the next group reads the candidates)
+    if (!blocks_only && cands && cand_defer && pc == kPathLarge) {
+      if (p512 == kPathDesc && defer && tc.n_max <= kSelCapHost) {
+        *defer = t512;
+        *cand_defer = tc;
+        return hip_status(launch_desc_seg_tau(t512, tc, st));
+      }
+      if (p512 == kPathOneBlock && tc.n_max > kSelCapHost) {
+        *cand_defer = tc;
+        return hip_status(launch_topk_kth_gather(t512, tc, st));
+      }
+    }
+    if (!blocks_only) {
+      s = launch_planned(t512, p512, st, defer);
       if (s) return s;
     }
-    if (mode == CSA2_FULL && sh->hier) {
-      TopkArgs t = topk_args(bmax, nb, a->row_seq, sh->seq_len, 8, R, nb, CSA2_KEEP_BLOCKS, sh->cand_blocks);
-      t.lv[1] = m64;     // maxima of 8 block maxima
-      t.lv_stride[1] = cdiv(n_max, 64);
-      s = run_topk(t, tw, st);
+    if (cands) {
+      s = launch_planned(tc, pc, st);
       if (s) return s;
     }
     return CSA2_OK;
@@ -743,18 +792,20 @@ csa2_status csa2_group_step(csa2_mode first_mode, int32_t n_layers, const csa2_l
   const AttnWs aw = na > 0 ? carve_attn(bp, R, na, CSA2_TOPK) : AttnWs{nullptr, nullptr, 0, 0};
   if (bp.over) return CSA2_ERR_WORKSPACE;
   // the split Top-512's final selection may be left to the attention launch
-  TopkArgs fin{};
+  TopkArgs fin{}, cfin{};
   fin.out = nullptr;
+  cfin.out = nullptr;
   if (first_mode != CSA2_REUSE) {
     Bump ib{w, index_off, index_end};
-    s = run_index(first_mode, &layers[0], sh, ib, blocks_only, st, na > 0 ? &fin : nullptr);
+    s = run_index(first_mode, &layers[0], sh, ib, blocks_only, st, na > 0 ? &fin : nullptr,
+                  na > 0 ? &cfin : nullptr);
     if (s) return s;
   }
   if (na == 0) return CSA2_OK;
   AttnLayerIn L[CSA2_MAX_GROUP_LAYERS];
   for (int i = 0; i < na; ++i) L[i] = layer_in(&layers[a0 + i]);
   return do_attn(L, na, &sh->kv, layers[0].row_seq, sh->seq_len, sh->topk_idx, CSA2_TOPK, R, aw, w, st,
-                 fin.out ? &fin : nullptr);
+                 fin.out ? &fin : nullptr, cfin.out ? &cfin : nullptr);
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, const csa2_shared* sh, void* ws,

@@ -152,8 +152,15 @@ hipError_t launch_topk_large(const TopkArgs& a, hipStream_t st);
 hipError_t launch_topk_desc(const TopkArgs& a, hipStream_t st);
 hipError_t launch_desc_seg(const TopkArgs& a, hipStream_t st);
 hipError_t launch_desc_final(const TopkArgs& a, hipStream_t st);
+// launches that pair a group step's independent pieces (topk.hip)
+hipError_t launch_desc_seg_tau(const TopkArgs& d, const TopkArgs& g, hipStream_t st);
+hipError_t launch_topk_kth_gather(const TopkArgs& t, const TopkArgs& g, hipStream_t st);
+hipError_t launch_seg_final(const TopkArgs& g, hipStream_t st);
 hipError_t launch_maxima(const MaximaArgs& a, hipStream_t st);
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+// cand: the candidate blocks' final selection, when it is to share the
+// merge's launch (after the attention)
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st, const TopkArgs* cand = nullptr);
+hipError_t launch_merge_final(const AttnArgs& a, const TopkArgs& g, hipStream_t st);
 hipError_t launch_quant(const float* x, int64_t n, const int64_t* dst, uint8_t* fp4, uint8_t* scale,
                         int64_t n_slots, hipStream_t st);
 hipError_t launch_fp8_key_quant(const uint16_t* k, int64_t n, const int64_t* dst, uint8_t* codes, float* scale,

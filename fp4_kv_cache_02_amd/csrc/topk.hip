@@ -27,16 +27,20 @@
 //   * at level 0 the exact top k is taken (ties cut by index) and written in
 //     index order.
 #include "topk_row.h"
+#include "merge_row.h"
 
 namespace csa2 {
 
-__global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
+// One block's work; every kernel of this file is a thin launch of such a
+// function (block index -> (segment, row)), so that two of them can share a
+// launch (topk_kth_kernel, desc_seg_tau_kernel, attn.hip's merge_final_kernel).
+CSA2_DEV void topk_block(const TopkArgs& a, int r0) {
   __shared__ SelSmem sm;
   __shared__ int32_t par[2][kSelCap / 8];
   __shared__ int32_t cmap[kSelCap / 8];     // the row's candidate blocks (output index map)
   const int tid = threadIdx.x;
   CSA2_SPAN(a, 256, 0);
-  int r = blockIdx.x;
+  int r = r0;
   if (a.row_list) {
     if ((uint32_t)r >= *a.row_list_count) return;
     r = a.row_list[r];
@@ -77,10 +81,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) {
 // order (= index order) and the exact top k of them; a row with more than
 // kTauCap gathered values takes the general path in the same block.
 
-__global__ __launch_bounds__(kSelThreads) void seg_tau_gather_kernel(TopkArgs a) {
+CSA2_DEV void seg_tau_gather_block(const TopkArgs& a, int s, int r) {
   __shared__ SelSmemT<1> sm;                       // (the keys stay in registers)
   __shared__ uint32_t cnt[kSegPer * kSelWaves];    // values kept per (round, wave)
-  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int64_t n0 = row_count(a, r);
   const int64_t lo = (int64_t)s * kSegLen;
@@ -146,9 +150,9 @@ __global__ __launch_bounds__(kSelThreads) void seg_tau_gather_kernel(TopkArgs a)
 // per segment selecting over the row's 16384 maxima of 8 costs more than the
 // extra launch.)
 
-__global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) {
+CSA2_DEV void seg_kth_block(const TopkArgs& a, int s, int r) {
   __shared__ SelSmemT<kSegLen + kSegLen / 32> sm;
-  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int64_t n0 = row_count(a, r);
   const int64_t lo = (int64_t)s * kSegLen;
   const int n = (int)max((int64_t)0, min(n0 - lo, (int64_t)kSegLen));
@@ -256,10 +260,10 @@ __global__ __launch_bounds__(kSelThreads) void seg_gather_kernel(TopkArgs a) {
   if (tid == 0) a.seg_cnt[rs] = tot;
 }
 
-__global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
+CSA2_DEV void seg_final_block(const TopkArgs& a, int r) {
   __shared__ FinalOrGeneral u;
   FinalSmem& sm = u.f;
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const uint32_t K = (uint32_t)a.k;
   int32_t* out = a.out + (int64_t)r * a.out_stride;
@@ -348,12 +352,12 @@ __global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) {
 // the same block.
 
 template <int SEGPER>
-__global__ __launch_bounds__(kSelThreads) void desc_seg_kernel(TopkArgs a) {
+CSA2_DEV void desc_seg_block(const TopkArgs& a, int s, int r) {
   constexpr int kSeg = SEGPER * kSelThreads;
   __shared__ SelSmemT<1> sm;                  // the keys stay in registers
   __shared__ uint32_t cnt[SEGPER * kSelWaves];
   __shared__ int32_t cm[kSeg / 8];            // the segment's candidate blocks
-  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const uint32_t K = (uint32_t)a.k;
   const int64_t n0 = row_count(a, r);
@@ -428,6 +432,87 @@ __global__ __launch_bounds__(kSelThreads) void desc_seg_kernel(TopkArgs a) {
   }
   if (tid == 0) a.seg_cnt[rs] = tot;
   CSA2_MARK(a, 2);
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkArgs a) { topk_block(a, blockIdx.x); }
+__global__ __launch_bounds__(kSelThreads) void seg_tau_gather_kernel(TopkArgs a) {
+  seg_tau_gather_block(a, blockIdx.x, blockIdx.y);
+}
+__global__ __launch_bounds__(kSelThreads) void seg_kth_kernel(TopkArgs a) { seg_kth_block(a, blockIdx.x, blockIdx.y); }
+__global__ __launch_bounds__(kSelThreads) void seg_final_kernel(TopkArgs a) { seg_final_block(a, blockIdx.x); }
+template <int SEGPER>
+__global__ __launch_bounds__(kSelThreads) void desc_seg_kernel(TopkArgs a) {
+  desc_seg_block<SEGPER>(a, blockIdx.x, blockIdx.y);
+}
+
+// Two independent pieces of a group step in one launch (both read only the
+// scan's outputs): blocks [0, d.nseg * d.R) build the split Top-512's segment
+// lists, the rest take the candidate blocks' threshold and gather
+// (seg_tau_gather); the candidates' final selection joins the merge launch.
+template <int SEGPER>
+__global__ __launch_bounds__(kSelThreads) void desc_seg_tau_kernel(TopkArgs d, TopkArgs g) {
+  const int nd = d.nseg * d.R;
+  const int b = blockIdx.x;
+  if (b < nd) {
+    desc_seg_block<SEGPER>(d, b % d.nseg, b / d.nseg);
+  } else {
+    const int b2 = b - nd;
+    seg_tau_gather_block(g, b2 % g.nseg, b2 / g.nseg);
+  }
+}
+// ... and for rows past kSelCap block maxima: blocks [0, t.R) take the
+// Top-512 one row per block, the rest the candidate segments' thresholds
+// (seg_kth), which the one-block rows leave most CUs free for.
+__global__ __launch_bounds__(kSelThreads) void topk_kth_kernel(TopkArgs t, TopkArgs g) {
+  const int b = blockIdx.x;
+  if (b < t.R) {
+    topk_block(t, b);
+  } else {
+    const int b2 = b - t.R;
+    seg_kth_block(g, b2 % g.nseg, b2 / g.nseg);
+  }
+}
+
+// The attention's merge and the candidate blocks' final selection in one
+// launch of 512-thread blocks: the first ceil(4 n_layers R / 2) each run two
+// merge blocks of 256 threads, the rest one final selection (seg_final) each.
+__global__ __launch_bounds__(kSelThreads) void merge_final_kernel(AttnArgs a, TopkArgs g) {
+  const int nm = 4 * a.n_layers * a.R;
+  const int np = (nm + 1) / 2;
+  const int b = blockIdx.x;
+  if (b < np) {
+    const int unit = 2 * b + (int)(threadIdx.x >> 8);
+    if (unit < nm) merge_block(a, unit, threadIdx.x & 255);
+  } else {
+    seg_final_block(g, b - np);
+  }
+}
+
+hipError_t launch_merge_final(const AttnArgs& a, const TopkArgs& g, hipStream_t st) {
+  const int nm = 4 * a.n_layers * a.R;
+  hipLaunchKernelGGL(merge_final_kernel, dim3((unsigned)((nm + 1) / 2 + g.R)), dim3(kSelThreads), 0, st, a, g);
+  return hipGetLastError();
+}
+hipError_t launch_seg_final(const TopkArgs& g, hipStream_t st) {
+  if (g.R == 0) return hipSuccess;
+  hipLaunchKernelGGL(seg_final_kernel, dim3(g.R), dim3(kSelThreads), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_desc_seg_tau(const TopkArgs& d, const TopkArgs& g, hipStream_t st) {
+  if (d.R == 0) return hipSuccess;
+  const unsigned nb = (unsigned)(d.nseg * d.R + g.nseg * g.R);
+  if (d.n_max <= 16 * 2 * kSelThreads)
+    hipLaunchKernelGGL(desc_seg_tau_kernel<2>, dim3(nb), dim3(kSelThreads), 0, st, d, g);
+  else
+    hipLaunchKernelGGL(desc_seg_tau_kernel<8>, dim3(nb), dim3(kSelThreads), 0, st, d, g);
+  return hipGetLastError();
+}
+hipError_t launch_topk_kth_gather(const TopkArgs& t, const TopkArgs& g, hipStream_t st) {
+  if (t.R == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kth_kernel, dim3((unsigned)(t.R + g.nseg * g.R)), dim3(kSelThreads), 0, st, t, g);
+  hipLaunchKernelGGL(seg_gather_kernel, dim3(g.nseg, g.R), dim3(kSelThreads), 0, st, g);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(kSelThreads) void desc_final_kernel(TopkArgs a) {
