@@ -21,8 +21,9 @@
 //      (l % 16, l / 16) loads key 16u + c of the wave's keys, dims 128g ..
 //      128g+127, and reads the query fragment of head c from LDS);
 //   2. the block's softmax statistics per head are combined through LDS and
-//      P (split into hi + lo halves, so the product keeps ~22 (fp16) or 16
-//      (bf16) bits) is written to LDS as [16 heads x 128 keys];
+//      P is written to LDS as [16 heads x 128 keys]: for main steps in fp16
+//      (11 significant bits; the softmax sum is taken over those rounded
+//      weights), for the window step as bf16 hi + lo halves (16 bits);
 //   3. wave w computes O[16 heads x dims DPW w .. DPW w + DPW - 1] = P V over
 //      all 128 keys: 4 K-steps of 32 keys, NT = DPW / 16 output tiles, tile j
 //      covering dims {DPW w + NT c + j : c = 0..15}, so lane (c, g) needs one
@@ -187,7 +188,6 @@ CSA2_DEV void pv_main(const AttnSmem& sm, RowState<Shape<NW>::NT>& st, int w, in
       sv[i] = u2h(sm.sh2[key * kSh2Row + sb]);
     }
     const uint4 ph = *(const uint4*)&sm.p_hi[c * kPRow + key0];
-    const uint4 pl = *(const uint4*)&sm.p_lo[c * kPRow + key0];
 #pragma unroll
     for (int sel = 0; sel < NSEL; ++sel) {
       uint32_t h[8];
@@ -196,9 +196,7 @@ CSA2_DEV void pv_main(const AttnSmem& sm, RowState<Shape<NW>::NT>& st, int w, in
       const uint4 b0 = make_uint4(pack_lo(h[0], h[1]), pack_lo(h[2], h[3]), pack_lo(h[4], h[5]), pack_lo(h[6], h[7]));
       const uint4 b1 = make_uint4(pack_hi(h[0], h[1]), pack_hi(h[2], h[3]), pack_hi(h[4], h[5]), pack_hi(h[6], h[7]));
       st.o[2 * sel] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(ph), as_h8(b0), st.o[2 * sel], 0, 0, 0);
-      st.o[2 * sel] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(pl), as_h8(b0), st.o[2 * sel], 0, 0, 0);
       st.o[2 * sel + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(ph), as_h8(b1), st.o[2 * sel + 1], 0, 0, 0);
-      st.o[2 * sel + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(pl), as_h8(b1), st.o[2 * sel + 1], 0, 0, 0);
     }
   }
 }
@@ -341,23 +339,25 @@ CSA2_DEV void step_softmax(AttnSmem& sm, RowState<Shape<NW>::NT>& st, float (&s)
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       p[e] = (mnew_c == -__builtin_inff()) ? 0.f : __expf(s[e] - mnew_c);
+      // main steps: the weights as the fp16 values the P V product takes, so
+      // that the output is a convex combination of the values
+      if (MAIN) p[e] = (float)(_Float16)p[e];
       psum += p[e];
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     if (g == 0) sm.red_l[w][c] = psum;
-    // P hi/lo -> LDS [head c][key KPW w + sigma(g, e)]
+    // P -> LDS [head c][key KPW w + sigma(g, e)]: fp16 for main steps, bf16
+    // hi + lo halves for the window step
     {
       uint32_t hw[NE / 2], lw[NE / 2];
 #pragma unroll
       for (int e = 0; e < NE; e += 2) {
         uint32_t h0, h1, l0, l1;
         if (MAIN) {
-          const _Float16 a0 = (_Float16)p[e], a1 = (_Float16)p[e + 1];
-          h0 = __builtin_bit_cast(uint16_t, a0);
-          h1 = __builtin_bit_cast(uint16_t, a1);
-          l0 = __builtin_bit_cast(uint16_t, (_Float16)(p[e] - (float)a0));
-          l1 = __builtin_bit_cast(uint16_t, (_Float16)(p[e + 1] - (float)a1));
+          h0 = __builtin_bit_cast(uint16_t, (_Float16)p[e]);       // (exact: p is an fp16 value)
+          h1 = __builtin_bit_cast(uint16_t, (_Float16)p[e + 1]);
+          l0 = l1 = 0;
         } else {
           h0 = f32_to_bf16_rne(p[e]);
           h1 = f32_to_bf16_rne(p[e + 1]);
@@ -372,7 +372,7 @@ CSA2_DEV void step_softmax(AttnSmem& sm, RowState<Shape<NW>::NT>& st, float (&s)
 #pragma unroll
       for (int u = 0; u < S::NU; ++u) {
         *(uint2*)(ph + 16 * u + 4 * g) = make_uint2(hw[2 * u], hw[2 * u + 1]);
-        *(uint2*)(pl + 16 * u + 4 * g) = make_uint2(lw[2 * u], lw[2 * u + 1]);
+        if (!MAIN) *(uint2*)(pl + 16 * u + 4 * g) = make_uint2(lw[2 * u], lw[2 * u + 1]);
       }
     }
     __syncthreads();

@@ -61,6 +61,7 @@ def run_fullsize(w, rows, fp8_keys=False):
     gP, gS = host(inp.kv_fp4), host(inp.kv_scale)
     row_seq = w.row_seq()
     state = O.GroupState(w.R)
+    emax = 0.0
     for gi, (li0, n) in enumerate(run.groups):
         say(w.name, "group", gi, w.schedule[li0:li0 + n])
         run.step_group(gi)
@@ -90,6 +91,8 @@ def run_fullsize(w, rows, fp8_keys=False):
                 e = rel_err(go[r], res[r][0])
                 assert np.all(e <= ATTN_TOL), (w.name, li, r, e.max())
                 assert lse_ok(gl[r], res[r][1]), (w.name, li, r)
+                emax = max(emax, float(e.max()))
+    say(w.name, "attention max relative error", f"{emax:.3e}")
 
 
 def test_fullsize_decode_128k():
