@@ -13,8 +13,8 @@
 //   1. pass 0 (MFMA): s~ for every (row, position), stored rounded to bf16;
 //      per row and group of 64 positions the maximum of s~ (gmax); the
 //      largest |key| element (kmax).
-//   2. threshold (wave 0 of the row's pass-1 block): tau = (a lower bound
-//      of) the k-th largest gmax of the row.
+//   2. threshold (the row's pass-1 block, before its filter): tau = (a
+//      lower bound of) the k-th largest gmax of the row.
 //      At least k groups hold a position with s~ >= tau, so at least k
 //      positions have a canonical score >= tau - D, where D bounds |s~ - s|;
 //      hence every position of the exact Top-k has s >= tau - D and
@@ -247,29 +247,12 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 #undef PF_LOAD1
 }
 
-// Threshold theta of row r (one wave; lane is its lane): tau = the largest
-// key T with its low 12 bits zero such that at least k group maxima have
-// keys >= T (a lower bound of the k-th largest group maximum), theta =
-// tau - 2D; -inf when fewer than k groups are present.  Valid in every lane.
-template <int NREG, bool HAS_W>
-CSA2_DEV float pref_theta(const PrefArgs& a, int r, int lane) {
+// The error margin D of row r (one wave; lane is its lane; valid in every
+// lane): sum_h |w_h| |q_h|_1 * kmax * (17 u + 73 u') (1 + 2^-10) + 2^-120,
+// kmax the largest |key element| over the row's visible chunks.
+template <bool HAS_W>
+CSA2_DEV double pref_margin(const PrefArgs& a, int r, int lane) {
   const int L = pref_row_len(a, r);
-  const int G = (L + kPGroup - 1) / kPGroup;
-  uint32_t key[NREG];
-#pragma unroll
-  for (int i = 0; i < NREG; ++i) {
-    const int gi = lane + 64 * i;
-    key[i] = gi < G ? order_key(a.gmax[(int64_t)r * a.gmax_stride + gi]) : 0u;
-  }
-  uint32_t T = 0u;
-  for (int b = 31; b >= 12; --b) {
-    const uint32_t cand = T | (1u << b);
-    uint32_t cnt = 0u;
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) cnt += (uint32_t)__popcll(__ballot(key[i] >= cand));
-    if (cnt >= (uint32_t)a.k) T = cand;
-  }
-  // kmax over the chunks of the sequence
   const int nchunk = (L + kPChunk - 1) / kPChunk;
   float km = 0.0f;
   for (int i = lane; i < nchunk; i += 64) km = fmaxf(km, a.kmax_part[i]);
@@ -283,16 +266,65 @@ CSA2_DEV float pref_theta(const PrefArgs& a, int r, int lane) {
                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 16))) +
                    (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 32)) +
                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), 48)));
-  float theta = -__builtin_inff();
-  if (T != 0u) {
-    const double tau = (double)key_to_float(T);
-    const double u = 0x1p-24, u2 = 0x1p-20;
-    const double D = (double)aq * (double)km * (17.0 * u + 73.0 * u2) * (1.0 + 0x1p-10) + 0x1p-120;
-    float t = (float)(tau - 2.0 * D);
-    t = t - fabsf(t) * 0x1p-20f;
-    theta = t;
+  const double u = 0x1p-24, u2 = 0x1p-20;
+  return (double)aq * (double)km * (17.0 * u + 73.0 * u2) * (1.0 + 0x1p-10) + 0x1p-120;
+}
+
+// One 8-bit digit of the row's threshold key, over the whole block (256
+// threads, one histogram bin each).  Among the keys whose bits above
+// shift + 8 equal `pre` (every key for the leading digit), the largest digit
+// d (bits shift .. shift + 7) with above + #{keys with digit >= d} >= k;
+// `above` then also counts the keys whose digit is larger.  Returns -1 when
+// even d = 0 falls short (only possible for the leading digit: fewer than k
+// keys).  The leading digit (sign and high exponent bits) takes few values,
+// so each wave adds one count per distinct value instead of one atomic per
+// key into the same bin.
+struct FiltSmem {
+  uint32_t hist[256];
+  uint32_t wsum[4];
+  uint32_t above;
+  int dig;
+};
+template <int KPT>
+CSA2_DEV int theta_digit(const uint32_t (&key)[KPT], int shift, uint32_t pre, bool lead, uint32_t k, uint32_t& above,
+                         FiltSmem& f, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  f.hist[tid] = 0u;
+  if (tid == 0) f.dig = -1;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const bool on = key[i] != 0u && (lead || (uint32_t)((uint64_t)key[i] >> (shift + 8)) == pre);
+    const uint32_t d = (key[i] >> shift) & 255u;
+    if (lead) {
+      uint64_t act = __ballot(on);
+      while (act) {                                  // uniform
+        const int l0 = __ffsll((unsigned long long)act) - 1;
+        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, l0);
+        const uint64_t m = __ballot(on && d == d0);
+        if (lane == l0) atomicAdd(&f.hist[d0], (uint32_t)__popcll(m));
+        act &= ~m;
+      }
+    } else if (on) {
+      atomicAdd(&f.hist[d], 1u);
+    }
   }
-  return theta;
+  __syncthreads();
+  // thread t: bin 255 - t; its inclusive prefix = #{keys with digit >= 255 - t}
+  const uint32_t v = f.hist[255 - tid];
+  uint32_t P = wave_incl_scan_u32(v);
+  if (lane == 63) f.wsum[wave] = P;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) P += f.wsum[w];
+  if (above + P >= k && above + P - v < k) {
+    f.dig = 255 - tid;
+    f.above = above + P - v;
+  }
+  __syncthreads();
+  const int dg = f.dig;
+  if (dg >= 0) above = f.above;
+  __syncthreads();                                   // (the next digit rewrites f)
+  return dg;
 }
 
 // Pass 1: the candidates of row r are the positions, inside the groups whose
@@ -304,17 +336,24 @@ CSA2_DEV float pref_theta(const PrefArgs& a, int r, int lane) {
 // compaction, one LDS reservation per wave), then eight lanes per group,
 // 16 bytes (8 scores) each, kFUnroll groups in flight per lane; the hits of
 // a wave take one reservation (a wave prefix sum of the lanes' counts).  The
-// list is in no particular order: the selection sorts it.  Wave 0 first
-// finds the row's theta (pref_theta) while the group maxima come in.
+// list is in no particular order: the selection sorts it.
+//
+// The row's threshold first: tau = the largest key T with its low 8 bits
+// zero such that at least k group maxima have keys >= T (a lower bound of
+// the k-th largest group maximum), found digit by digit (bits 31..24,
+// 23..16, 15..8) with block-wide histograms; theta = tau - 2D, or -inf
+// when fewer than k groups hold a visible position.
 constexpr int kFWaves = 4;
 constexpr int kFUnroll = 8;
 template <int NREG, bool HAS_W>
 __global__ __launch_bounds__(kFWaves * 64) void pref_filter_kernel(PrefArgs a) {
   constexpr int kMaxG = kPrefMaxN / kPGroup;
-  constexpr int kGPer = kMaxG / (kFWaves * 64);
+  constexpr int kGPer = NREG / kFWaves;          // group maxima per thread (64 NREG per row at most)
+  static_assert(kFWaves * 64 == 256, "one histogram bin per thread");
   __shared__ int32_t grp[kMaxG];
   __shared__ uint32_t ng, nc;
   __shared__ float s_th;
+  __shared__ FiltSmem fs;
   const int r = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t lt = (1ull << lane) - 1ull;
   const int L = pref_row_len(a, r);
@@ -325,17 +364,32 @@ __global__ __launch_bounds__(kFWaves * 64) void pref_filter_kernel(PrefArgs a) {
     if (r == 0) *a.fb_count = 0u;      // the selection lists its overflowing rows there
   }
   float gv[kGPer];
+  uint32_t key[kGPer];
 #pragma unroll
   for (int i = 0; i < kGPer; ++i) {
     const int gi = tid + kFWaves * 64 * i;
     gv[i] = gi < G ? a.gmax[(int64_t)r * a.gmax_stride + gi] : -__builtin_inff();
+    key[i] = order_key(gv[i]);                    // 0: absent, or no visible position
   }
-  if (wave == 0) {
-    const float t = pref_theta<NREG, HAS_W>(a, r, lane);
-    if (lane == 0) {
-      s_th = t;
-      a.theta[r] = t;
+  double D = 0.0;
+  if (wave == 0) D = pref_margin<HAS_W>(a, r, lane);
+  const uint32_t K = (uint32_t)a.k;
+  uint32_t above = 0u, T = 0u;
+  const int d0 = theta_digit<kGPer>(key, 24, 0u, true, K, above, fs, tid);
+  if (d0 >= 0) {                                  // uniform
+    const int d1 = theta_digit<kGPer>(key, 16, (uint32_t)d0, false, K, above, fs, tid);
+    const int d2 = theta_digit<kGPer>(key, 8, ((uint32_t)d0 << 8) | (uint32_t)d1, false, K, above, fs, tid);
+    // (d1, d2 >= 0: the keys of the chosen prefix reach k with those above)
+    T = (d1 < 0 || d2 < 0) ? 0u : ((uint32_t)d0 << 24) | ((uint32_t)d1 << 16) | ((uint32_t)d2 << 8);
+  }
+  if (tid == 0) {
+    float theta = -__builtin_inff();
+    if (T != 0u) {
+      float t = (float)((double)key_to_float(T) - 2.0 * D);
+      theta = t - fabsf(t) * 0x1p-20f;
     }
+    s_th = theta;
+    a.theta[r] = theta;
   }
   __syncthreads();
   const float th = s_th;
