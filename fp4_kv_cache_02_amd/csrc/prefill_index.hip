@@ -121,7 +121,9 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   if (x0 >= L) return;
   const int n_here = (int)min((int64_t)kPChunk, (int64_t)L - x0);
   const int n_stage = (n_here + kPStage - 1) / kPStage;
-  const int rw0 = blockIdx.y * kPRows + 16 * wave;     // first row of the wave
+  // first row of the wave (uniform: the score buffer resource below lives in
+  // scalar registers)
+  const int rw0 = blockIdx.y * kPRows + 16 * __builtin_amdgcn_readfirstlane(wave);
 
   // query fragments (rows past R read row R-1; their results are dropped)
   bf16x8_t A[4][2];
@@ -136,14 +138,20 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   int orow[4];
   int olen[4];
   float w[4][4];
-  uint16_t* srow[4];        // the rows' stored scores (a row past R stores nothing)
+  // the wave's 16 rows of stored scores as one buffer resource: a store to a
+  // row past R lies past its end, a position past L gets an offset far past
+  // it, and the hardware drops both, so the epilogue stores without a branch
+  // (16 rows x 262144 positions x 2 bytes: 32-bit offsets)
+  const int sstride = (int)a.sb_stride * 2;             // bytes per row
+  const int nrow_w = max(0, min(16, a.R - rw0));
+  const uint64_t sbase = (uint64_t)(a.sb + (int64_t)min(rw0, a.R - 1) * a.sb_stride);
+  const int snum = nrow_w * sstride;
   bool sw[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     orow[mt] = rw0 + 4 * mt + g;
     olen[mt] = pref_row_len(a, orow[mt]);
     const int rr = min(orow[mt], a.R - 1);
-    srow[mt] = a.sb + (int64_t)rr * a.sb_stride;
     sw[mt] = orow[mt] < a.R;
 #pragma unroll
     for (int h = 0; h < 4; ++h) w[mt][h] = HAS_W ? a.head_w[(int64_t)rr * 4 + h] : 1.0f;
@@ -200,6 +208,8 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
       const bool pres = sm.present[pl] != 0u;
       const int pos = (int)x0 + s * kPStage + pl;          // < kPrefMaxN
       const bool in_l = pos < L;
+      // byte offset of (row g, pos) in the wave's rows; far past them when pos >= L
+      const int po = in_l ? g * sstride + 2 * pos : 0x40000000;
       f32x4_t acc[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -219,7 +229,15 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
         const bool vis = pres && pos < olen[mt];
         gm[mt] = fmaxf(gm[mt], vis ? sc : -__builtin_inff());
         // the score for pass 1 (NaN where not visible: no comparison passes)
-        if (in_l && sw[mt]) srow[mt][pos] = vis ? bf16_bits(sc) : kBf16NaN;
+        // (the resource is rebuilt here from values read as uniform: one kept
+        // across the loop ends up in vector registers and each store in a
+        // loop over its distinct values)
+        const __amdgpu_buffer_rsrc_t sbuf = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32)) << 32) |
+                    (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sbase)),
+            0, __builtin_amdgcn_readfirstlane(snum), 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(vis ? bf16_bits(sc) : kBf16NaN), sbuf,
+                                              po + 4 * mt * sstride, 0, 0);
       }
       if ((nt & 3) == 3) {      // end of a group of 64 positions
         const int grp = ((int)x0 + s * kPStage) / kPGroup + (nt >> 2);
