@@ -40,6 +40,7 @@
 //   |s~ - s| <= sum_h |w_h| M_h (11u + 73u' + 6u)(1 + 2^-10) =: D,
 // and a subnormal product the hardware might flush adds at most 2^-120.
 #include "select.h"
+#include <type_traits>
 #include "kernels.h"
 
 namespace csa2 {
@@ -138,14 +139,14 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
   int orow[4];
   int olen[4];
   float w[4][4];
-  // the wave's 16 rows of stored scores as one buffer resource: a store to a
-  // row past R lies past its end, a position past L gets an offset far past
-  // it, and the hardware drops both, so the epilogue stores without a branch
-  // (16 rows x 262144 positions x 2 bytes: 32-bit offsets)
+  // the wave's rows of stored scores through buffer resources (rows 4 mt ..
+  // 15 for the lane's row 4 mt + g): a store to a row past R lies past the
+  // resource's end, a position past L gets an offset far past it, and the
+  // hardware drops both, so the epilogue stores without a branch (16 rows x
+  // 262144 positions x 2 bytes: 32-bit offsets)
   const int sstride = (int)a.sb_stride * 2;             // bytes per row
   const int nrow_w = max(0, min(16, a.R - rw0));
   const uint64_t sbase = (uint64_t)(a.sb + (int64_t)min(rw0, a.R - 1) * a.sb_stride);
-  const int snum = nrow_w * sstride;
   bool sw[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -156,6 +157,12 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) w[mt][h] = HAS_W ? a.head_w[(int64_t)rr * 4 + h] : 1.0f;
   }
+  // the shortest visible length over the wave's rows below R (uniform)
+  int mlen = 0x7FFFFFFF;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) mlen = sw[mt] ? min(mlen, olen[mt]) : mlen;
+  mlen = min(min(__builtin_amdgcn_readlane(mlen, 0), __builtin_amdgcn_readlane(mlen, 16)),
+             min(__builtin_amdgcn_readlane(mlen, 32), __builtin_amdgcn_readlane(mlen, 48)));
   const bool want_kmax = blockIdx.y == 0;
   uint32_t kmx = 0u;
 
@@ -200,15 +207,22 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
     __syncthreads();
     if (s + 1 < n_stage) { PF_LOAD_STAGE(s + 1); }
 
+    // a stage whose 128 positions are present and visible to every row of the
+    // wave (uniform) takes the epilogue without the visibility selects
+    const int sp0 = (int)x0 + s * kPStage;
+    const bool full = sp0 + kPStage <= min(L, mlen) &&
+                      __ballot(sm.present[lane] == 0u || sm.present[64 + lane] == 0u) == 0ull;
+    auto tile_loop = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll 2
     for (int nt = 0; nt < kPStage / 16; ++nt) {
       const int pl = 16 * nt + c;
       const uint4 b0 = sm.keys[pl * 8 + (g ^ (pl & 7))];
       const uint4 b1 = sm.keys[pl * 8 + ((4 + g) ^ (pl & 7))];
-      const bool pres = sm.present[pl] != 0u;
+      const bool pres = FULL || sm.present[pl] != 0u;
       const int pos = (int)x0 + s * kPStage + pl;          // < kPrefMaxN
-      const bool in_l = pos < L;
-      // byte offset of (row g, pos) in the wave's rows; far past them when pos >= L
+      const bool in_l = FULL || pos < L;
+      // byte offset of (row 4 mt + g, pos) from row 4 mt; far past the rows when pos >= L
       const int po = in_l ? g * sstride + 2 * pos : 0x40000000;
       f32x4_t acc[4];
 #pragma unroll
@@ -226,18 +240,18 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
           sc = (w[mt][0] * r0 + w[mt][1] * r1) + (w[mt][2] * r2 + w[mt][3] * r3);
         else
           sc = (r0 + r1) + (r2 + r3);
-        const bool vis = pres && pos < olen[mt];
+        const bool vis = FULL || (pres && pos < olen[mt]);
         gm[mt] = fmaxf(gm[mt], vis ? sc : -__builtin_inff());
-        // the score for pass 1 (NaN where not visible: no comparison passes)
-        // (the resource is rebuilt here from values read as uniform: one kept
-        // across the loop ends up in vector registers and each store in a
-        // loop over its distinct values)
-        const __amdgpu_buffer_rsrc_t sbuf = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32)) << 32) |
-                    (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sbase)),
-            0, __builtin_amdgcn_readfirstlane(snum), 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(vis ? bf16_bits(sc) : kBf16NaN), sbuf,
-                                              po + 4 * mt * sstride, 0, 0);
+        // the score for pass 1 (NaN where not visible: no comparison passes),
+        // through a resource over rows 4 mt .. 15 of the wave (rebuilt here
+        // from values read as uniform: one kept across the loop ends up in
+        // vector registers and each store in a loop over its distinct values)
+        const uint64_t bmt = (((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sbase)) +
+                             (uint64_t)(4 * mt) * (uint32_t)__builtin_amdgcn_readfirstlane(sstride);
+        const int nmt = max(0, __builtin_amdgcn_readfirstlane(nrow_w) - 4 * mt) * __builtin_amdgcn_readfirstlane(sstride);
+        const __amdgpu_buffer_rsrc_t sbuf = __builtin_amdgcn_make_buffer_rsrc((void*)bmt, 0, nmt, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(vis ? bf16_bits(sc) : kBf16NaN), sbuf, po, 0, 0);
       }
       if ((nt & 3) == 3) {      // end of a group of 64 positions
         const int grp = ((int)x0 + s * kPStage) / kPGroup + (nt >> 2);
@@ -249,6 +263,9 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
         }
       }
     }
+    };
+    if (full) tile_loop(std::true_type{});
+    else tile_loop(std::false_type{});
   }
 
   if (want_kmax) {
