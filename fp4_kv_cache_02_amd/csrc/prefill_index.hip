@@ -379,7 +379,7 @@ CSA2_DEV int theta_digit(const uint32_t (&key)[KPT], int shift, uint32_t pre, bo
 // 23..16, 15..8) with block-wide histograms; theta = tau - 2D, or -inf
 // when fewer than k groups hold a visible position.
 constexpr int kFWaves = 4;
-constexpr int kFUnroll = 8;
+constexpr int kFUnroll = 4;
 template <int NREG, bool HAS_W>
 __global__ __launch_bounds__(kFWaves * 64) void pref_filter_kernel(PrefArgs a) {
   constexpr int kMaxG = kPrefMaxN / kPGroup;
