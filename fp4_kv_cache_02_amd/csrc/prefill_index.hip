@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kPWaves * 64) void pref_pass_kernel(PrefArgs a) {
                       __ballot(sm.present[lane] == 0u || sm.present[64 + lane] == 0u) == 0ull;
     auto tile_loop = [&](auto full_c) {
       constexpr bool FULL = decltype(full_c)::value;
-#pragma unroll 2
+#pragma unroll 4
     for (int nt = 0; nt < kPStage / 16; ++nt) {
       const int pl = 16 * nt + c;
       const uint4 b0 = sm.keys[pl * 8 + (g ^ (pl & 7))];
